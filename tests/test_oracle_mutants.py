@@ -1,0 +1,110 @@
+"""Planted mistakes in the oracle must each fail at least one pin (CPU only).
+
+Each mutant is one plausible slip (a wrong index, a dropped term, a wrong
+sign, a transposed operand). The mutated source is built in a temporary
+directory and the pins run against it in a child process, so a crash also
+counts as detected. The real oracle source is never modified.
+"""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ORACLE_C = os.path.join(ROOT, "oracle", "oracle.c")
+BLOCKMGR = os.path.join(ROOT, "oracle", "blockmgr.py")
+
+C_MUTANTS = {
+    "offset_in_block": ("int64_t off = i % B;", "int64_t off = (i + 1) % B;"),
+    "logical_block": ("int64_t b = i / B;", "int64_t b = i / (B + 1);"),
+    "head_dim_transposed": ("row_off[i] = ((f * B + off) * H + h) * D;",
+                            "row_off[i] = ((f * B + off) * H) * D + h;"),
+    "scale_dropped": ("a[j] = scale * dot;", "a[j] = dot;"),
+    "v_read_from_k": ("acc += a[j] * load(vc, dtype, row_off[j] + e);",
+                      "acc += a[j] * load(kc, dtype, row_off[j] + e);"),
+    "last_token_dropped": ("attend_rows(q, ((int64_t)s * H + h) * D, k_cache, v_cache, row_off, ctx, D,",
+                           "attend_rows(q, ((int64_t)s * H + h) * D, k_cache, v_cache, row_off, ctx - 1, D,"),
+    "softmax_sign": ("a[j] = exp(a[j] - m);", "a[j] = exp(m - a[j]);"),
+    "f16_exponent_bias": ("expo - 25", "expo - 24"),
+    "f16_subnormal_scale": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    "bf16_hidden_bit": ("(double)(128 + frac)", "(double)(frac)"),
+    "append_offset_dropped": ("size_t dst = (size_t)(frame * B + off) * row_bytes;",
+                              "size_t dst = (size_t)(frame * B) * row_bytes;"),
+    "gather_offset": ("(const char*)cache + (size_t)(f * B + i % B) * row_bytes",
+                      "(const char*)cache + (size_t)(f * B + (i + 1) % B) * row_bytes"),
+    "merge_weight_dropped": ("L += exp(m[p] - M) * l[p];", "L += l[p];"),
+    "query_head_transposed": ("attend_rows(q, ((int64_t)s * H + h) * D, k_cache",
+                              "attend_rows(q, ((int64_t)h * S + s) * D, k_cache"),
+    "dense_head_dropped": ("row_off[j] = ((seq_start[s] + j) * H + h) * D;",
+                           "row_off[j] = ((seq_start[s] + j) * H) * D;"),
+    "normaliser_dropped": ("out[e] = acc / z;", "out[e] = acc;"),
+}
+
+PY_MUTANTS = {
+    "lifo_pool": ("block_id = self.free_blocks.pop(0)", "block_id = self.free_blocks.pop()"),
+    "free_to_head": ("self.free_blocks.append(block_id)", "self.free_blocks.insert(0, block_id)"),
+    "new_frame_rule": ("if cur_len % self.block_size == 0:", "if (cur_len + 1) % self.block_size == 0:"),
+    "prefill_floor": ("n = math.ceil(prompt_tokens / self.block_size)",
+                      "n = prompt_tokens // self.block_size"),
+    "no_cow": ("if self.pool.ref_counts[cur_block_id] > 1:", "if self.pool.ref_counts[cur_block_id] > 99:"),
+    "fork_no_ref": ("self.pool.add_reference(b_id)", "pass"),
+    "cow_no_copy": ("slot_ident[new * B:(new + 1) * B] = slot_ident[old * B:(old + 1) * B]", "pass"),
+    "free_ignores_refcount": ("if self.ref_counts[block_id] == 0:", "if True:"),
+}
+
+
+def _mutate(src_path, find, repl, dst_path):
+    with open(src_path) as f:
+        src = f.read()
+    assert src.count(find) == 1, f"mutation anchor not unique: {find!r}"
+    with open(dst_path, "w") as f:
+        f.write(src.replace(find, repl))
+
+
+def _run_c_mutant(name, tmp):
+    from oracle.build import build
+
+    find, repl = C_MUTANTS[name]
+    src = os.path.join(tmp, f"{name}.c")
+    lib = os.path.join(tmp, f"lib{name}.so")
+    _mutate(ORACLE_C, find, repl, src)
+    build(src=src, out=lib, extra=["-Wno-unused-variable", "-Wno-unused-parameter"])
+    r = subprocess.run([sys.executable, "-m", "tests.oracle_pins", lib], cwd=ROOT,
+                       capture_output=True, text=True, timeout=300)
+    return r.returncode, r.stdout + r.stderr
+
+
+def _run_py_mutant(name, tmp):
+    find, repl = PY_MUTANTS[name]
+    dst = os.path.join(tmp, f"blockmgr_{name}.py")
+    _mutate(BLOCKMGR, find, repl, dst)
+    r = subprocess.run([sys.executable, "-m", "tests.blockmgr_pins", dst], cwd=ROOT,
+                       capture_output=True, text=True, timeout=300)
+    return r.returncode, r.stdout + r.stderr
+
+
+def test_every_oracle_mutant_is_caught(tmp_path):
+    tmp = str(tmp_path)
+    jobs = [("c", n) for n in C_MUTANTS] + [("py", n) for n in PY_MUTANTS]
+    with ThreadPoolExecutor(max_workers=6) as ex:
+        futs = {(k, n): ex.submit(_run_c_mutant if k == "c" else _run_py_mutant, n, tmp)
+                for k, n in jobs}
+    survivors = []
+    for (k, n), fut in futs.items():
+        rc, out = fut.result()
+        if rc == 0:
+            survivors.append(f"{k}:{n}")
+    assert not survivors, f"mutants not caught by any pin: {survivors}"
+
+
+def test_unmutated_oracle_passes_pin_runner():
+    from oracle.oracle import DEFAULT_LIB
+
+    r = subprocess.run([sys.executable, "-m", "tests.oracle_pins", DEFAULT_LIB], cwd=ROOT,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    r = subprocess.run([sys.executable, "-m", "tests.blockmgr_pins", BLOCKMGR], cwd=ROOT,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr

@@ -1,0 +1,189 @@
+"""The five seeded synthetic decode workloads, as plain data.
+
+Each workload is a *schedule*: which sequences are prefilled with how many
+tokens, which are forked from which, which sequences append one token at each
+decode step, and after which steps decode attention runs. It also fixes the
+shapes, the storage dtype, the frame-pool size and the pool's initial free
+order. Nothing here allocates frames or computes slots; a block manager plays
+the schedule.
+
+Token values are identified by an integer *identity* per (sequence, position):
+a forked child shares its parent's identities for the shared prompt, so the
+bytes it attends to are the same bytes the parent wrote. Query values are
+identified by ``step * num_seqs + seq``. Values themselves come from
+:mod:`workloads.values`.
+
+The structure draws use ``numpy.random.default_rng(seed)`` with seed equal to
+the workload number (1-5), in the order documented per workload.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    dtype: str                 # storage dtype of q, K and V: "f32", "f16", "bf16"
+    H: int                     # heads (q heads == kv heads)
+    D: int                     # head dim
+    B: int                     # tokens per block
+    NB: int                    # frames in the pool
+    num_seqs: int
+    prefill: list              # [(seq, n_tokens)] in allocation order
+    forks: list = field(default_factory=list)     # [(parent, child)] after prefill
+    steps: list = field(default_factory=list)     # per decode step: seqs appending, in order
+    attend_after: list = field(default_factory=lambda: [-1])  # -1 = after prefill/forks
+    frame_order: np.ndarray | None = None         # initial free list; None = 0..NB-1
+    share_len: np.ndarray | None = None           # per seq: prompt positions shared with parent
+    share_src: np.ndarray | None = None           # per seq: parent whose identities are shared
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def _ident_base(self) -> np.ndarray:
+        # identities of sequence s occupy [s * stride, s * stride + max_len)
+        return np.arange(self.num_seqs, dtype=np.int64) * self.ident_stride
+
+    @property
+    def ident_stride(self) -> int:
+        total = {}
+        for s, n in self.prefill:
+            total[s] = total.get(s, 0) + n
+        longest = max(total.values(), default=0) + len(self.steps) + 1
+        return int(longest)
+
+    def idents(self, seq: int, positions) -> np.ndarray:
+        """Value identities of sequence ``seq`` at token ``positions``."""
+        pos = np.asarray(positions, dtype=np.int64)
+        out = seq * self.ident_stride + pos
+        if self.share_len is not None and self.share_len[seq] > 0:
+            src = int(self.share_src[seq])
+            shared = pos < self.share_len[seq]
+            out = np.where(shared, self.idents(src, pos), out)
+        return out
+
+    def q_idents(self, step_index: int) -> np.ndarray:
+        """Query identities for the attention run ``step_index`` (0-based)."""
+        return step_index * self.num_seqs + np.arange(self.num_seqs, dtype=np.int64)
+
+
+def config1() -> Workload:
+    """Worked allocation example: B=10, 100 frames, prefill 8/5/12/9, 3 steps."""
+    return Workload(
+        name="cfg1_worked_example", seed=1, dtype="f32", H=2, D=16, B=10, NB=100,
+        num_seqs=4,
+        prefill=[(0, 8), (1, 5), (2, 12), (3, 9)],
+        steps=[[0, 1, 2, 3]] * 3,
+        attend_after=[0, 1, 2],
+        description="B=10, 100 frames, FIFO; prefill A:8 B:5 C:12 D:9; 3 decode steps; "
+                    "2 heads x 16, fp32",
+    )
+
+
+def config2(S: int = 64, H: int = 32, NB: int = 20000, max_ctx: int = 2048) -> Workload:
+    """Decode batch 64, bf16, ctx ~ U{1..2048}, permuted 20k-frame pool.
+
+    Draw order: ``ctx = integers(1, max_ctx + 1, S)``, then ``permutation(NB)``.
+    """
+    rng = np.random.default_rng(2)
+    ctx = rng.integers(1, max_ctx + 1, size=S)
+    order = rng.permutation(NB)
+    return Workload(
+        name="cfg2_batch64_bf16" if (S, H) == (64, 32) else f"cfg2_S{S}_H{H}",
+        seed=2, dtype="bf16", H=H, D=128, B=16, NB=NB, num_seqs=S,
+        prefill=[(s, int(ctx[s])) for s in range(S)], frame_order=order,
+        description=f"S={S}, H={H}, d=128, B=16, bf16, ctx U[1,{max_ctx}], permuted pool of {NB}",
+    )
+
+
+def config3(S: int = 8, H: int = 40, ctx: int = 32768, NB: int = 20000) -> Workload:
+    """Long context: every sequence exactly 32,768 tokens, permuted pool."""
+    rng = np.random.default_rng(3)
+    order = rng.permutation(NB)
+    return Workload(
+        name="cfg3_long_ctx_bf16" if (S, H, ctx) == (8, 40, 32768) else f"cfg3_S{S}_H{H}_L{ctx}",
+        seed=3, dtype="bf16", H=H, D=128, B=16, NB=NB, num_seqs=S,
+        prefill=[(s, ctx) for s in range(S)], frame_order=order,
+        description=f"S={S}, H={H}, d=128, B=16, bf16, ctx {ctx}, permuted pool of {NB}",
+    )
+
+
+def config4(prompts: int = 64, n: int = 4, prompt_len: int = 1000, H: int = 32,
+            NB: int = 8192, max_tail: int = 200) -> Workload:
+    """Shared-prefix parallel sampling: each prompt forked into n branches.
+
+    Sequence ``p * n + b`` is branch ``b`` of prompt ``p``; branch 0 is the
+    prefilled parent. Draw order: ``tails = integers(1, max_tail + 1, prompts * n)``.
+    Tails are appended one token per decode step, all live branches in
+    sequence order, then attention runs once.
+    """
+    rng = np.random.default_rng(4)
+    S = prompts * n
+    tails = rng.integers(1, max_tail + 1, size=S)
+    prefill = [(p * n, prompt_len) for p in range(prompts)]
+    forks = [(p * n, p * n + b) for p in range(prompts) for b in range(1, n)]
+    steps = []
+    for t in range(int(tails.max())):
+        steps.append([s for s in range(S) if tails[s] > t])
+    share_len = np.zeros(S, dtype=np.int64)
+    share_src = np.zeros(S, dtype=np.int64)
+    for p in range(prompts):
+        for b in range(1, n):
+            share_len[p * n + b] = prompt_len
+            share_src[p * n + b] = p * n
+    return Workload(
+        name="cfg4_shared_prefix_f16" if (prompts, H) == (64, 32) else f"cfg4_P{prompts}_H{H}",
+        seed=4, dtype="f16", H=H, D=128, B=32, NB=NB, num_seqs=S,
+        prefill=prefill, forks=forks, steps=steps, attend_after=[len(steps) - 1],
+        share_len=share_len, share_src=share_src,
+        description=f"{prompts} prompts x {prompt_len} tokens, n={n} branches, tails U[1,{max_tail}], "
+                    f"B=32, H={H}, d=128, fp16, FIFO pool of {NB}",
+    )
+
+
+def config5(S: int = 256, H: int = 64, NB: int = 32768, cap: int = 8192) -> Workload:
+    """Large-model decode step: lognormal contexts, append then attend.
+
+    Draw order: ``z = standard_normal(S)``; ``ctx = clip(rint(exp(ln 1000 + 0.8 z)), 1, cap)``.
+    ``ctx`` counts the token appended by the step, so the prefill is ctx - 1.
+    """
+    rng = np.random.default_rng(5)
+    z = rng.standard_normal(S)
+    ctx = np.clip(np.rint(np.exp(np.log(1000.0) + 0.8 * z)), 1, cap).astype(np.int64)
+    return Workload(
+        name="cfg5_batch256_f16" if (S, H) == (256, 64) else f"cfg5_S{S}_H{H}",
+        seed=5, dtype="f16", H=H, D=128, B=16, NB=NB, num_seqs=S,
+        prefill=[(s, int(ctx[s]) - 1) for s in range(S)],
+        steps=[list(range(S))], attend_after=[0],
+        description=f"S={S}, H={H}, d=128, B=16, fp16, lognormal ctx (median 1000, sigma 0.8, "
+                    f"cap {cap}); append one token then attend; FIFO pool of {NB}",
+    )
+
+
+FULL = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+
+
+def small(cfg_id: int) -> Workload:
+    """Reduced variants the oracle finishes in seconds, with the same structure."""
+    if cfg_id == 1:
+        return config1()
+    if cfg_id == 2:
+        return config2(S=8, H=4, NB=2000)
+    if cfg_id == 3:
+        return config3(S=2, H=2, ctx=32768, NB=4200)
+    if cfg_id == 4:
+        return config4(prompts=3, H=4, NB=600)
+    if cfg_id == 5:
+        return config5(S=24, H=4, NB=4000)
+    raise ValueError(cfg_id)
