@@ -1,0 +1,258 @@
+"""Benchmark: paged decode attention, batch 64 x 32 heads x 128, bf16, B=16.
+
+One step is one decode-attention pass over the whole batch (the partition
+kernel, then the log-sum-exp merge kernel) with the KV cache already resident
+in HBM. Before every step a 2 GiB buffer is rewritten so the step starts with
+cold caches (MI355X has a 256 MB last-level cache); the step itself is timed
+with HIP events on the stream the kernels run on. Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload 2] [--partition-tokens P]
+
+Inputs are synthetic and seeded (see workloads/): context lengths uniform in
+[1, 2048], frames drawn from a randomly permuted pool of 20,000, q/k/v
+standard-normal values rounded to bf16.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+METRIC = "paged decode attention: KV GB/s (% of HBM peak) + µs/step, bf16 batch 64"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("paged_decode.hip", "pa_device.h", "pa_launch.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_126_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, digest: str):
+    """HBM bytes per partition-kernel launch from committed rocprofv3 counter
+    runs, if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_paged_decode_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, tables, ctx, budget_s: float = 12.0):
+    """The fp64 oracle on a bounded sample of the same workload (host cores)."""
+    from oracle import blockmgr as obm
+    from oracle.oracle import STORAGE, default
+    from workloads import values as V
+
+    orc = default()
+    rng = np.random.default_rng(12345)
+    sample = np.sort(rng.choice(w.num_seqs, size=min(16, w.num_seqs), replace=False))
+    snaps, _, _ = obm.replay(w)
+    snap = snaps[-1]
+    # compact the sample's frames (a relabelling of frames leaves the result
+    # unchanged) so the host cache holds only what the sample reads
+    sub_tables = snap.tables[sample]
+    sub_ctx = snap.context_lens[sample]
+    used = np.unique(np.concatenate([sub_tables[i, :-(-int(c) // w.B)] for i, c in enumerate(sub_ctx)]))
+    remap = {int(f): i for i, f in enumerate(used)}
+    tab = np.vectorize(lambda f: remap.get(int(f), 0))(sub_tables).astype(np.int32)
+    nb = len(used)
+    nan = V.nan_bits(w.dtype)
+    k = np.full((nb, w.B, w.H, w.D), nan, dtype=STORAGE[w.dtype])
+    v = k.copy()
+    slots_all = (used[:, None] * w.B + np.arange(w.B)[None, :]).reshape(-1)
+    ids = snap.slot_ident[slots_all]
+    keep = ids >= 0
+    new_slots = np.arange(nb * w.B, dtype=np.int64)[keep]
+    k.reshape(nb * w.B, w.H, w.D)[new_slots] = V.draw_np(w.seed, V.STREAM_K, ids[keep], w.H, w.D, w.dtype)
+    v.reshape(nb * w.B, w.H, w.D)[new_slots] = V.draw_np(w.seed, V.STREAM_V, ids[keep], w.H, w.D, w.dtype)
+    q = V.draw_np(w.seed, V.STREAM_Q, w.q_idents(0)[sample], w.H, w.D, w.dtype)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        orc.paged_decode(q, k, v, tab, sub_ctx, w.B, w.scale, w.dtype)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 50:
+            break
+    kv_bytes = 2 * w.H * w.D * w.elem_bytes * int(sub_ctx.sum())
+    t = float(np.median(times))
+    return {
+        "value": kv_bytes / t / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
+        "sample": f"{len(sample)} of {w.num_seqs} sequences (all {w.H} heads, "
+                  f"{int(sub_ctx.sum())} tokens, {kv_bytes / 1e6:.1f} MB of KV), fp64 C oracle, "
+                  f"median of {len(times)} runs",
+        "seconds_per_sample": t,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
+              "has no cross-GPU step in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+    from paged_kv_cache_126_amd.driver import DeviceCache, execute, plan
+    from workloads import configs
+    from workloads import values as V
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pkv.load()
+    dev = torch.device("cuda:0")
+    w = configs.FULL[args.workload]()
+    log(f"[bench] workload {w.name}: {w.description}")
+
+    events, _ = plan(w)
+    cache = DeviceCache(w.NB, w.B, w.H, w.D, V.torch_dtype(w.dtype), dev, poison=True)
+    points = []
+
+    def rows(seqs, positions):
+        ids = np.empty(len(seqs), dtype=np.int64)
+        for s in np.unique(seqs):
+            m = seqs == s
+            ids[m] = w.idents(int(s), positions[m])
+        idt = torch.from_numpy(ids).to(dev)
+        return (V.draw_torch(w.seed, V.STREAM_K, idt, w.H, w.D, w.dtype, dev).contiguous(),
+                V.draw_torch(w.seed, V.STREAM_V, idt, w.H, w.D, w.dtype, dev).contiguous())
+
+    execute(events, cache, rows, points.append, chunk_rows=max(256, (1 << 25) // (w.H * w.D)))
+    pt = points[-1]
+    torch.cuda.synchronize()
+    log(f"[bench] cache written: {w.NB} frames, sum ctx {int(pt.context_lens.sum())}")
+
+    q = V.draw_torch(w.seed, V.STREAM_Q, w.q_idents(pt.step), w.H, w.D, w.dtype, dev).contiguous()
+    bt = torch.from_numpy(pt.tables).to(dev)
+    cl = torch.from_numpy(pt.context_lens).to(dev)
+    out = torch.empty((w.num_seqs, w.H, w.D), dtype=torch.float32, device=dev)
+    max_ctx = int(pt.context_lens.max())
+    shape = pkv.lib.make_shape(q, cache.k, bt, max_ctx, pkv.lib.PA_F32, args.partition_tokens)
+    ws = pkv.alloc_workspace(shape, dev)
+    part_tokens = pkv.partition_tokens(shape)
+    sum_ctx = int(pt.context_lens.sum())
+    kv_bytes = 2 * w.H * w.D * w.elem_bytes * sum_ctx
+    flush_buf = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
+                              args.partition_tokens, phase="partitions")
+        if evs is not None:
+            evs[1].record()
+        pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
+                              args.partition_tokens, phase="merge")
+        if evs is not None:
+            evs[2].record()
+
+    for i in range(args.warmup):
+        if not args.no_flush:
+            flush_buf.fill_(i & 0xFF)
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush_buf.fill_((i + 1) & 0xFF)
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    merge_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    ms = float(step_ms.mean())
+    log(f"[bench] {args.steps} steps: step {ms * 1e3:.1f} us (median {np.median(step_ms) * 1e3:.1f}), "
+        f"partition kernel {part_ms.mean() * 1e3:.1f} us, merge {merge_ms.mean() * 1e3:.1f} us")
+
+    # warm (no flush) back-to-back rate, reported beside the cold headline
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / args.steps
+
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    part_gbs = kv_bytes / (part_ms.mean() * 1e-3) / 1e9
+    digest = kernel_source_digest()
+    traffic = measured_traffic(w.name, digest)
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.num_seqs, "heads": w.H, "head_dim": w.D,
+            "block_size": w.B, "num_blocks": w.NB, "context": "uniform [1, 2048]",
+            "sum_ctx": sum_ctx, "kv_bytes": kv_bytes, "partition_tokens": part_tokens,
+            "out_dtype": "f32", "cache_flush_between_steps": not args.no_flush,
+        },
+        "us_per_step": round(ms * 1e3, 2),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "warm_us_per_step": round(warm_ms * 1e3, 2),
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "kernels_us": {"partition": round(float(part_ms.mean()) * 1e3, 2),
+                       "merge": round(float(merge_ms.mean()) * 1e3, 2)},
+        "roofline": {
+            "kernel": "decode_partition_kernel", "bound": "hbm",
+            "achieved": round(part_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(part_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": kv_bytes,
+        },
+        "kernel_source_digest": digest,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline(w, pt.tables, pt.context_lens)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

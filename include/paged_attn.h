@@ -1,0 +1,191 @@
+/*
+ * paged_attn.h - C ABI of the paged decode-attention library (AMD gfx950).
+ *
+ * The library implements the device-side hot path of PagedAttention:
+ *
+ *   kv_append          writes each new token's K and V rows into the slot the
+ *                      host block manager chose for it;
+ *   paged_attn_decode  single-query scaled dot-product attention of every
+ *                      sequence over its tokens, fetched from fixed-size
+ *                      physical frames through a block table.
+ *
+ * Definitions followed (by page title and section):
+ *   - "PagedAttention: Virtual Memory Guide for LLM Inference", section "The
+ *     Mathematics of Block Translation": token i of a sequence is in logical
+ *     block floor(i / B) at offset i mod B; the block table maps the logical
+ *     block to a physical frame. Section "3. PagedAttention CUDA Kernel
+ *     Execution": the attention kernel takes the block table directly and
+ *     resolves addresses itself, with no gather into a temporary buffer.
+ *   - "Solving the LLM Memory Wall: A Deep Dive into PagedAttention", section
+ *     "1. The Mathematical Foundation": the result is ordinary softmax
+ *     attention, o = sum_j softmax_j(q . k_j * scale) v_j; section
+ *     "Implementation": K and V caches are [num_blocks, block_size, heads,
+ *     head_dim], and writing a token stores its [heads, head_dim] rows at
+ *     [frame, offset].
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers, owned by the caller. The library
+ *     allocates nothing, keeps no pointer after returning, and never
+ *     synchronises the host: work is queued on `stream` (a hipStream_t; NULL
+ *     means the default stream) and results are visible once the stream
+ *     reaches that point.
+ *   - Tensors are dense and row-major in the shapes given below. Base
+ *     pointers of q, k_cache, v_cache, k_new, v_new and out must be 16-byte
+ *     aligned; head_dim * element size must be a multiple of 16 bytes.
+ *   - Errors are detected on the host from the arguments alone, before any
+ *     launch; a call that returns an error has queued nothing.
+ *   - Element types: q, k_cache, v_cache, k_new and v_new share one dtype.
+ *     Accumulation is fp32.
+ *
+ * Device-side preconditions (not checked, since checking them would need a
+ * device-to-host copy; breaking them yields unspecified results but never an
+ * access outside the buffers):
+ *   - 0 <= context_lens[s] <= max_context_len; larger values are clamped to
+ *     max_context_len and negative values to 0;
+ *   - block_tables[s][b] is a frame in [0, num_blocks) for every
+ *     b < ceil(context_lens[s] / B); out-of-range entries are clamped into
+ *     the pool; entries past that column are never read;
+ *   - the slots of one kv_append call are distinct (two tokens written to one
+ *     slot race).
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2
+} pa_dtype;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_EINVAL = -1,      /* null pointer, non-positive size, or an unsupported
+                          dtype / head_dim combination */
+  PA_EALIGN = -2,      /* a base pointer is not 16-byte aligned */
+  PA_EWORKSPACE = -3,  /* workspace missing, misaligned or too small */
+  PA_EHIP = -4         /* the HIP runtime reported an error for the launch */
+} pa_status;
+
+/* Shapes and types of one decode call. */
+typedef struct pa_decode_shape {
+  int32_t num_seqs;            /* S: queries, one per sequence */
+  int32_t num_heads;           /* H: query heads == KV heads */
+  int32_t head_dim;            /* D: 16, 32, 64, 128 or 256 */
+  int32_t block_size;          /* B: tokens per frame, >= 1 */
+  int64_t num_blocks;          /* NB: frames in each cache */
+  int32_t max_blocks_per_seq;  /* row stride of block_tables, >= ceil(max_context_len / B) */
+  int32_t max_context_len;     /* host-known bound on context_lens; sizes the launch */
+  pa_dtype kv_dtype;           /* dtype of q, k_cache and v_cache */
+  pa_dtype out_dtype;          /* PA_F32, or kv_dtype (rounded to nearest even) */
+  int32_t partition_tokens;    /* tokens per context partition; 0 = library default.
+                                  Rounded up to what the kernel's tiling needs. */
+} pa_decode_shape;
+
+/* Human-readable name of a status code. Never NULL. */
+const char* pa_status_string(pa_status status);
+
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+/*
+ * kv_append: store new tokens' K and V rows in their cache slots.
+ *
+ *   k_new, v_new   [num_tokens, H, D] in `dtype`
+ *   slot_mapping   [num_tokens] int64: slot = frame * B + offset
+ *   k_cache,
+ *   v_cache        [num_blocks, B, H, D] in `dtype`, updated in place
+ *
+ * Token n's rows are copied bit for bit to k_cache[slot / B][slot % B] and
+ * v_cache[slot / B][slot % B]. A negative slot marks padding and is skipped,
+ * as is a slot >= num_blocks * B. num_tokens == 0 queues nothing and
+ * returns PA_OK. ("Solving the LLM Memory Wall", "Implementation", the cache
+ * update of one token; "PagedAttention: Virtual Memory Guide", "1. Demand
+ * Paging during Autoregressive Decoding", the write at offset t mod B.)
+ */
+pa_status kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                    void* k_cache, void* v_cache, int64_t num_tokens, int32_t num_heads,
+                    int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                    void* stream);
+
+/*
+ * Workspace bytes paged_attn_decode needs for `shape` (partial results of
+ * context partitions); 0 when every sequence fits one partition. Returns 0
+ * for an invalid shape too: validate through paged_attn_decode.
+ */
+size_t paged_attn_workspace_size(const pa_decode_shape* shape);
+
+/* Partition size (tokens) the library uses for `shape`; 0 if invalid. */
+int32_t paged_attn_partition_tokens(const pa_decode_shape* shape);
+
+/*
+ * paged_attn_decode: decode attention through block tables.
+ *
+ *   q             [S, H, D] in kv_dtype: one query per sequence and head
+ *   k_cache,
+ *   v_cache       [NB, B, H, D] in kv_dtype
+ *   block_tables  [S, max_blocks_per_seq] int32: logical block -> frame
+ *   context_lens  [S] int32: tokens each query attends to (its own included)
+ *   block_size    B (must equal shape->block_size)
+ *   scale         multiplier of q . k (1 / sqrt(D) for standard attention)
+ *   out           [S, H, D] in out_dtype
+ *   workspace     device buffer of workspace_bytes >= paged_attn_workspace_size,
+ *                 256-byte aligned; may be NULL when that size is 0
+ *
+ * out[s][h] = sum_{i < ctx} w_i v_i / sum_{i < ctx} w_i with
+ * w_i = exp(scale * q[s][h] . k_i - max), k_i and v_i read at frame
+ * block_tables[s][i / B], offset i % B, head h. A sequence with ctx == 0
+ * gets a zero output. Long contexts are split into partitions processed in
+ * parallel and merged by a log-sum-exp reduction (the two kernels run back
+ * to back on `stream`).
+ */
+pa_status paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t block_size, float scale, void* out,
+                            const pa_decode_shape* shape, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * The two launches of paged_attn_decode, exposed separately (same arguments
+ * and rules): the partition pass writes `out` for sequences that fit one
+ * partition and partial results to `workspace` for the others; the merge
+ * pass combines those partials into `out`. Calling both in order on one
+ * stream is exactly paged_attn_decode.
+ */
+pa_status paged_attn_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       int32_t block_size, float scale, void* out,
+                                       const pa_decode_shape* shape, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+pa_status paged_attn_merge(const int32_t* context_lens, void* out, const pa_decode_shape* shape,
+                           const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_gather: block translation made visible, for checking it bit for bit.
+ * Copies, for each sequence s and token i < context_lens[s], the row
+ * cache[block_tables[s][i / B]][i % B] ([H, D], `dtype`) to
+ * out[out_row_start[s] + i]. Uses the same device translation routine as
+ * paged_attn_decode's general path. out_row_start is a device int64 [S]
+ * array chosen by the caller (normally the prefix sums of context_lens).
+ * Not part of the hot path.
+ */
+pa_status paged_gather(const void* cache, const int32_t* block_tables,
+                       const int32_t* context_lens, const int64_t* out_row_start, void* out,
+                       int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                       int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                       pa_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

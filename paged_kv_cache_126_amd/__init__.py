@@ -1,0 +1,13 @@
+"""Paged decode attention and KV append for AMD MI355X (gfx950).
+
+``lib`` binds the HIP library's C ABI; ``block_manager`` is the host-side
+frame pool and block tables that feed it.
+"""
+from .block_manager import AppendResult, BlockPool, SeqManager
+from .lib import (PagedAttnError, alloc_workspace, kv_append, load, paged_attn_decode, paged_gather,
+                  partition_tokens, workspace_size)
+
+__all__ = [
+    "AppendResult", "BlockPool", "SeqManager", "PagedAttnError", "alloc_workspace", "kv_append",
+    "load", "paged_attn_decode", "paged_gather", "partition_tokens", "workspace_size",
+]

@@ -1,0 +1,185 @@
+"""Host-side block manager: frame pool, block tables and slot mapping.
+
+This is the control plane the kernels are fed by. It follows the memory
+manager described on "PagedAttention: Virtual Memory Guide for LLM
+Inference" (sections "1. Demand Paging during Autoregressive Decoding",
+"2. Zero-Copy Branching via Copy-on-Write" and "Reference Implementation:
+Block Table & Paged Cache Manager") and the worked example of
+"PagedAttention, simply explained":
+
+* free frames are handed out first-in first-out; a frame whose reference
+  count falls to zero rejoins the tail of the free list;
+* a prompt of L tokens takes ceil(L / B) frames at once;
+* token t of a sequence (t = tokens it already holds) goes to offset t mod B
+  of its last frame; a new frame is taken exactly when t mod B == 0 (this
+  includes t = 0, the first token of an empty sequence);
+* fork shares every frame of the parent and adds one reference to each;
+* appending into a shared partial last frame first moves the sequence to a
+  private copy of that frame (copy-on-write): the caller copies the frame's
+  first t mod B rows on the device, then writes the new token.
+
+Slots are ``frame * B + offset``; with caches laid out [NB, B, H, D] a slot is
+the row index of the cache viewed as [NB * B, H, D].
+"""
+from __future__ import annotations
+
+from collections import deque
+from dataclasses import dataclass
+
+import numpy as np
+
+
+class BlockPool:
+    """Physical frames: FIFO free list plus a reference count per frame."""
+
+    def __init__(self, num_frames: int, order=None):
+        if num_frames <= 0:
+            raise ValueError("num_frames must be positive")
+        self.num_frames = int(num_frames)
+        if order is None:
+            self._free = deque(range(self.num_frames))
+        else:
+            order = [int(f) for f in order]
+            if sorted(order) != list(range(self.num_frames)):
+                raise ValueError("order must be a permutation of the frame ids")
+            self._free = deque(order)
+        self.ref = np.zeros(self.num_frames, dtype=np.int64)
+
+    @property
+    def free_count(self) -> int:
+        return len(self._free)
+
+    def free_list(self) -> list:
+        return list(self._free)
+
+    def allocate(self) -> int:
+        if not self._free:
+            raise MemoryError("frame pool exhausted")
+        f = self._free.popleft()
+        self.ref[f] = 1
+        return f
+
+    def allocate_many(self, n: int) -> list:
+        """n frames in FIFO order, or MemoryError with nothing taken."""
+        if n > len(self._free):
+            raise MemoryError(f"frame pool exhausted: need {n}, have {len(self._free)}")
+        out = [self._free.popleft() for _ in range(n)]
+        self.ref[out] = 1
+        return out
+
+    def add_ref(self, frame: int) -> None:
+        self.ref[frame] += 1
+
+    def free(self, frame: int) -> None:
+        """Drop one reference; a frame reaching zero goes to the free tail.
+        Freeing a frame that holds no reference does nothing."""
+        if self.ref[frame] <= 0:
+            return
+        self.ref[frame] -= 1
+        if self.ref[frame] == 0:
+            self._free.append(frame)
+
+
+@dataclass(frozen=True)
+class AppendResult:
+    slot: int                    # where the new token's K/V rows go
+    cow_src: int | None = None   # frame to copy from (copy-on-write), or None
+    cow_dst: int | None = None   # the sequence's new private frame
+    cow_rows: int = 0            # rows of cow_src to copy (offsets 0 .. cow_rows - 1)
+
+
+class SeqManager:
+    """Per-sequence block tables and lengths over one BlockPool."""
+
+    def __init__(self, pool: BlockPool, block_size: int):
+        if block_size <= 0:
+            raise ValueError("block_size must be positive")
+        self.pool = pool
+        self.B = int(block_size)
+        self._tables: dict = {}
+        self._lens: dict = {}
+
+    # ------------------------------------------------------------ lifecycle
+    def init_sequence(self, sid, n_tokens: int) -> np.ndarray:
+        """Allocate ceil(n_tokens / B) frames; return the n_tokens slots."""
+        if sid in self._tables:
+            raise KeyError(f"sequence {sid!r} exists")
+        n_tokens = int(n_tokens)
+        frames = self.pool.allocate_many(-(-n_tokens // self.B))
+        self._tables[sid] = frames
+        self._lens[sid] = n_tokens
+        return self.slots(sid, np.arange(n_tokens))
+
+    def append_token(self, sid) -> AppendResult:
+        t = self._lens[sid]
+        table = self._tables[sid]
+        off = t % self.B
+        cow = (None, None, 0)
+        if off == 0:
+            table.append(self.pool.allocate())
+        else:
+            last = table[-1]
+            if self.pool.ref[last] > 1:
+                new = self.pool.allocate()
+                self.pool.free(last)
+                table[-1] = new
+                cow = (last, new, off)
+        self._lens[sid] = t + 1
+        return AppendResult(table[-1] * self.B + off, *cow)
+
+    def fork(self, parent, child) -> None:
+        if child in self._tables:
+            raise KeyError(f"sequence {child!r} exists")
+        table = self._tables[parent]
+        for f in table:
+            self.pool.add_ref(f)
+        self._tables[child] = list(table)
+        self._lens[child] = self._lens[parent]
+
+    def free_sequence(self, sid) -> None:
+        """Release a finished sequence's frames; unknown ids are ignored."""
+        table = self._tables.pop(sid, None)
+        if table is None:
+            return
+        del self._lens[sid]
+        for f in table:
+            self.pool.free(f)
+
+    # ------------------------------------------------------------ queries
+    def block_table(self, sid) -> list:
+        return list(self._tables[sid])
+
+    def context_len(self, sid) -> int:
+        return self._lens[sid]
+
+    def slots(self, sid, positions) -> np.ndarray:
+        """Slots (frame * B + offset) of token positions of a sequence."""
+        pos = np.asarray(positions, dtype=np.int64)
+        table = np.asarray(self._tables[sid], dtype=np.int64)
+        return table[pos // self.B] * self.B + pos % self.B
+
+    def tables(self, sids, pad: int, max_blocks: int | None = None) -> np.ndarray:
+        """int32 [len(sids), max_blocks] block tables, unused columns = pad."""
+        width = max((len(self._tables[s]) for s in sids), default=0)
+        mb = max(1, width if max_blocks is None else max_blocks)
+        if width > mb:
+            raise ValueError("max_blocks smaller than the longest table")
+        out = np.full((len(sids), mb), pad, dtype=np.int32)
+        for r, s in enumerate(sids):
+            t = self._tables[s]
+            out[r, :len(t)] = t
+        return out
+
+    def context_lens(self, sids) -> np.ndarray:
+        return np.array([self._lens[s] for s in sids], dtype=np.int32)
+
+    def waste_slots(self, sid) -> int:
+        """Allocated but unused slots of a sequence (< B by construction)."""
+        return len(self._tables[sid]) * self.B - self._lens[sid]
+
+
+def memory_efficiency(tokens: int, block_size: int) -> float:
+    """Used share of the slots allocated for ``tokens`` tokens (page 2's
+    "Performance Analysis" figure: B = 4 and 7 tokens give 7 / 8)."""
+    frames = -(-int(tokens) // int(block_size))
+    return tokens / (frames * block_size) if frames else 1.0

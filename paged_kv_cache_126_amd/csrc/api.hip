@@ -1,0 +1,240 @@
+// C ABI of the library (declared in include/paged_attn.h): argument checks,
+// launch sizing and dispatch. Every check uses host-known arguments only and
+// happens before anything is queued; nothing here synchronises the device.
+#include <cmath>
+#include <cstdint>
+
+#include "paged_attn.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int32_t kDefaultPartitionTokens = 256;
+constexpr int64_t kMaxGridYZ = 65535;
+constexpr size_t kWorkspaceAlign = 256;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_dtype(pa_dtype d) { return d == PA_F32 || d == PA_F16 || d == PA_BF16; }
+
+int64_t elem_bytes(pa_dtype d) { return d == PA_F32 ? 4 : 2; }
+
+pa::Dtype to_internal(pa_dtype d) {
+  return d == PA_F32 ? pa::Dtype::F32 : (d == PA_F16 ? pa::Dtype::F16 : pa::Dtype::BF16);
+}
+
+bool supported_head_dim(int32_t d) {
+  return d == 16 || d == 32 || d == 64 || d == 128 || d == 256;
+}
+
+// Shape validity apart from pointers; fills the partition size and count.
+pa_status check_shape(const pa_decode_shape* sh, int32_t* part_tokens, int32_t* max_parts) {
+  if (!sh) return PA_EINVAL;
+  if (sh->num_seqs < 0 || sh->num_heads <= 0 || sh->block_size <= 0 || sh->num_blocks <= 0 ||
+      sh->num_blocks > 0x7FFFFFFFLL ||
+      sh->max_blocks_per_seq <= 0 || sh->max_context_len < 0 || sh->partition_tokens < 0)
+    return PA_EINVAL;
+  if (!supported_head_dim(sh->head_dim) || !valid_dtype(sh->kv_dtype)) return PA_EINVAL;
+  if (sh->out_dtype != PA_F32 && sh->out_dtype != sh->kv_dtype) return PA_EINVAL;
+  if (static_cast<int64_t>(sh->max_context_len) >
+      static_cast<int64_t>(sh->max_blocks_per_seq) * sh->block_size)
+    return PA_EINVAL;
+  if (sh->num_seqs > kMaxGridYZ) return PA_EINVAL;
+  // One frame's bytes must fit 31 bits (the kernels address inside a frame
+  // with 32-bit offsets).
+  if (static_cast<int64_t>(sh->block_size) * sh->num_heads * sh->head_dim * elem_bytes(sh->kv_dtype) >
+      0x7FFFFFFFLL)
+    return PA_EINVAL;
+  const int chunk = pa::chunk_tokens(to_internal(sh->kv_dtype), sh->head_dim);
+  if (chunk <= 0) return PA_EINVAL;
+  int64_t pt = sh->partition_tokens > 0 ? sh->partition_tokens : kDefaultPartitionTokens;
+  pt = (pt + chunk - 1) / chunk * chunk;
+  if (pt > (1 << 30)) return PA_EINVAL;
+  // partition starts (part * pt) and ends stay in int32
+  if (static_cast<int64_t>(sh->max_context_len) + pt > 0x7FFFFFFFLL) return PA_EINVAL;
+  int64_t parts = sh->max_context_len <= pt ? 1 : (sh->max_context_len + pt - 1) / pt;
+  if (parts > kMaxGridYZ) return PA_EINVAL;
+  *part_tokens = static_cast<int32_t>(pt);
+  *max_parts = static_cast<int32_t>(parts);
+  return PA_OK;
+}
+
+size_t ml_bytes(const pa_decode_shape* sh, int32_t max_parts) {
+  size_t b = static_cast<size_t>(sh->num_seqs) * sh->num_heads * max_parts * 2 * sizeof(float);
+  return (b + kWorkspaceAlign - 1) / kWorkspaceAlign * kWorkspaceAlign;
+}
+
+size_t workspace_bytes_for(const pa_decode_shape* sh, int32_t max_parts) {
+  if (max_parts <= 1) return 0;
+  return ml_bytes(sh, max_parts) +
+         static_cast<size_t>(sh->num_seqs) * sh->num_heads * max_parts * sh->head_dim * sizeof(float);
+}
+
+pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
+
+// Shared validation and argument packing of the decode entry points.
+pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         int32_t block_size, float scale, void* out, const pa_decode_shape* sh,
+                         void* workspace, size_t workspace_bytes, pa::DecodeArgs* a) {
+  int32_t pt = 0, parts = 0;
+  pa_status st = check_shape(sh, &pt, &parts);
+  if (st != PA_OK) return st;
+  if (block_size != sh->block_size || !std::isfinite(scale)) return PA_EINVAL;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_EINVAL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, static_cast<uintptr_t>(elem_bytes(sh->out_dtype))) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_EALIGN;
+  const size_t need = workspace_bytes_for(sh, parts);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kWorkspaceAlign)))
+    return PA_EWORKSPACE;
+  a->q = q;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->out = out;
+  a->ws_ml = need ? static_cast<float*>(workspace) : nullptr;
+  a->ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes(sh, parts))
+                   : nullptr;
+  a->num_blocks = sh->num_blocks;
+  a->scale_log2 = scale * 1.4426950408889634f;  // log2(e)
+  a->num_seqs = sh->num_seqs;
+  a->block_size = sh->block_size;
+  a->num_heads = sh->num_heads;
+  a->max_blocks = sh->max_blocks_per_seq;
+  a->max_ctx = sh->max_context_len;
+  a->part_tokens = pt;
+  a->max_parts = parts;
+  a->out_f32 = sh->out_dtype == PA_F32 ? 1 : 0;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_EINVAL: return "PA_EINVAL: invalid argument or unsupported shape/dtype";
+    case PA_EALIGN: return "PA_EALIGN: misaligned pointer";
+    case PA_EWORKSPACE: return "PA_EWORKSPACE: workspace missing or too small";
+    case PA_EHIP: return "PA_EHIP: HIP launch error";
+  }
+  return "unknown pa_status";
+}
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+pa_status kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                    void* k_cache, void* v_cache, int64_t num_tokens, int32_t num_heads,
+                    int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype,
+                    void* stream) {
+  if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      !valid_dtype(dtype))
+    return PA_EINVAL;
+  const int64_t row_bytes = static_cast<int64_t>(num_heads) * head_dim * elem_bytes(dtype);
+  if ((static_cast<int64_t>(head_dim) * elem_bytes(dtype)) % 16 != 0) return PA_EINVAL;
+  if (num_tokens > 0x7FFFFFFF) return PA_EINVAL;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_EINVAL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(slot_mapping, 8))
+    return PA_EALIGN;
+  return from_hip(pa::launch_kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, num_tokens,
+                                       row_bytes, num_blocks * block_size,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t paged_attn_workspace_size(const pa_decode_shape* shape) {
+  int32_t pt = 0, parts = 0;
+  if (check_shape(shape, &pt, &parts) != PA_OK) return 0;
+  return workspace_bytes_for(shape, parts);
+}
+
+int32_t paged_attn_partition_tokens(const pa_decode_shape* shape) {
+  int32_t pt = 0, parts = 0;
+  if (check_shape(shape, &pt, &parts) != PA_OK) return 0;
+  return pt;
+}
+
+pa_status paged_attn_decode_partitions(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* context_lens,
+                                       int32_t block_size, float scale, void* out,
+                                       const pa_decode_shape* shape, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  pa::DecodeArgs a;
+  pa_status st = prepare_decode(q, k_cache, v_cache, block_tables, context_lens, block_size,
+                                scale, out, shape, workspace, workspace_bytes, &a);
+  if (st != PA_OK) return st;
+  if (shape->num_seqs == 0) return PA_OK;
+  return from_hip(pa::launch_decode_partitions(a, to_internal(shape->kv_dtype), shape->head_dim,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+pa_status paged_attn_merge(const int32_t* context_lens, void* out, const pa_decode_shape* shape,
+                           const void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t pt = 0, parts = 0;
+  pa_status st = check_shape(shape, &pt, &parts);
+  if (st != PA_OK) return st;
+  if (!context_lens || !out) return PA_EINVAL;
+  if (!aligned(out, static_cast<uintptr_t>(elem_bytes(shape->out_dtype))) ||
+      !aligned(context_lens, 4))
+    return PA_EALIGN;
+  const size_t need = workspace_bytes_for(shape, parts);
+  if (need == 0 || shape->num_seqs == 0) return PA_OK;  // nothing was split
+  if (!workspace || workspace_bytes < need || !aligned(workspace, kWorkspaceAlign))
+    return PA_EWORKSPACE;
+  pa::DecodeArgs a = {};
+  a.context_lens = context_lens;
+  a.out = out;
+  a.ws_ml = static_cast<float*>(const_cast<void*>(workspace));
+  a.ws_acc = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
+                                      ml_bytes(shape, parts));
+  a.num_seqs = shape->num_seqs;
+  a.num_heads = shape->num_heads;
+  a.max_ctx = shape->max_context_len;
+  a.part_tokens = pt;
+  a.max_parts = parts;
+  a.out_f32 = shape->out_dtype == PA_F32 ? 1 : 0;
+  return from_hip(pa::launch_decode_merge(a, to_internal(shape->kv_dtype), shape->head_dim,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+pa_status paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t block_size, float scale, void* out,
+                            const pa_decode_shape* shape, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  pa_status st = paged_attn_decode_partitions(q, k_cache, v_cache, block_tables, context_lens,
+                                              block_size, scale, out, shape, workspace,
+                                              workspace_bytes, stream);
+  if (st != PA_OK) return st;
+  return paged_attn_merge(context_lens, out, shape, workspace, workspace_bytes, stream);
+}
+
+pa_status paged_gather(const void* cache, const int32_t* block_tables,
+                       const int32_t* context_lens, const int64_t* out_row_start, void* out,
+                       int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,
+                       int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                       pa_dtype dtype, void* stream) {
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      num_blocks > 0x7FFFFFFFLL || max_blocks_per_seq <= 0 || max_context_len < 0 || !valid_dtype(dtype))
+    return PA_EINVAL;
+  if ((static_cast<int64_t>(head_dim) * elem_bytes(dtype)) % 16 != 0) return PA_EINVAL;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return PA_EINVAL;
+  if (num_seqs > kMaxGridYZ) return PA_EINVAL;
+  if (num_seqs == 0 || max_context_len == 0) return PA_OK;
+  if (!cache || !block_tables || !context_lens || !out_row_start || !out) return PA_EINVAL;
+  if (!aligned(cache, 16) || !aligned(out, 16)) return PA_EALIGN;
+  const int64_t row_bytes = static_cast<int64_t>(num_heads) * head_dim * elem_bytes(dtype);
+  return from_hip(pa::launch_gather(cache, block_tables, context_lens, out_row_start, out,
+                                    num_seqs, row_bytes, block_size, num_blocks,
+                                    max_blocks_per_seq, max_context_len,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

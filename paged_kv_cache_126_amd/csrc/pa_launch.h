@@ -1,0 +1,53 @@
+// Host-side launchers of the library's kernels (internal interface between
+// the C ABI layer and the kernel translation units).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything one decode launch needs, passed to the kernels by value.
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  float* ws_ml;   // [S, H, max_parts, 2]: running max (log2 units) and sum per partition
+  float* ws_acc;  // [S, H, max_parts, D]: unnormalised output per partition
+  int64_t num_blocks;
+  float scale_log2;  // scale * log2(e): scores are kept in base-2 exponent units
+  int32_t num_seqs;
+  int32_t block_size;
+  int32_t num_heads;
+  int32_t max_blocks;
+  int32_t max_ctx;
+  int32_t part_tokens;
+  int32_t max_parts;
+  int32_t out_f32;  // 1: out is fp32; 0: out has the cache dtype
+};
+
+enum class Dtype : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+// Tokens one wavefront processes per loop iteration for (dtype, head_dim);
+// partition sizes are multiples of it. 0 if the combination is unsupported.
+int chunk_tokens(Dtype dt, int head_dim);
+
+// Queue the partition pass / the merge pass. Return a hipError_t.
+hipError_t launch_decode_partitions(const DecodeArgs& a, Dtype dt, int head_dim,
+                                    hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs& a, Dtype dt, int head_dim, hipStream_t stream);
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots,
+                            void* k_cache, void* v_cache, int64_t num_tokens, int64_t row_bytes,
+                            int64_t num_slots, hipStream_t stream);
+
+hipError_t launch_gather(const void* cache, const int32_t* block_tables,
+                         const int32_t* context_lens, const int64_t* out_row_start, void* out,
+                         int32_t num_seqs, int64_t row_bytes, int32_t block_size,
+                         int64_t num_blocks, int32_t max_blocks, int32_t max_ctx,
+                         hipStream_t stream);
+
+}  // namespace pa

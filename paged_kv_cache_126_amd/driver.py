@@ -1,0 +1,131 @@
+"""Plays a decode schedule through the block manager and the library.
+
+A schedule is any object with the attributes ``NB``, ``B``, ``num_seqs``,
+``prefill`` ([(seq, n_tokens)]), ``forks`` ([(parent, child)]), ``steps``
+(per decode step, the sequences appending one token, in order),
+``attend_after`` (step indices after which attention runs; -1 = after the
+prefill) and ``frame_order`` (initial free list or None).
+
+:func:`plan` runs only the host block manager and returns the ordered list of
+KV writes and attention points: what a serving loop would hand the device.
+:class:`DeviceCache` plus :func:`execute` carry the writes out on the GPU with
+``kv_append`` (copy-on-write copies are re-appends of the copied rows).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .block_manager import BlockPool, SeqManager
+
+
+@dataclass
+class WriteBatch:
+    seqs: np.ndarray       # int64 [N]: sequence of each row
+    positions: np.ndarray  # int64 [N]: token position inside that sequence
+    slots: np.ndarray      # int64 [N]: destination slot (frame * B + offset)
+
+
+@dataclass
+class AttendPoint:
+    step: int                 # index in schedule.attend_after order
+    tables: np.ndarray        # int32 [S, max_blocks]
+    context_lens: np.ndarray  # int32 [S]
+
+
+def plan(schedule, pad: int = -1, max_blocks: int | None = None):
+    """Host-only replay. Returns (events, manager); each event is a
+    WriteBatch or an AttendPoint, in the order a serving loop issues them."""
+    pool = BlockPool(schedule.NB, schedule.frame_order)
+    mgr = SeqManager(pool, schedule.B)
+    B = schedule.B
+    sids = list(range(schedule.num_seqs))
+    events = []
+    seqs, poss, slots = [], [], []
+
+    def flush():
+        if seqs:
+            events.append(WriteBatch(np.concatenate(seqs), np.concatenate(poss), np.concatenate(slots)))
+            seqs.clear(), poss.clear(), slots.clear()
+
+    n_attend = 0
+
+    def attend():
+        nonlocal n_attend
+        flush()
+        events.append(AttendPoint(n_attend, mgr.tables(sids, pad, max_blocks), mgr.context_lens(sids)))
+        n_attend += 1
+
+    for s, n in schedule.prefill:
+        sl = mgr.init_sequence(s, n)
+        seqs.append(np.full(n, s, dtype=np.int64))
+        poss.append(np.arange(n, dtype=np.int64))
+        slots.append(sl)
+    for parent, child in schedule.forks:
+        mgr.fork(parent, child)
+    if -1 in schedule.attend_after:
+        attend()
+    else:
+        flush()
+    for k, step in enumerate(schedule.steps):
+        for s in step:
+            t = mgr.context_len(s)
+            r = mgr.append_token(s)
+            if r.cow_src is not None:
+                # copy-on-write: the new private frame receives the rows the
+                # shared frame held at offsets 0 .. cow_rows - 1
+                first = t - r.cow_rows
+                seqs.append(np.full(r.cow_rows, s, dtype=np.int64))
+                poss.append(np.arange(first, t, dtype=np.int64))
+                slots.append(r.cow_dst * B + np.arange(r.cow_rows, dtype=np.int64))
+            seqs.append(np.array([s], dtype=np.int64))
+            poss.append(np.array([t], dtype=np.int64))
+            slots.append(np.array([r.slot], dtype=np.int64))
+        if k in schedule.attend_after:
+            attend()
+        else:
+            flush()
+    flush()
+    return events, mgr
+
+
+class DeviceCache:
+    """K and V caches [NB, B, H, D] in device memory, optionally NaN-filled."""
+
+    def __init__(self, NB: int, B: int, H: int, D: int, dtype, device="cuda", poison: bool = True):
+        import torch
+
+        self.k = torch.empty((NB, B, H, D), dtype=dtype, device=device)
+        self.v = torch.empty_like(self.k)
+        if poison:
+            self.k.fill_(float("nan"))
+            self.v.fill_(float("nan"))
+        self.B = B
+
+    def append(self, k_new, v_new, slots, stream=None) -> None:
+        from .lib import kv_append
+
+        kv_append(k_new, v_new, slots, self.k, self.v, stream=stream)
+
+
+def execute(events, cache: DeviceCache, rows, on_attend, chunk_rows: int = 1 << 16) -> None:
+    """Apply the events on the device.
+
+    ``rows(seqs, positions)`` returns device tensors (k_new, v_new) [N, H, D]
+    for those tokens; ``on_attend(point)`` is called at each AttendPoint once
+    every earlier write has been queued. Large write batches are applied in
+    chunks of ``chunk_rows`` tokens.
+    """
+    import torch
+
+    dev = cache.k.device
+    for ev in events:
+        if isinstance(ev, WriteBatch):
+            for lo in range(0, len(ev.slots), chunk_rows):
+                hi = min(lo + chunk_rows, len(ev.slots))
+                k_new, v_new = rows(ev.seqs[lo:hi], ev.positions[lo:hi])
+                sl = torch.from_numpy(np.ascontiguousarray(ev.slots[lo:hi])).to(dev)
+                cache.append(k_new, v_new, sl)
+        else:
+            on_attend(ev)

@@ -1,0 +1,202 @@
+"""ctypes binding of ``libpaged_attn.so`` (C ABI in include/paged_attn.h).
+
+Argument marshalling only: every step of the hot path runs in the library's
+HIP kernels. torch tensors supply device pointers and the current stream;
+nothing here computes on them. If the library is missing the functions raise
+immediately; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpaged_attn.so")
+
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+STATUS = {0: "PA_OK", -1: "PA_EINVAL", -2: "PA_EALIGN", -3: "PA_EWORKSPACE", -4: "PA_EHIP"}
+
+EXPORTS = (
+    "pa_status_string", "pa_abi_version", "kv_append", "paged_attn_workspace_size",
+    "paged_attn_partition_tokens", "paged_attn_decode", "paged_attn_decode_partitions",
+    "paged_attn_merge", "paged_gather",
+)
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, func: str, status: int):
+        super().__init__(f"{func} returned {STATUS.get(status, status)}")
+        self.status = status
+
+
+class DecodeShape(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_context_len", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int),
+        ("out_dtype", ctypes.c_int),
+        ("partition_tokens", ctypes.c_int32),
+    ]
+
+
+_LIB = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library once; raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with paged_kv_cache_126_amd/build.py")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    SH = ctypes.POINTER(DecodeShape)
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_abi_version.argtypes = []
+    lib.pa_abi_version.restype = I32
+    lib.kv_append.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I64, ctypes.c_int, P]
+    lib.kv_append.restype = ctypes.c_int
+    lib.paged_attn_workspace_size.argtypes = [SH]
+    lib.paged_attn_workspace_size.restype = SZ
+    lib.paged_attn_partition_tokens.argtypes = [SH]
+    lib.paged_attn_partition_tokens.restype = I32
+    dec = [P, P, P, P, P, I32, F, P, SH, P, SZ, P]
+    for name in ("paged_attn_decode", "paged_attn_decode_partitions"):
+        getattr(lib, name).argtypes = dec
+        getattr(lib, name).restype = ctypes.c_int
+    lib.paged_attn_merge.argtypes = [P, P, SH, P, SZ, P]
+    lib.paged_attn_merge.restype = ctypes.c_int
+    lib.paged_gather.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32, I32, ctypes.c_int, P]
+    lib.paged_gather.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _check(func: str, status: int) -> None:
+    if status != 0:
+        raise PagedAttnError(func, status)
+
+
+def dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dense(*tensors) -> None:
+    for t in tensors:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def make_shape(q, k_cache, block_tables, max_context_len: int, out_dtype_code: int | None = None,
+               partition_tokens: int = 0) -> DecodeShape:
+    S, H, D = q.shape
+    NB, B = k_cache.shape[0], k_cache.shape[1]
+    kv = dtype_code(k_cache)
+    return DecodeShape(S, H, D, B, NB, block_tables.shape[1], int(max_context_len), kv,
+                       kv if out_dtype_code is None else out_dtype_code, int(partition_tokens))
+
+
+def workspace_size(shape: DecodeShape) -> int:
+    return int(load().paged_attn_workspace_size(ctypes.byref(shape)))
+
+
+def partition_tokens(shape: DecodeShape) -> int:
+    return int(load().paged_attn_partition_tokens(ctypes.byref(shape)))
+
+
+def alloc_workspace(shape: DecodeShape, device=None):
+    """A device buffer big enough for ``shape`` (None when none is needed)."""
+    import torch
+
+    n = workspace_size(shape)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """Write ``k_new``/``v_new`` ``[N, H, D]`` rows into their slots (int64 ``[N]``)."""
+    _dense(k_new, v_new, slot_mapping, k_cache, v_cache)
+    N, H, D = k_new.shape
+    NB, B = k_cache.shape[0], k_cache.shape[1]
+    if k_cache.shape != (NB, B, H, D) or v_cache.shape != k_cache.shape or v_new.shape != k_new.shape:
+        raise ValueError("shape mismatch")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("dtype mismatch")
+    if slot_mapping.shape != (N,) or str(slot_mapping.dtype) != "torch.int64":
+        raise TypeError("slot_mapping must be int64 [N]")
+    _check("kv_append", load().kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
+                                         _ptr(v_cache), N, H, D, B, NB, dtype_code(k_cache),
+                                         _stream(stream)))
+
+
+def _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out):
+    _dense(q, k_cache, v_cache, block_tables, context_lens, out)
+    S, H, D = q.shape
+    if k_cache.shape[2:] != (H, D) or v_cache.shape != k_cache.shape or out.shape != (S, H, D):
+        raise ValueError("shape mismatch")
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("q, k_cache and v_cache must share a dtype")
+    if str(block_tables.dtype) != "torch.int32" or str(context_lens.dtype) != "torch.int32":
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables / context_lens do not match q")
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_size: int, scale: float,
+                      out, max_context_len: int, workspace=None, partition_tokens: int = 0,
+                      stream=None, phase: str = "both") -> None:
+    """Decode attention into ``out``; see include/paged_attn.h.
+
+    ``phase`` selects "both" (paged_attn_decode), "partitions" or "merge"
+    (the two launches it is made of).
+    """
+    _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out)
+    shape = make_shape(q, k_cache, block_tables, max_context_len, dtype_code(out), partition_tokens)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    lib = load()
+    st = _stream(stream)
+    if phase == "merge":
+        _check("paged_attn_merge", lib.paged_attn_merge(_ptr(context_lens), _ptr(out),
+                                                        ctypes.byref(shape), _ptr(workspace),
+                                                        ws_bytes, st))
+        return
+    fn = {"both": "paged_attn_decode", "partitions": "paged_attn_decode_partitions"}[phase]
+    _check(fn, getattr(lib, fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                _ptr(context_lens), int(block_size), float(scale), _ptr(out),
+                                ctypes.byref(shape), _ptr(workspace), ws_bytes, st))
+
+
+def paged_gather(cache, block_tables, context_lens, out_row_start, out, max_context_len: int,
+                 stream=None) -> None:
+    """Copy each sequence's rows, in logical order, into ``out`` ``[T, H, D]``."""
+    _dense(cache, block_tables, context_lens, out_row_start, out)
+    NB, B, H, D = cache.shape
+    S = context_lens.shape[0]
+    _check("paged_gather", load().paged_gather(_ptr(cache), _ptr(block_tables), _ptr(context_lens),
+                                               _ptr(out_row_start), _ptr(out), S, H, D, B, NB,
+                                               block_tables.shape[1], int(max_context_len),
+                                               dtype_code(cache), _stream(stream)))

@@ -1,0 +1,111 @@
+"""The C-ABI library loads, exports what include/paged_attn.h declares, and
+rejects bad arguments before launching anything (CPU only: no kernel runs)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_126_amd as pkv
+from paged_kv_cache_126_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("kv_append", "paged_attn_decode", "paged_attn_workspace_size", "pa_status_string"):
+        assert n in names
+    assert set(names) == set(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pkv.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.pa_abi_version() == 1
+
+
+def test_status_strings():
+    lib = pkv.load()
+    for code in (0, -1, -2, -3, -4):
+        assert lib.pa_status_string(code).decode().startswith(L.STATUS[code])
+
+
+def shape(**kw):
+    base = dict(num_seqs=64, num_heads=32, head_dim=128, block_size=16, num_blocks=20000,
+                max_blocks_per_seq=128, max_context_len=2048, kv_dtype=L.PA_BF16,
+                out_dtype=L.PA_F32, partition_tokens=0)
+    base.update(kw)
+    return L.DecodeShape(**base)
+
+
+def test_workspace_and_partition_sizing():
+    sh = shape()
+    pt = pkv.partition_tokens(sh)
+    assert pt > 0 and pt % 16 == 0
+    parts = -(-2048 // pt)
+    ml = 64 * 32 * parts * 2 * 4
+    ml = -(-ml // 256) * 256
+    assert pkv.workspace_size(sh) == ml + 64 * 32 * parts * 128 * 4
+    # everything fits one partition: no workspace
+    assert pkv.workspace_size(shape(max_context_len=pt)) == 0
+    # partition sizes round up to the tiling (64 tokens per chunk for fp32 d=16)
+    assert pkv.partition_tokens(shape(head_dim=16, kv_dtype=L.PA_F32, out_dtype=L.PA_F32,
+                                      block_size=10, max_context_len=40,
+                                      max_blocks_per_seq=4, partition_tokens=70)) == 128
+
+
+@pytest.mark.parametrize("bad", [
+    dict(head_dim=96), dict(head_dim=8), dict(kv_dtype=7), dict(out_dtype=L.PA_F16),
+    dict(max_context_len=2049), dict(num_heads=0), dict(block_size=0), dict(num_blocks=0),
+    dict(num_blocks=1 << 32), dict(partition_tokens=-1), dict(num_seqs=70000),
+    dict(block_size=65536, num_heads=64, head_dim=256, max_context_len=4096, max_blocks_per_seq=1),
+])
+def test_invalid_shapes(bad):
+    assert pkv.workspace_size(shape(**bad)) == 0
+    assert pkv.partition_tokens(shape(**bad)) == 0
+    lib = pkv.load()
+    p = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    sh = shape(**bad)
+    rc = lib.paged_attn_decode(p, p, p, p, p, sh.block_size, 0.1, p, ctypes.byref(sh), p, 1 << 30, None)
+    assert rc == -1
+
+
+def test_decode_argument_errors():
+    lib = pkv.load()
+    sh = shape()
+    p = ctypes.c_void_p(1 << 20)
+    args = lambda **o: [o.get("q", p), o.get("k", p), o.get("v", p), o.get("bt", p), o.get("cl", p),
+                        o.get("B", 16), o.get("scale", 0.088), o.get("out", p),
+                        ctypes.byref(sh), o.get("ws", p), o.get("wsb", 1 << 30), None]
+    assert lib.paged_attn_decode(*args(q=None)) == -1
+    assert lib.paged_attn_decode(*args(out=None)) == -1
+    assert lib.paged_attn_decode(*args(B=32)) == -1               # disagrees with the shape
+    assert lib.paged_attn_decode(*args(scale=float("nan"))) == -1
+    assert lib.paged_attn_decode(*args(k=ctypes.c_void_p((1 << 20) + 8))) == -2
+    assert lib.paged_attn_decode(*args(ws=None)) == -3
+    assert lib.paged_attn_decode(*args(wsb=16)) == -3
+    assert lib.paged_attn_decode(*args(ws=ctypes.c_void_p((1 << 20) + 16))) == -3
+    assert lib.paged_attn_decode(None, p, p, p, p, 16, 0.1, p, None, p, 0, None) == -1
+
+
+def test_append_and_gather_argument_errors():
+    lib = pkv.load()
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.kv_append(p, p, p, p, p, 0, 32, 128, 16, 100, L.PA_BF16, None) == 0  # no tokens
+    assert lib.kv_append(None, p, p, p, p, 4, 32, 128, 16, 100, L.PA_BF16, None) == -1
+    assert lib.kv_append(p, p, p, p, p, 4, 32, 128, 16, 100, 9, None) == -1
+    assert lib.kv_append(p, p, p, p, p, 4, 1, 4, 16, 100, L.PA_F16, None) == -1  # 8-byte rows
+    assert lib.kv_append(ctypes.c_void_p((1 << 20) + 4), p, p, p, p, 4, 32, 128, 16, 100,
+                         L.PA_BF16, None) == -2
+    assert lib.paged_gather(p, p, p, p, p, 2, 2, 16, 10, 100, 2, 21, L.PA_F32, None) == -1
+    assert lib.paged_gather(p, p, p, p, p, 0, 2, 16, 10, 100, 2, 20, L.PA_F32, None) == 0
+    assert lib.paged_gather(None, p, p, p, p, 2, 2, 16, 10, 100, 2, 20, L.PA_F32, None) == -1

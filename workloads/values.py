@@ -94,16 +94,19 @@ def quantile_table(dtype: str) -> np.ndarray:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def draw_np(seed: int, stream: int, idents, H: int, D: int, dtype: str) -> np.ndarray:
+def draw_np(seed: int, stream: int, idents, H: int, D: int, dtype: str, heads=None) -> np.ndarray:
     """Values for identities ``idents`` as a host array ``[len(idents), H, D]``.
 
-    float32 for "f32"; uint16 bit patterns for "f16" and "bf16".
+    float32 for "f32"; uint16 bit patterns for "f16" and "bf16". With
+    ``heads`` given, only those heads are drawn: ``[len(idents), len(heads), D]``
+    holding exactly the values the full draw has at those heads.
     """
     idents = np.asarray(idents, dtype=np.int64).reshape(-1)
-    hd = np.arange(H * D, dtype=np.int64)
+    hs = np.arange(H, dtype=np.int64) if heads is None else np.asarray(heads, dtype=np.int64)
+    hd = (hs[:, None] * D + np.arange(D, dtype=np.int64)[None, :]).reshape(-1)
     counter = idents[:, None] * (H * D) + hd[None, :]
     idx = _index16(counter, stream_key(seed, stream))
-    return quantile_table(dtype)[idx].reshape(len(idents), H, D)
+    return quantile_table(dtype)[idx].reshape(len(idents), len(hs), D)
 
 
 _TORCH_TABLES: dict = {}
