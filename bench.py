@@ -2,7 +2,7 @@
 
 One step is one decode-attention pass over the whole batch (the partition
 kernel, then the log-sum-exp merge kernel) with the KV cache already resident
-in HBM. Before every step a 2 GiB buffer is rewritten so the step starts with
+in HBM. Before every step a 2 GiB buffer is read so the step starts with
 cold caches (MI355X has a 256 MB last-level cache); the step itself is timed
 with HIP events on the stream the kernels run on. Prints one JSON line.
 
@@ -113,6 +113,9 @@ def main():
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="first run one plain device-to-device copy of BYTES (a known-size "
+                         "reference for hardware traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
@@ -162,7 +165,22 @@ def main():
     part_tokens = pkv.partition_tokens(shape)
     sum_ctx = int(pt.context_lens.sum())
     kv_bytes = 2 * w.H * w.D * w.elem_bytes * sum_ctx
-    flush_buf = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    # Cache flush between steps: read a 2 GiB buffer (8x the 256 MB last-level
+    # cache). A read leaves clean lines; a write would leave dirty lines whose
+    # write-back competes with the timed step.
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy of {args.copy_calibration} bytes done")
+    flush_buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush():
+        torch.sum(flush_buf, dim=0, out=flush_sink)
 
     def step(evs=None):
         if evs is not None:
@@ -178,7 +196,7 @@ def main():
 
     for i in range(args.warmup):
         if not args.no_flush:
-            flush_buf.fill_(i & 0xFF)
+            flush()
         step()
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
@@ -188,7 +206,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         if not args.no_flush:
-            flush_buf.fill_((i + 1) & 0xFF)
+            flush()
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int32_t kDefaultPartitionTokens = 256;
+constexpr int32_t kDefaultPartitionTokens = 512;
 constexpr int64_t kMaxGridYZ = 65535;
 constexpr size_t kWorkspaceAlign = 256;
 

@@ -40,6 +40,12 @@ __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Streaming load: the row is read once, so it is marked non-temporal and
+// does not displace reusable lines in the caches.
+__device__ __forceinline__ u32x4 load16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ void store16(void* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }

@@ -36,7 +36,7 @@ namespace pa {
 namespace {
 
 constexpr float kNegBig = -1.0e30f;
-constexpr int kNW = 4;  // wavefronts per workgroup
+constexpr int kNW = 8;  // wavefronts per workgroup
 constexpr int kU = 4;   // row loads per lane per chunk (for each of K and V)
 
 template <typename T, int D>
@@ -127,8 +127,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(DecodeArgs a
       for (int u = 0; u < kU; ++u) {
         u32x4 kz = {0u, 0u, 0u, 0u}, vz = {0u, 0u, 0u, 0u};
         if (valid[u]) {
-          kz = load16(kbase + step_base[u] + lane_off);
-          vz = load16(vbase + step_base[u] + lane_off);
+          kz = load16_stream(kbase + step_base[u] + lane_off);
+          vz = load16_stream(vbase + step_base[u] + lane_off);
         }
         kv[u] = kz;
         vv[u] = vz;
@@ -141,8 +141,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(DecodeArgs a
           const int64_t off =
               token_row(table_row, t0 + u * RPL + grp, a.block_size, a.num_blocks) * row_bytes +
               lane_bytes;
-          kz = load16(kbase + off);
-          vz = load16(vbase + off);
+          kz = load16_stream(kbase + off);
+          vz = load16_stream(vbase + off);
         }
         kv[u] = kz;
         vv[u] = vz;
