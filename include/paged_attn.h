@@ -66,6 +66,15 @@ typedef enum pa_dtype {
   PA_BF16 = 2
 } pa_dtype;
 
+/* How the decode kernel reads the caches. */
+typedef enum pa_cache_policy {
+  PA_CACHE_STREAM = 0,  /* each frame is read once per call: non-temporal loads
+                           that leave the caches to other data (default) */
+  PA_CACHE_REUSE = 1    /* sequences of the call share frames (forked prefixes):
+                           ordinary loads, so a frame read for one sequence can
+                           be served from cache for the others */
+} pa_cache_policy;
+
 typedef enum pa_status {
   PA_OK = 0,
   PA_EINVAL = -1,      /* null pointer, non-positive size, or an unsupported
@@ -86,8 +95,10 @@ typedef struct pa_decode_shape {
   int32_t max_context_len;     /* host-known bound on context_lens; sizes the launch */
   pa_dtype kv_dtype;           /* dtype of q, k_cache and v_cache */
   pa_dtype out_dtype;          /* PA_F32, or kv_dtype (rounded to nearest even) */
-  int32_t partition_tokens;    /* tokens per context partition; 0 = library default.
-                                  Rounded up to what the kernel's tiling needs. */
+  int32_t partition_tokens;    /* tokens per context partition; 0 = chosen by the
+                                  library from the shape. Rounded up to what the
+                                  kernel's tiling needs. */
+  int32_t cache_policy;        /* a pa_cache_policy value */
 } pa_decode_shape;
 
 /* Human-readable name of a status code. Never NULL. */

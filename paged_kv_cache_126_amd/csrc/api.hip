@@ -9,7 +9,14 @@
 
 namespace {
 
-constexpr int32_t kDefaultPartitionTokens = 512;
+// Default partition size: the largest of 2048, 1024, 512 tokens that still
+// yields about kTargetWorkgroups workgroups (32 per compute unit of a 256-CU
+// MI355X), estimated from the host-known bound max_context_len. Long
+// partitions write fewer partial results; enough workgroups keep every CU
+// busy until the end of the launch.
+constexpr int32_t kMaxDefaultPartition = 2048;
+constexpr int32_t kMinDefaultPartition = 512;
+constexpr int64_t kTargetWorkgroups = 8192;
 constexpr int64_t kMaxGridYZ = 65535;
 constexpr size_t kWorkspaceAlign = 256;
 
@@ -47,7 +54,15 @@ pa_status check_shape(const pa_decode_shape* sh, int32_t* part_tokens, int32_t* 
     return PA_EINVAL;
   const int chunk = pa::chunk_tokens(to_internal(sh->kv_dtype), sh->head_dim);
   if (chunk <= 0) return PA_EINVAL;
-  int64_t pt = sh->partition_tokens > 0 ? sh->partition_tokens : kDefaultPartitionTokens;
+  if (sh->cache_policy != PA_CACHE_STREAM && sh->cache_policy != PA_CACHE_REUSE) return PA_EINVAL;
+  int64_t pt = sh->partition_tokens;
+  if (pt == 0) {
+    pt = kMaxDefaultPartition;
+    const int64_t pairs = static_cast<int64_t>(sh->num_seqs) * sh->num_heads;
+    while (pt > kMinDefaultPartition &&
+           pairs * ((sh->max_context_len + pt - 1) / pt) < kTargetWorkgroups)
+      pt /= 2;
+  }
   pt = (pt + chunk - 1) / chunk * chunk;
   if (pt > (1 << 30)) return PA_EINVAL;
   // partition starts (part * pt) and ends stay in int32
@@ -108,6 +123,7 @@ pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache
   a->part_tokens = pt;
   a->max_parts = parts;
   a->out_f32 = sh->out_dtype == PA_F32 ? 1 : 0;
+  a->stream_loads = sh->cache_policy == PA_CACHE_STREAM ? 1 : 0;
   return PA_OK;
 }
 

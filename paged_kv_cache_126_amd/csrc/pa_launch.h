@@ -27,6 +27,7 @@ struct DecodeArgs {
   int32_t part_tokens;
   int32_t max_parts;
   int32_t out_f32;  // 1: out is fp32; 0: out has the cache dtype
+  int32_t stream_loads;  // 1: non-temporal K/V loads; 0: ordinary cached loads
 };
 
 enum class Dtype : int { F32 = 0, F16 = 1, BF16 = 2 };

@@ -39,6 +39,14 @@ constexpr float kNegBig = -1.0e30f;
 constexpr int kNW = 8;  // wavefronts per workgroup
 constexpr int kU = 4;   // row loads per lane per chunk (for each of K and V)
 
+template <bool kStream>
+__device__ __forceinline__ u32x4 load_row(const char* p) {
+  if constexpr (kStream)
+    return load16_stream(p);
+  else
+    return load16(p);
+}
+
 template <typename T, int D>
 struct Tiling {
   static constexpr int kVEC = Vec<T>::kElems;  // elements a lane holds per row
@@ -48,7 +56,9 @@ struct Tiling {
   static_assert(kLPR >= 1 && kLPR <= 64 && (64 % kLPR) == 0, "row must tile a wavefront");
 };
 
-template <typename T, int D, int BT>
+// kStream selects non-temporal K/V loads (frames read once) or ordinary
+// cached loads (frames shared by several sequences of the call).
+template <typename T, int D, int BT, bool kStream>
 __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(DecodeArgs a) {
   using Tl = Tiling<T, D>;
   constexpr int VEC = Tl::kVEC, LPR = Tl::kLPR, RPL = Tl::kRPL, CH = Tl::kCH;
@@ -127,8 +137,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(DecodeArgs a
       for (int u = 0; u < kU; ++u) {
         u32x4 kz = {0u, 0u, 0u, 0u}, vz = {0u, 0u, 0u, 0u};
         if (valid[u]) {
-          kz = load16_stream(kbase + step_base[u] + lane_off);
-          vz = load16_stream(vbase + step_base[u] + lane_off);
+          kz = load_row<kStream>(kbase + step_base[u] + lane_off);
+          vz = load_row<kStream>(vbase + step_base[u] + lane_off);
         }
         kv[u] = kz;
         vv[u] = vz;
@@ -141,8 +151,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(DecodeArgs a
           const int64_t off =
               token_row(table_row, t0 + u * RPL + grp, a.block_size, a.num_blocks) * row_bytes +
               lane_bytes;
-          kz = load16_stream(kbase + off);
-          vz = load16_stream(vbase + off);
+          kz = load_row<kStream>(kbase + off);
+          vz = load_row<kStream>(vbase + off);
         }
         kv[u] = kz;
         vv[u] = vz;
@@ -287,7 +297,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 template <typename T, int D, int BT>
 hipError_t launch_part(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.num_heads, a.max_parts, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, BT>), grid, dim3(kNW * 64), 0, stream, a);
+  if (a.stream_loads)
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, BT, true>), grid, dim3(kNW * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, BT, false>), grid, dim3(kNW * 64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -32,6 +32,14 @@ class AttendPoint:
     step: int                 # index in schedule.attend_after order
     tables: np.ndarray        # int32 [S, max_blocks]
     context_lens: np.ndarray  # int32 [S]
+    shared_frames: bool = False  # some frame is referenced by two or more sequences
+
+    @property
+    def cache_policy(self) -> int:
+        """The decode cache hint that fits these tables (see pa_cache_policy)."""
+        from .lib import PA_CACHE_REUSE, PA_CACHE_STREAM
+
+        return PA_CACHE_REUSE if self.shared_frames else PA_CACHE_STREAM
 
 
 def plan(schedule, pad: int = -1, max_blocks: int | None = None):
@@ -54,7 +62,8 @@ def plan(schedule, pad: int = -1, max_blocks: int | None = None):
     def attend():
         nonlocal n_attend
         flush()
-        events.append(AttendPoint(n_attend, mgr.tables(sids, pad, max_blocks), mgr.context_lens(sids)))
+        events.append(AttendPoint(n_attend, mgr.tables(sids, pad, max_blocks), mgr.context_lens(sids),
+                                  bool(mgr.pool.ref.max() > 1)))
         n_attend += 1
 
     for s, n in schedule.prefill:

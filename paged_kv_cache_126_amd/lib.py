@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpaged_attn.so")
 
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_CACHE_STREAM, PA_CACHE_REUSE = 0, 1
 STATUS = {0: "PA_OK", -1: "PA_EINVAL", -2: "PA_EALIGN", -3: "PA_EWORKSPACE", -4: "PA_EHIP"}
 
 EXPORTS = (
@@ -41,6 +42,7 @@ class DecodeShape(ctypes.Structure):
         ("kv_dtype", ctypes.c_int),
         ("out_dtype", ctypes.c_int),
         ("partition_tokens", ctypes.c_int32),
+        ("cache_policy", ctypes.c_int32),
     ]
 
 
@@ -111,12 +113,13 @@ def _dense(*tensors) -> None:
 
 
 def make_shape(q, k_cache, block_tables, max_context_len: int, out_dtype_code: int | None = None,
-               partition_tokens: int = 0) -> DecodeShape:
+               partition_tokens: int = 0, cache_policy: int = PA_CACHE_STREAM) -> DecodeShape:
     S, H, D = q.shape
     NB, B = k_cache.shape[0], k_cache.shape[1]
     kv = dtype_code(k_cache)
     return DecodeShape(S, H, D, B, NB, block_tables.shape[1], int(max_context_len), kv,
-                       kv if out_dtype_code is None else out_dtype_code, int(partition_tokens))
+                       kv if out_dtype_code is None else out_dtype_code, int(partition_tokens),
+                       int(cache_policy))
 
 
 def workspace_size(shape: DecodeShape) -> int:
@@ -168,14 +171,16 @@ def _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out):
 
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_size: int, scale: float,
                       out, max_context_len: int, workspace=None, partition_tokens: int = 0,
-                      stream=None, phase: str = "both") -> None:
+                      stream=None, phase: str = "both", cache_policy: int = PA_CACHE_STREAM) -> None:
     """Decode attention into ``out``; see include/paged_attn.h.
 
     ``phase`` selects "both" (paged_attn_decode), "partitions" or "merge"
-    (the two launches it is made of).
+    (the two launches it is made of). ``cache_policy`` is PA_CACHE_REUSE when
+    sequences of the batch share frames, else PA_CACHE_STREAM.
     """
     _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out)
-    shape = make_shape(q, k_cache, block_tables, max_context_len, dtype_code(out), partition_tokens)
+    shape = make_shape(q, k_cache, block_tables, max_context_len, dtype_code(out), partition_tokens,
+                       cache_policy)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load()
     st = _stream(stream)

@@ -63,7 +63,7 @@ def pad_frame_for(w) -> int:
 
 
 def run_gpu(w, partition_tokens: int = 0, out_dtype=None, phases: bool = False, poison=True,
-            keep_cache=False):
+            keep_cache=False, cache_policy=None):
     """Play workload ``w`` on cuda:0. Returns a list of (AttendPoint, out cpu
     tensor) and, with keep_cache, the DeviceCache."""
     import torch
@@ -85,16 +85,18 @@ def run_gpu(w, partition_tokens: int = 0, out_dtype=None, phases: bool = False, 
         odt = torch.float32 if out_dtype is None else out_dtype
         out = torch.full((w.num_seqs, w.H, w.D), float("nan"), dtype=odt, device=dev)
         max_ctx = int(pt.context_lens.max())
-        shape = pkv.lib.make_shape(q, cache.k, bt, max_ctx, pkv.lib.dtype_code(out), partition_tokens)
+        policy = pt.cache_policy if cache_policy is None else cache_policy
+        shape = pkv.lib.make_shape(q, cache.k, bt, max_ctx, pkv.lib.dtype_code(out), partition_tokens,
+                                   policy)
         ws = pkv.alloc_workspace(shape, dev)
+        kw = dict(partition_tokens=partition_tokens, cache_policy=policy)
         if phases:
             pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
-                                  partition_tokens, phase="partitions")
+                                  phase="partitions", **kw)
             pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
-                                  partition_tokens, phase="merge")
+                                  phase="merge", **kw)
         else:
-            pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
-                                  partition_tokens)
+            pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws, **kw)
         torch.cuda.synchronize()
         results.append((pt, out.cpu()))
 

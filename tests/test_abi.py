@@ -42,7 +42,7 @@ def test_status_strings():
 def shape(**kw):
     base = dict(num_seqs=64, num_heads=32, head_dim=128, block_size=16, num_blocks=20000,
                 max_blocks_per_seq=128, max_context_len=2048, kv_dtype=L.PA_BF16,
-                out_dtype=L.PA_F32, partition_tokens=0)
+                out_dtype=L.PA_F32, partition_tokens=0, cache_policy=L.PA_CACHE_STREAM)
     base.update(kw)
     return L.DecodeShape(**base)
 
@@ -57,6 +57,16 @@ def test_workspace_and_partition_sizing():
     assert pkv.workspace_size(sh) == ml + 64 * 32 * parts * 128 * 4
     # everything fits one partition: no workspace
     assert pkv.workspace_size(shape(max_context_len=pt)) == 0
+    # default partition size from the launch shape: longest of 2048/1024/512
+    # tokens that keeps about 8192 workgroups
+    assert pt == 512
+    assert pkv.partition_tokens(shape(num_seqs=8, num_heads=40, max_context_len=32768,
+                                      max_blocks_per_seq=2048)) == 1024
+    assert pkv.partition_tokens(shape(num_seqs=256, num_heads=64, max_context_len=8192,
+                                      max_blocks_per_seq=512)) == 2048
+    assert pkv.partition_tokens(shape(num_seqs=256, num_heads=32, max_context_len=1200,
+                                      block_size=32, max_blocks_per_seq=38)) == 2048
+    assert pkv.partition_tokens(shape(cache_policy=L.PA_CACHE_REUSE)) == 512
     # partition sizes round up to the tiling (64 tokens per chunk for fp32 d=16)
     assert pkv.partition_tokens(shape(head_dim=16, kv_dtype=L.PA_F32, out_dtype=L.PA_F32,
                                       block_size=10, max_context_len=40,
@@ -66,7 +76,7 @@ def test_workspace_and_partition_sizing():
 @pytest.mark.parametrize("bad", [
     dict(head_dim=96), dict(head_dim=8), dict(kv_dtype=7), dict(out_dtype=L.PA_F16),
     dict(max_context_len=2049), dict(num_heads=0), dict(block_size=0), dict(num_blocks=0),
-    dict(num_blocks=1 << 32), dict(partition_tokens=-1), dict(num_seqs=70000),
+    dict(num_blocks=1 << 32), dict(partition_tokens=-1), dict(num_seqs=70000), dict(cache_policy=2),
     dict(block_size=65536, num_heads=64, head_dim=256, max_context_len=4096, max_blocks_per_seq=1),
 ])
 def test_invalid_shapes(bad):
