@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="workloads 2 and 3: tokens per frame (default 16; the pool keeps its "
+                         "slot count)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -134,7 +137,13 @@ def main():
         sys.exit(1)
     pkv.load()
     dev = torch.device("cuda:0")
-    w = configs.FULL[args.workload]()
+    if args.block_size and args.workload not in (2, 3):
+        print("--block-size applies to workloads 2 and 3 only", file=sys.stderr)
+        sys.exit(2)
+    if args.block_size:
+        w = {2: configs.config2, 3: configs.config3}[args.workload](B=args.block_size)
+    else:
+        w = configs.FULL[args.workload]()
     log(f"[bench] workload {w.name}: {w.description}")
 
     events, _ = plan(w)

@@ -128,6 +128,24 @@ pa_status kv_append(const void* k_new, const void* v_new, const int64_t* slot_ma
                     void* stream);
 
 /*
+ * kv_copy_blocks: copy whole frames, for copy-on-write.
+ *
+ *   k_cache, v_cache  [num_blocks, B, H, D] in `dtype`, updated in place
+ *   block_pairs       [num_pairs, 2] int64 (device): (src frame, dst frame)
+ *
+ * For each pair, frame src of both caches is copied bit for bit to frame dst
+ * (B * H * D elements each). A pair naming a frame outside [0, num_blocks)
+ * is skipped. Destination frames must be distinct and must not be the source
+ * of another pair in the same call (copies run concurrently).
+ * num_pairs == 0 queues nothing. ("PagedAttention: Virtual Memory Guide",
+ * "2. Zero-Copy Branching via Copy-on-Write": a branch about to modify a
+ * shared frame gets a private copy of that one frame.)
+ */
+pa_status kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
+                         int64_t num_pairs, int32_t num_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, pa_dtype dtype, void* stream);
+
+/*
  * Workspace bytes paged_attn_decode needs for `shape` (partial results of
  * context partitions); 0 when every sequence fits one partition. Returns 0
  * for an invalid shape too: validate through paged_attn_decode.

@@ -164,6 +164,23 @@ pa_status kv_append(const void* k_new, const void* v_new, const int64_t* slot_ma
                                        static_cast<hipStream_t>(stream)));
 }
 
+pa_status kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pairs,
+                         int64_t num_pairs, int32_t num_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, pa_dtype dtype, void* stream) {
+  if (num_pairs < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      !valid_dtype(dtype))
+    return PA_EINVAL;
+  if ((static_cast<int64_t>(head_dim) * elem_bytes(dtype)) % 16 != 0) return PA_EINVAL;
+  if (num_pairs > 0x7FFFFFFF) return PA_EINVAL;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_pairs) return PA_EINVAL;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(block_pairs, 8)) return PA_EALIGN;
+  const int64_t frame_bytes =
+      static_cast<int64_t>(block_size) * num_heads * head_dim * elem_bytes(dtype);
+  return from_hip(pa::launch_kv_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, frame_bytes,
+                                            num_blocks, static_cast<hipStream_t>(stream)));
+}
+
 size_t paged_attn_workspace_size(const pa_decode_shape* shape) {
   int32_t pt = 0, parts = 0;
   if (check_shape(shape, &pt, &parts) != PA_OK) return 0;

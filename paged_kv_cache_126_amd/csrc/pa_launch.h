@@ -45,6 +45,10 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t*
                             void* k_cache, void* v_cache, int64_t num_tokens, int64_t row_bytes,
                             int64_t num_slots, hipStream_t stream);
 
+hipError_t launch_kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs,
+                                 int64_t num_pairs, int64_t frame_bytes, int64_t num_blocks,
+                                 hipStream_t stream);
+
 hipError_t launch_gather(const void* cache, const int32_t* block_tables,
                          const int32_t* context_lens, const int64_t* out_row_start, void* out,
                          int32_t num_seqs, int64_t row_bytes, int32_t block_size,

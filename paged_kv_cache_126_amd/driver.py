@@ -7,9 +7,11 @@ A schedule is any object with the attributes ``NB``, ``B``, ``num_seqs``,
 prefill) and ``frame_order`` (initial free list or None).
 
 :func:`plan` runs only the host block manager and returns the ordered list of
-KV writes and attention points: what a serving loop would hand the device.
-:class:`DeviceCache` plus :func:`execute` carry the writes out on the GPU with
-``kv_append`` (copy-on-write copies are re-appends of the copied rows).
+frame copies (copy-on-write), KV writes and attention points: what a serving
+loop would hand the device. :class:`DeviceCache` plus :func:`execute` carry
+them out on the GPU with ``kv_copy_blocks`` and ``kv_append``. Within one
+decode step every copy is issued before any write, so a copy always reads the
+shared frame as it was before the step.
 """
 from __future__ import annotations
 
@@ -25,6 +27,11 @@ class WriteBatch:
     seqs: np.ndarray       # int64 [N]: sequence of each row
     positions: np.ndarray  # int64 [N]: token position inside that sequence
     slots: np.ndarray      # int64 [N]: destination slot (frame * B + offset)
+
+
+@dataclass
+class CopyBlocks:
+    pairs: np.ndarray      # int64 [n, 2]: (source frame, new private frame), copy-on-write
 
 
 @dataclass
@@ -50,9 +57,12 @@ def plan(schedule, pad: int = -1, max_blocks: int | None = None):
     B = schedule.B
     sids = list(range(schedule.num_seqs))
     events = []
-    seqs, poss, slots = [], [], []
+    seqs, poss, slots, copies = [], [], [], []
 
     def flush():
+        if copies:
+            events.append(CopyBlocks(np.array(copies, dtype=np.int64).reshape(-1, 2)))
+            copies.clear()
         if seqs:
             events.append(WriteBatch(np.concatenate(seqs), np.concatenate(poss), np.concatenate(slots)))
             seqs.clear(), poss.clear(), slots.clear()
@@ -82,12 +92,7 @@ def plan(schedule, pad: int = -1, max_blocks: int | None = None):
             t = mgr.context_len(s)
             r = mgr.append_token(s)
             if r.cow_src is not None:
-                # copy-on-write: the new private frame receives the rows the
-                # shared frame held at offsets 0 .. cow_rows - 1
-                first = t - r.cow_rows
-                seqs.append(np.full(r.cow_rows, s, dtype=np.int64))
-                poss.append(np.arange(first, t, dtype=np.int64))
-                slots.append(r.cow_dst * B + np.arange(r.cow_rows, dtype=np.int64))
+                copies.append((r.cow_src, r.cow_dst))  # copy-on-write of the shared frame
             seqs.append(np.array([s], dtype=np.int64))
             poss.append(np.array([t], dtype=np.int64))
             slots.append(np.array([r.slot], dtype=np.int64))
@@ -117,6 +122,11 @@ class DeviceCache:
 
         kv_append(k_new, v_new, slots, self.k, self.v, stream=stream)
 
+    def copy_blocks(self, pairs, stream=None) -> None:
+        from .lib import kv_copy_blocks
+
+        kv_copy_blocks(self.k, self.v, pairs, stream=stream)
+
 
 def execute(events, cache: DeviceCache, rows, on_attend, chunk_rows: int = 1 << 16) -> None:
     """Apply the events on the device.
@@ -130,7 +140,9 @@ def execute(events, cache: DeviceCache, rows, on_attend, chunk_rows: int = 1 << 
 
     dev = cache.k.device
     for ev in events:
-        if isinstance(ev, WriteBatch):
+        if isinstance(ev, CopyBlocks):
+            cache.copy_blocks(torch.from_numpy(np.ascontiguousarray(ev.pairs)).to(dev))
+        elif isinstance(ev, WriteBatch):
             for lo in range(0, len(ev.slots), chunk_rows):
                 hi = min(lo + chunk_rows, len(ev.slots))
                 k_new, v_new = rows(ev.seqs[lo:hi], ev.positions[lo:hi])

@@ -18,7 +18,7 @@ PA_CACHE_STREAM, PA_CACHE_REUSE = 0, 1
 STATUS = {0: "PA_OK", -1: "PA_EINVAL", -2: "PA_EALIGN", -3: "PA_EWORKSPACE", -4: "PA_EHIP"}
 
 EXPORTS = (
-    "pa_status_string", "pa_abi_version", "kv_append", "paged_attn_workspace_size",
+    "pa_status_string", "pa_abi_version", "kv_append", "kv_copy_blocks", "paged_attn_workspace_size",
     "paged_attn_partition_tokens", "paged_attn_decode", "paged_attn_decode_partitions",
     "paged_attn_merge", "paged_gather",
 )
@@ -65,6 +65,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_abi_version.restype = I32
     lib.kv_append.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I64, ctypes.c_int, P]
     lib.kv_append.restype = ctypes.c_int
+    lib.kv_copy_blocks.argtypes = [P, P, P, I64, I32, I32, I32, I64, ctypes.c_int, P]
+    lib.kv_copy_blocks.restype = ctypes.c_int
     lib.paged_attn_workspace_size.argtypes = [SH]
     lib.paged_attn_workspace_size.restype = SZ
     lib.paged_attn_partition_tokens.argtypes = [SH]
@@ -154,6 +156,19 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None
     _check("kv_append", load().kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
                                          _ptr(v_cache), N, H, D, B, NB, dtype_code(k_cache),
                                          _stream(stream)))
+
+
+def kv_copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
+    """Copy frames ``block_pairs[:, 0]`` to ``block_pairs[:, 1]`` (int64 ``[n, 2]``) in both caches."""
+    _dense(k_cache, v_cache, block_pairs)
+    NB, B, H, D = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2 or str(block_pairs.dtype) != "torch.int64":
+        raise TypeError("block_pairs must be int64 [n, 2]")
+    _check("kv_copy_blocks", load().kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs),
+                                                   block_pairs.shape[0], H, D, B, NB,
+                                                   dtype_code(k_cache), _stream(stream)))
 
 
 def _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out):

@@ -119,3 +119,13 @@ def test_append_and_gather_argument_errors():
     assert lib.paged_gather(p, p, p, p, p, 2, 2, 16, 10, 100, 2, 21, L.PA_F32, None) == -1
     assert lib.paged_gather(p, p, p, p, p, 0, 2, 16, 10, 100, 2, 20, L.PA_F32, None) == 0
     assert lib.paged_gather(None, p, p, p, p, 2, 2, 16, 10, 100, 2, 20, L.PA_F32, None) == -1
+
+
+def test_copy_blocks_argument_errors():
+    lib = pkv.load()
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.kv_copy_blocks(p, p, p, 0, 32, 128, 16, 100, L.PA_BF16, None) == 0
+    assert lib.kv_copy_blocks(None, p, p, 3, 32, 128, 16, 100, L.PA_BF16, None) == -1
+    assert lib.kv_copy_blocks(p, p, p, -1, 32, 128, 16, 100, L.PA_BF16, None) == -1
+    assert lib.kv_copy_blocks(p, p, ctypes.c_void_p((1 << 20) + 4), 3, 32, 128, 16, 100,
+                              L.PA_BF16, None) == -2

@@ -12,7 +12,7 @@ import pytest
 
 from oracle import blockmgr as obm
 from paged_kv_cache_126_amd import block_manager as bm
-from paged_kv_cache_126_amd.driver import AttendPoint, WriteBatch, plan
+from paged_kv_cache_126_amd.driver import AttendPoint, CopyBlocks, WriteBatch, plan
 from workloads import configs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -125,7 +125,10 @@ def _slot_idents(w, events):
     img = np.full(w.NB * w.B, -1, dtype=np.int64)
     out = []
     for e in events:
-        if isinstance(e, WriteBatch):
+        if isinstance(e, CopyBlocks):
+            for src, dst in e.pairs:
+                img[dst * w.B:(dst + 1) * w.B] = img[src * w.B:(src + 1) * w.B]
+        elif isinstance(e, WriteBatch):
             ids = np.concatenate([w.idents(int(s), [int(p)]) for s, p in zip(e.seqs, e.positions)]) \
                 if len(e.seqs) < 2000 else _idents_vec(w, e)
             img[e.slots] = ids
@@ -168,3 +171,19 @@ def test_plan_full_config5_lengths():
     assert pt.context_lens.max() <= 8192
     last = events[-1] if isinstance(events[-1], WriteBatch) else events[-2]
     assert len(last.slots) == w.num_seqs  # one append per sequence, no CoW
+
+
+def test_plan_emits_frame_copies_before_writes():
+    """Copy-on-write in the shared-prefix workload: each prompt's partial
+    frame is copied for all branches but the last to append, before that
+    step's writes."""
+    w = configs.small(4)
+    events, _ = plan(w)
+    copies = [e for e in events if isinstance(e, CopyBlocks)]
+    n_prompts = len(w.prefill)
+    assert sum(len(c.pairs) for c in copies) == n_prompts * 3
+    i = events.index(copies[0])
+    assert isinstance(events[i + 1], WriteBatch)
+    for c in copies:
+        assert len(np.unique(c.pairs[:, 1])) == len(c.pairs)
+        assert not set(c.pairs[:, 1]) & set(c.pairs[:, 0])

@@ -256,3 +256,30 @@ def test_narrow_output_dtype_within_one_ulp(cfg):
         got = out.view(torch.int16).numpy().view(np.uint16)
         want = torch.from_numpy(o).to(tdt).view(torch.int16).numpy().view(np.uint16)
         assert int(_ulp_distance(got, want).max()) <= 1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_copy_blocks_bit_exact(dtype):
+    """kv_copy_blocks copies whole frames bit for bit, leaves every other frame
+    untouched and skips pairs naming a frame outside the pool."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+
+    say(f"[gpu] kv_copy_blocks, {dtype}")
+    NB, B, H, D = 40, 16, 4, 128 if dtype == "bf16" else 32
+    dev = torch.device("cuda:0")
+    n = NB * B
+    k = V.draw_torch(31, V.STREAM_K, np.arange(n), H, D, dtype, dev).reshape(NB, B, H, D).contiguous()
+    v = V.draw_torch(31, V.STREAM_V, np.arange(n), H, D, dtype, dev).reshape(NB, B, H, D).contiguous()
+    pairs = np.array([[3, 17], [5, 0], [39, 21], [0, 2], [-1, 9], [7, NB]], dtype=np.int64)
+    ref_k, ref_v = k.cpu().clone(), v.cpu().clone()
+    for src, dst in pairs:
+        if 0 <= src < NB and 0 <= dst < NB:
+            ref_k[dst] = k.cpu()[src]
+            ref_v[dst] = v.cpu()[src]
+    pkv.kv_copy_blocks(k, v, torch.from_numpy(pairs).to(dev))
+    torch.cuda.synchronize()
+    view = torch.int32 if dtype == "f32" else torch.int16
+    assert torch.equal(k.cpu().view(view), ref_k.view(view))
+    assert torch.equal(v.cpu().view(view), ref_v.view(view))

@@ -51,10 +51,6 @@ class Workload:
     def elem_bytes(self) -> int:
         return 4 if self.dtype == "f32" else 2
 
-    def _ident_base(self) -> np.ndarray:
-        # identities of sequence s occupy [s * stride, s * stride + max_len)
-        return np.arange(self.num_seqs, dtype=np.int64) * self.ident_stride
-
     @property
     def ident_stride(self) -> int:
         total = {}
@@ -91,31 +87,43 @@ def config1() -> Workload:
     )
 
 
-def config2(S: int = 64, H: int = 32, NB: int = 20000, max_ctx: int = 2048) -> Workload:
+def config2(S: int = 64, H: int = 32, NB: int | None = None, max_ctx: int = 2048,
+            B: int = 16) -> Workload:
     """Decode batch 64, bf16, ctx ~ U{1..2048}, permuted 20k-frame pool.
 
     Draw order: ``ctx = integers(1, max_ctx + 1, S)``, then ``permutation(NB)``.
+    Another block size keeps the pool's slot count (NB = 20000 * 16 / B).
     """
+    NB = NB if NB is not None else 20000 * 16 // B
     rng = np.random.default_rng(2)
     ctx = rng.integers(1, max_ctx + 1, size=S)
     order = rng.permutation(NB)
+    name = "cfg2_batch64_bf16" if (S, H) == (64, 32) else f"cfg2_S{S}_H{H}"
+    if B != 16:
+        name += f"_B{B}"
     return Workload(
-        name="cfg2_batch64_bf16" if (S, H) == (64, 32) else f"cfg2_S{S}_H{H}",
-        seed=2, dtype="bf16", H=H, D=128, B=16, NB=NB, num_seqs=S,
+        name=name, seed=2, dtype="bf16", H=H, D=128, B=B, NB=NB, num_seqs=S,
         prefill=[(s, int(ctx[s])) for s in range(S)], frame_order=order,
-        description=f"S={S}, H={H}, d=128, B=16, bf16, ctx U[1,{max_ctx}], permuted pool of {NB}",
+        description=f"S={S}, H={H}, d=128, B={B}, bf16, ctx U[1,{max_ctx}], permuted pool of {NB}",
     )
 
 
-def config3(S: int = 8, H: int = 40, ctx: int = 32768, NB: int = 20000) -> Workload:
-    """Long context: every sequence exactly 32,768 tokens, permuted pool."""
+def config3(S: int = 8, H: int = 40, ctx: int = 32768, NB: int | None = None,
+            B: int = 16) -> Workload:
+    """Long context: every sequence exactly 32,768 tokens, permuted pool.
+
+    Another block size keeps the pool's slot count (NB = 20000 * 16 / B).
+    """
+    NB = NB if NB is not None else 20000 * 16 // B
     rng = np.random.default_rng(3)
     order = rng.permutation(NB)
+    name = "cfg3_long_ctx_bf16" if (S, H, ctx) == (8, 40, 32768) else f"cfg3_S{S}_H{H}_L{ctx}"
+    if B != 16:
+        name += f"_B{B}"
     return Workload(
-        name="cfg3_long_ctx_bf16" if (S, H, ctx) == (8, 40, 32768) else f"cfg3_S{S}_H{H}_L{ctx}",
-        seed=3, dtype="bf16", H=H, D=128, B=16, NB=NB, num_seqs=S,
+        name=name, seed=3, dtype="bf16", H=H, D=128, B=B, NB=NB, num_seqs=S,
         prefill=[(s, ctx) for s in range(S)], frame_order=order,
-        description=f"S={S}, H={H}, d=128, B=16, bf16, ctx {ctx}, permuted pool of {NB}",
+        description=f"S={S}, H={H}, d=128, B={B}, bf16, ctx {ctx}, permuted pool of {NB}",
     )
 
 
