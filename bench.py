@@ -146,7 +146,7 @@ def main():
         w = configs.FULL[args.workload]()
     log(f"[bench] workload {w.name}: {w.description}")
 
-    events, _ = plan(w)
+    events, plan_mgr = plan(w)
     cache = DeviceCache(w.NB, w.B, w.H, w.D, V.torch_dtype(w.dtype), dev, poison=True)
     points = []
 
@@ -256,6 +256,34 @@ def main():
         f"partition kernel {part_ms.mean() * 1e3:.1f} us, merge {merge_ms.mean() * 1e3:.1f} us"
         + (f", kv_append {append_ms.mean() * 1e3:.1f} us" if append_args else ""))
 
+    # Copy-on-write frame copies (shared-prefix workload): the step's copies,
+    # redirected to frames the schedule never uses so the cache stays intact.
+    from paged_kv_cache_126_amd.driver import CopyBlocks
+
+    cow = None
+    cow_pairs = [e.pairs for e in events if isinstance(e, CopyBlocks)]
+    if cow_pairs:
+        pairs = np.concatenate(cow_pairs).copy()
+        spare = plan_mgr.pool.free_list()[-len(pairs):]
+        if len(spare) == len(pairs):
+            pairs[:, 1] = spare
+            pairs_dev = torch.from_numpy(pairs).to(dev)
+            cts = []
+            for i in range(args.steps):
+                if not args.no_flush:
+                    flush()
+                c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                c0.record()
+                cache.copy_blocks(pairs_dev)
+                c1.record()
+                torch.cuda.synchronize()
+                cts.append(c0.elapsed_time(c1))
+            cbytes = 2 * 2 * len(pairs) * w.B * w.H * w.D * w.elem_bytes  # K and V, read + write
+            cus = float(np.mean(cts)) * 1e3
+            cow = {"pairs": len(pairs), "us": round(cus, 2), "bytes": cbytes,
+                   "GB/s": round(cbytes / cus / 1e3, 1)}
+            log(f"[bench] copy-on-write: {len(pairs)} frame copies in {cus:.1f} us")
+
     # warm (no flush) back-to-back rate, reported beside the cold headline
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -308,6 +336,7 @@ def main():
             "algorithmic_bytes_per_launch": kv_bytes_unique,
         },
         "kernel_source_digest": digest,
+        "cow_frame_copies": cow,
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")

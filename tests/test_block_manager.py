@@ -187,3 +187,53 @@ def test_plan_emits_frame_copies_before_writes():
     for c in copies:
         assert len(np.unique(c.pairs[:, 1])) == len(c.pairs)
         assert not set(c.pairs[:, 1]) & set(c.pairs[:, 0])
+
+
+def test_random_operation_sequences_match_oracle():
+    """Random interleavings of prefill, fork, append and free: the product and
+    the oracle block managers agree on every table, length, free list and
+    reference count after every operation."""
+    for seed in range(12):
+        rng = np.random.default_rng(100 + seed)
+        NB, B = int(rng.integers(20, 200)), int(rng.choice([1, 2, 3, 4, 8, 16]))
+        order = rng.permutation(NB) if seed % 2 else None
+        p_pool, o_pool = bm.BlockPool(NB, order), obm.PhysicalBlockPool(NB, order)
+        p_mgr, o_mgr = bm.SeqManager(p_pool, B), obm.SequenceGroupMemoryManager(o_pool, B)
+        live, next_id = [], 0
+        for _ in range(300):
+            op = rng.choice(["init", "fork", "append", "append", "append", "free"])
+            try:
+                if op == "init" or not live:
+                    n = int(rng.integers(0, 3 * B + 2))
+                    if -(-n // B) > p_pool.free_count:
+                        continue
+                    p_mgr.init_sequence(next_id, n)
+                    o_mgr.init_sequence(next_id, n)
+                    live.append(next_id)
+                    next_id += 1
+                elif op == "fork":
+                    parent = live[int(rng.integers(len(live)))]
+                    p_mgr.fork(parent, next_id)
+                    o_mgr.fork_sequence(parent, next_id)
+                    live.append(next_id)
+                    next_id += 1
+                elif op == "append":
+                    s = live[int(rng.integers(len(live)))]
+                    if p_pool.free_count == 0:
+                        continue
+                    r = p_mgr.append_token(s)
+                    copied = o_mgr.append_token(s)
+                    assert (copied is None) == (r.cow_src is None)
+                    if copied is not None:
+                        assert copied == (r.cow_src, r.cow_dst)
+                else:
+                    s = live.pop(int(rng.integers(len(live))))
+                    p_mgr.free_sequence(s)
+                    o_mgr.free_sequence(s)
+            except MemoryError:
+                raise AssertionError("the test only issues operations that fit the pool")
+            for s in live:
+                assert p_mgr.block_table(s) == o_mgr.block_tables[s]
+                assert p_mgr.context_len(s) == o_mgr.seq_lens[s]
+            assert p_pool.free_list() == o_pool.free_blocks
+            assert [int(p_pool.ref[f]) for f in range(NB)] == [o_pool.ref_counts[f] for f in range(NB)]
