@@ -237,6 +237,71 @@ int oracle_dense_attention(const void* q, const void* k, const void* v, const in
 }
 
 /*
+ * Causal multi-query (prefill) attention through the block tables.
+ *
+ *   q            [T, H, D]: sequence s owns rows query_start[s] .. query_start[s+1]-1
+ *   query_start  [S + 1] int32, non-decreasing, query_start[0] = 0
+ *   out          [T, H, D] double
+ *
+ * The n_s queries of sequence s are its last n_s tokens: query r sits at
+ * position p = ctx_s - n_s + r and attends to tokens 0 .. p, the causal sum
+ * o_i = sum_{j <= i} softmax_j(a_ij) v_j of "Solving the LLM Memory Wall"
+ * ("1. The Mathematical Foundation"), each token fetched through the table as
+ * in oracle_paged_decode. Requires n_s <= ctx_s.
+ */
+int oracle_paged_prefill(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens,
+                         const int32_t* query_start, int S, int H, int D, int B, int64_t NB,
+                         int max_blocks, double scale, int dtype, double* out) {
+  if (S < 0 || H <= 0 || D <= 0 || B <= 0 || NB <= 0 || max_blocks < 0 || !valid_dtype(dtype))
+    return ORACLE_BAD_ARG;
+  for (int s = 0; s < S; ++s) {
+    int64_t n = (int64_t)query_start[s + 1] - query_start[s];
+    if (n < 0 || n > context_lens[s] || context_lens[s] > (int64_t)max_blocks * B) return ORACLE_BAD_ARG;
+  }
+  int status = ORACLE_OK;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int s = 0; s < S; ++s) {
+    for (int h = 0; h < H; ++h) {
+      int64_t ctx = context_lens[s];
+      int64_t n = (int64_t)query_start[s + 1] - query_start[s];
+      int64_t* row_off = (int64_t*)malloc(sizeof(int64_t) * (ctx > 0 ? ctx : 1));
+      double* a = (double*)malloc(sizeof(double) * (ctx > 0 ? ctx : 1));
+      if (!row_off || !a) {
+        free(row_off);
+        free(a);
+#pragma omp atomic write
+        status = ORACLE_NO_MEMORY;
+        continue;
+      }
+      int bad = 0;
+      for (int64_t i = 0; i < ctx; ++i) {
+        int64_t f = block_tables[(int64_t)s * max_blocks + i / B];
+        if (f < 0 || f >= NB) {
+          bad = 1;
+          break;
+        }
+        row_off[i] = ((f * B + i % B) * H + h) * D;
+      }
+      if (bad) {
+#pragma omp atomic write
+        status = ORACLE_BAD_FRAME;
+      } else {
+        for (int64_t r = 0; r < n; ++r) {
+          int64_t t = query_start[s] + r;        /* query row */
+          int64_t pos = ctx - n + r;              /* its position in the sequence */
+          attend_rows(q, (t * H + h) * D, k_cache, v_cache, row_off, pos + 1, D, scale, dtype, a,
+                      out + (t * H + h) * D);
+        }
+      }
+      free(row_off);
+      free(a);
+    }
+  }
+  return status;
+}
+
+/*
  * Attention computed over context partitions of P tokens and merged by the
  * log-sum-exp rule: partition p yields m_p = max a, l_p = sum exp(a - m_p),
  * acc_p = sum exp(a - m_p) v; then with M = max_p m_p,

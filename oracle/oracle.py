@@ -46,10 +46,13 @@ class Oracle:
         L.oracle_paged_decode_split.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I, _D,
                                                 _I, _I, _P]
         L.oracle_dense_attention.argtypes = [_P, _P, _P, _P, _I, _I, _I, _D, _I, _P]
+        L.oracle_paged_prefill.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I64, _I, _D, _I,
+                                           _P]
         L.oracle_kv_append.argtypes = [_P, _P, _P, _I64, _I, _I, _I, _I64, _I, _P, _P]
         L.oracle_gather.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I64, _I, _I, _P]
         L.oracle_widen.argtypes = [_P, _I64, _I, _P]
         for f in ("oracle_paged_decode", "oracle_paged_decode_split", "oracle_dense_attention",
+                  "oracle_paged_prefill",
                   "oracle_kv_append", "oracle_gather", "oracle_widen", "oracle_num_threads"):
             getattr(L, f).restype = _I
 
@@ -95,6 +98,26 @@ class Oracle:
                                                 float(np.float32(scale)), DTYPE_CODE[dtype], P,
                                                 _ptr(out))
         self._check(rc, "oracle_paged_decode_split")
+        return out
+
+    def paged_prefill(self, q, k_cache, v_cache, block_tables, context_lens, query_start, B: int,
+                      scale: float, dtype: str) -> np.ndarray:
+        """fp64 [T, H, D]: causal attention of each sequence's last tokens (see oracle.c)."""
+        q = np.ascontiguousarray(q, dtype=STORAGE[dtype])
+        k_cache = np.ascontiguousarray(k_cache, dtype=STORAGE[dtype])
+        v_cache = np.ascontiguousarray(v_cache, dtype=STORAGE[dtype])
+        bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+        cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+        qs = np.ascontiguousarray(query_start, dtype=np.int32)
+        T, H, D = q.shape
+        S = cl.shape[0]
+        NB = k_cache.shape[0]
+        assert qs.shape == (S + 1,) and qs[-1] == T and k_cache.shape == (NB, B, H, D)
+        out = np.zeros((T, H, D), dtype=np.float64)
+        rc = self.lib.oracle_paged_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
+                                           _ptr(qs), S, H, D, B, NB, bt.shape[1],
+                                           float(np.float32(scale)), DTYPE_CODE[dtype], _ptr(out))
+        self._check(rc, "oracle_paged_prefill")
         return out
 
     def dense_attention(self, q, k_rows, v_rows, seq_start, scale: float, dtype: str) -> np.ndarray:

@@ -302,6 +302,71 @@ def pin_gather_matches_numpy(orc):
     assert got.tobytes() == ref.tobytes()
 
 
+def _prefill_case(seed, S, H, D, B, dtype, max_ctx, full=False):
+    c = Case(seed, S, H, D, B, dtype, max_ctx, min_ctx=1)
+    rng = np.random.default_rng(seed + 1)
+    n = c.ctx.copy() if full else np.array([int(rng.integers(1, k + 1)) for k in c.ctx], dtype=np.int32)
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q = draw_np(seed, STREAM_Q, np.arange(qs[-1]) + 5000 * seed, H, D, dtype)
+    return c, n, qs, q
+
+
+def pin_prefill_single_query_equals_decode(orc):
+    """One query per sequence (its last token) is decode attention."""
+    for dt in ("f32", "bf16"):
+        c = Case(101, 5, 2, 16, 4, dt, 60)
+        qs = np.arange(c.S + 1, dtype=np.int32)
+        pre = orc.paged_prefill(c.q, c.k, c.v, c.tables, c.ctx, qs, c.B, c.scale, dt)
+        dec = c.decode(orc)
+        assert np.array_equal(pre, dec)
+
+
+def pin_prefill_last_query_equals_decode(orc):
+    """In a full prefill the last query sees the whole context: it equals decode."""
+    c, n, qs, q = _prefill_case(102, 4, 2, 8, 3, "f16", 40, full=True)
+    pre = orc.paged_prefill(q, c.k, c.v, c.tables, c.ctx, qs, c.B, c.scale, "f16")
+    last = q[qs[1:] - 1]
+    dec = orc.paged_decode(last, c.k, c.v, c.tables, c.ctx, c.B, c.scale, "f16")
+    assert np.array_equal(pre[qs[1:] - 1], dec)
+
+
+def pin_prefill_is_causal(orc):
+    """Query at position p ignores every token after p and depends on token p."""
+    c, n, qs, q = _prefill_case(103, 3, 2, 8, 4, "f32", 30, full=True)
+    base = orc.paged_prefill(q, c.k, c.v, c.tables, c.ctx, qs, c.B, c.scale, "f32")
+    s, p = 1, int(c.ctx[1]) // 2
+    k2, v2 = c.k.copy(), c.v.copy()
+    for i in range(p + 1, int(c.ctx[s])):
+        f = c.tables[s, i // c.B]
+        k2[f, i % c.B] = 7.0
+        v2[f, i % c.B] = -3.0
+    after = orc.paged_prefill(q, k2, v2, c.tables, c.ctx, qs, c.B, c.scale, "f32")
+    row = qs[s] + p
+    assert np.array_equal(after[:row + 1], base[:row + 1])
+    assert not np.array_equal(after[row + 1:qs[s + 1]], base[row + 1:qs[s + 1]])
+    k3 = c.k.copy()
+    f = c.tables[s, p // c.B]
+    k3[f, p % c.B] = 5.0
+    moved = orc.paged_prefill(q, k3, c.v, c.tables, c.ctx, qs, c.B, c.scale, "f32")
+    assert not np.array_equal(moved[row], base[row])
+
+
+def pin_prefill_bruteforce(orc):
+    """Every query of a chunked prefill against the rational brute force."""
+    for seed, dt, B in ((104, "bf16", 3), (105, "f32", 10)):
+        c, n, qs, q = _prefill_case(seed, 3, 2, 6, B, dt, 22)
+        out = orc.paged_prefill(q, c.k, c.v, c.tables, c.ctx, qs, c.B, c.scale, dt)
+        kf, vf, qf = np_widen(c.k, dt).tolist(), np_widen(c.v, dt).tolist(), np_widen(q, dt)
+        for s in range(c.S):
+            for r in range(int(n[s])):
+                pos = int(c.ctx[s]) - int(n[s]) + r
+                t = qs[s] + r
+                for h in range(c.H):
+                    ref = bruteforce.decode_one(qf[t, h].tolist(), kf, vf, c.tables[s].tolist(),
+                                                pos + 1, h, c.B, c.scale)
+                    assert np.max(np.abs(out[t, h] - np.array(ref))) <= 1e-14, (seed, s, r, h)
+
+
 ALL = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 

@@ -40,6 +40,9 @@ C_MUTANTS = {
     "dense_head_dropped": ("row_off[j] = ((seq_start[s] + j) * H + h) * D;",
                            "row_off[j] = ((seq_start[s] + j) * H) * D;"),
     "normaliser_dropped": ("out[e] = acc / z;", "out[e] = acc;"),
+    "prefill_not_causal": ("row_off, pos + 1, D, scale", "row_off, ctx, D, scale"),
+    "prefill_excludes_self": ("row_off, pos + 1, D, scale", "row_off, pos, D, scale"),
+    "prefill_position": ("int64_t pos = ctx - n + r;", "int64_t pos = r;"),
 }
 
 PY_MUTANTS = {
