@@ -104,6 +104,69 @@ def cpu_baseline(w, tables, ctx, budget_s: float = 12.0):
     }
 
 
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
+
+
+def bench_prefill(args, w, pt, cache, dev):
+    """Prefill workloads: time paged_attn_prefill (one launch per step)."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+    from workloads import values as V
+
+    qs, ids = w.prefill_queries(pt.context_lens)
+    T = int(qs[-1])
+    q = V.draw_torch(w.seed, V.STREAM_Q, ids, w.H, w.D, w.dtype, dev).contiguous()
+    out = torch.empty((T, w.H, w.D), dtype=torch.float32, device=dev)
+    bt = torch.from_numpy(pt.tables).to(dev)
+    cl = torch.from_numpy(pt.context_lens).to(dev)
+    qsd = torch.from_numpy(qs.astype(np.int32)).to(dev)
+    max_ctx, max_q = int(pt.context_lens.max()), int(np.diff(qs).max())
+    # algorithmic work: 4 D flops per (query, visible key) per head
+    n = np.asarray(w.query_lens, dtype=np.int64)
+    ctx = pt.context_lens.astype(np.int64)
+    pairs = int(np.sum(n * (ctx - n) + n * (n + 1) // 2))
+    flops = 4 * w.D * w.H * pairs
+    flush_buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def step():
+        pkv.paged_attn_prefill(q, cache.k, cache.v, bt, cl, qsd, w.B, w.scale, out, max_ctx, max_q)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e0, e1 in evs:
+        if not args.no_flush:
+            torch.sum(flush_buf, dim=0, out=flush_sink)
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] prefill {args.steps} steps: {ms * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
+    res = {
+        "metric": "paged prefill attention: TFLOP/s (% of MFMA peak) + us/step",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "step": "prefill attention",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "queries": T,
+                   "sum_ctx": int(ctx.sum()), "visible_pairs": pairs, "flops": flops,
+                   "cache_flush_between_steps": not args.no_flush},
+        "us_per_step": round(ms * 1e3, 2),
+        "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +244,9 @@ def main():
     log(f"[bench] cache written: {w.NB} frames, sum ctx {int(pt.context_lens.sum())}"
         + (f"; step appends {len(step_append.slots)} tokens" if step_append is not None else ""))
 
+    if w.query_lens is not None:
+        bench_prefill(args, w, pt, cache, dev)
+        return
     q = V.draw_torch(w.seed, V.STREAM_Q, w.q_idents(pt.step), w.H, w.D, w.dtype, dev).contiguous()
     bt = torch.from_numpy(pt.tables).to(dev)
     cl = torch.from_numpy(pt.context_lens).to(dev)

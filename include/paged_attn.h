@@ -198,6 +198,46 @@ pa_status paged_attn_decode_partitions(const void* q, const void* k_cache, const
 pa_status paged_attn_merge(const int32_t* context_lens, void* out, const pa_decode_shape* shape,
                            const void* workspace, size_t workspace_bytes, void* stream);
 
+/* Shapes and types of one prefill call. */
+typedef struct pa_prefill_shape {
+  int32_t num_seqs;            /* S */
+  int32_t num_heads;           /* H */
+  int32_t head_dim;            /* D: 64 or 128 */
+  int32_t block_size;          /* B */
+  int64_t num_blocks;          /* NB */
+  int32_t max_blocks_per_seq;  /* row stride of block_tables */
+  int32_t max_context_len;     /* host-known bound on context_lens */
+  int32_t max_query_len;       /* host-known bound on queries per sequence; sizes the launch */
+  int32_t total_queries;       /* T: rows of q and out */
+  pa_dtype kv_dtype;           /* PA_F16 or PA_BF16 (the matrix-core path) */
+  pa_dtype out_dtype;          /* PA_F32 or kv_dtype */
+} pa_prefill_shape;
+
+/*
+ * paged_attn_prefill: causal multi-query attention over the paged cache.
+ *
+ *   q             [T, H, D] in kv_dtype; sequence s owns rows
+ *                 query_start[s] .. query_start[s+1]-1
+ *   query_start   [S + 1] int32 (device), non-decreasing, query_start[S] <= T
+ *   block_tables, context_lens, k_cache, v_cache, block_size, scale: as for
+ *                 paged_attn_decode
+ *   out           [T, H, D] in out_dtype
+ *
+ * The n_s = query_start[s+1] - query_start[s] queries of sequence s are its
+ * last n_s tokens, whose K and V are already in the cache: query r sits at
+ * position p = ctx_s - n_s + r and attends to tokens 0 .. p ("Solving the LLM
+ * Memory Wall", "1. The Mathematical Foundation": o_i = sum over j <= i of
+ * softmax_j(a_ij) v_j). n_s = ctx_s is a whole prompt, n_s < ctx_s a chunk of
+ * one, n_s = 1 a decode step. Device-side preconditions: 0 <= n_s <= ctx_s and
+ * n_s <= max_query_len (larger values are clamped). Scores and the output
+ * accumulate in fp32 on the matrix cores; the softmax weights enter the
+ * weighted sum of V as a 16-bit value plus its 16-bit residual.
+ */
+pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             const int32_t* query_start, int32_t block_size, float scale,
+                             void* out, const pa_prefill_shape* shape, void* stream);
+
 /*
  * paged_gather: block translation made visible, for checking it bit for bit.
  * Copies, for each sequence s and token i < context_lens[s], the row

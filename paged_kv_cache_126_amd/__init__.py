@@ -5,10 +5,11 @@ frame pool and block tables that feed it.
 """
 from .block_manager import AppendResult, BlockPool, SeqManager
 from .lib import (PagedAttnError, alloc_workspace, kv_append, kv_copy_blocks, load, paged_attn_decode,
-                  paged_gather, partition_tokens, workspace_size)
+                  paged_attn_prefill, paged_gather, partition_tokens, workspace_size)
 
 __all__ = [
     "AppendResult", "BlockPool", "SeqManager", "PagedAttnError", "alloc_workspace", "kv_append",
     "kv_copy_blocks",
-    "load", "paged_attn_decode", "paged_gather", "partition_tokens", "workspace_size",
+    "load", "paged_attn_decode", "paged_attn_prefill", "paged_gather", "partition_tokens",
+    "workspace_size",
 ]

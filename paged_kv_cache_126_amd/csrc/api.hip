@@ -248,6 +248,54 @@ pa_status paged_attn_decode(const void* q, const void* k_cache, const void* v_ca
   return paged_attn_merge(context_lens, out, shape, workspace, workspace_bytes, stream);
 }
 
+pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             const int32_t* query_start, int32_t block_size, float scale,
+                             void* out, const pa_prefill_shape* sh, void* stream) {
+  if (!sh) return PA_EINVAL;
+  if (sh->num_seqs < 0 || sh->num_heads <= 0 || sh->block_size <= 0 || sh->num_blocks <= 0 ||
+      sh->num_blocks > 0x7FFFFFFFLL || sh->max_blocks_per_seq <= 0 || sh->max_context_len < 0 ||
+      sh->max_query_len < 0 || sh->total_queries < 0 || !valid_dtype(sh->kv_dtype))
+    return PA_EINVAL;
+  if (!pa::prefill_supported(to_internal(sh->kv_dtype), sh->head_dim)) return PA_EINVAL;
+  if (sh->out_dtype != PA_F32 && sh->out_dtype != sh->kv_dtype) return PA_EINVAL;
+  if (block_size != sh->block_size || !std::isfinite(scale)) return PA_EINVAL;
+  if (static_cast<int64_t>(sh->max_context_len) >
+      static_cast<int64_t>(sh->max_blocks_per_seq) * sh->block_size)
+    return PA_EINVAL;
+  if (static_cast<int64_t>(sh->block_size) * sh->num_heads * sh->head_dim * elem_bytes(sh->kv_dtype) >
+      0x7FFFFFFFLL)
+    return PA_EINVAL;
+  if (sh->num_seqs > kMaxGridYZ || sh->num_heads > kMaxGridYZ) return PA_EINVAL;
+  if (sh->num_seqs == 0 || sh->max_query_len == 0 || sh->total_queries == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
+    return PA_EINVAL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, static_cast<uintptr_t>(elem_bytes(sh->out_dtype))) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+    return PA_EALIGN;
+  pa::PrefillArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.out = out;
+  a.num_blocks = sh->num_blocks;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = sh->num_seqs;
+  a.block_size = sh->block_size;
+  a.num_heads = sh->num_heads;
+  a.max_blocks = sh->max_blocks_per_seq;
+  a.max_ctx = sh->max_context_len;
+  a.max_query_len = sh->max_query_len;
+  a.total_queries = sh->total_queries;
+  a.out_f32 = sh->out_dtype == PA_F32 ? 1 : 0;
+  return from_hip(pa::launch_prefill(a, to_internal(sh->kv_dtype), sh->head_dim,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 pa_status paged_gather(const void* cache, const int32_t* block_tables,
                        const int32_t* context_lens, const int64_t* out_row_start, void* out,
                        int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t block_size,

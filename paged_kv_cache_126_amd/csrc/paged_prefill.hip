@@ -1,0 +1,364 @@
+// Paged prefill for gfx950: causal multi-query attention over the paged cache
+// on the matrix cores.
+//
+// What is computed ("Solving the LLM Memory Wall: A Deep Dive into
+// PagedAttention", "1. The Mathematical Foundation"): query i attends to keys
+// j <= i, o_i = sum_{j <= i} softmax_j(q_i . k_j * scale) v_j. The queries of
+// sequence s are its last n_s tokens (their K/V already appended), so the
+// same kernel serves a whole prompt (n_s = ctx_s) and a chunk of one. Keys
+// and values are fetched through the block table ("PagedAttention: Virtual
+// Memory Guide for LLM Inference", "The Mathematics of Block Translation").
+//
+// Work decomposition. One workgroup per (query tile of 128, head, sequence);
+// each of its 4 wavefronts owns 32 consecutive queries. The workgroup walks
+// the keys in tiles of 32: the tile's K and V rows are staged in LDS
+// row-major (the next tile is fetched into registers meanwhile), then every
+// wavefront
+//   1. forms S^T = K Q^T (32 keys x 32 queries) with D/16 MFMA 32x32x16
+//      steps; Q^T stays in registers as the B operand, so each lane owns one
+//      query column and 16 of the tile's keys,
+//   2. applies the causal mask and an online softmax per query (the two
+//      lanes sharing a query exchange one value),
+//   3. accumulates O^T += V^T P^T with P^T moved from the accumulator layout
+//      into the B-operand layout by one exchange between the wavefront's
+//      halves. P is split into a bf16/fp16 high part and the residual (two
+//      MFMAs), which keeps ~16 significant bits of every softmax weight.
+// Matrix layouts (verified on the device): for v_mfma_f32_32x32x16, A[i][k]
+// sits in lane i + 32 * (k / 8), element k % 8; B[k][j] in lane
+// j + 32 * (k / 8), element k % 8; D[i][j] in lane j + 32 * ((i / 4) % 2),
+// element (i % 4) + 4 * (i / 8).
+#include <type_traits>
+
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;                 // wavefronts per workgroup
+constexpr int kQW = 32;                   // queries per wavefront
+constexpr int kBM = kWaves * kQW;         // queries per workgroup
+constexpr int kBN = 32;                   // keys per tile
+constexpr float kNegBig = -1.0e30f;
+constexpr float kLazy = 8.0f;             // reference-maximum slack, log2 units
+constexpr int kTableCache = 2048;         // block-table entries staged in LDS
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// 64-bit transposing LDS read (ds_read_b64_tr_b16) of 16-bit elements.
+__device__ __forceinline__ v4i16 tr_read(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)((__attribute__((address_space(3))) uint16_t*)(p)));
+}
+
+// v_permlane32_swap: returns (a's lower half | b's lower half, a's upper
+// half | b's upper half), halves being lanes 0-31 and 32-63.
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// Combine a value with the same lane's value in the other half of the
+// wavefront (lane l and l ^ 32): both results are bit-identical.
+__device__ __forceinline__ float max_halves(float v) {
+  float a = v, b = v;
+  swap_halves(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_halves(float v) {
+  float a = v, b = v;
+  swap_halves(a, b);
+  return a + b;
+}
+
+__device__ __forceinline__ u32x4 join(v4i16 a, v4i16 b) {
+  const uint2 x = __builtin_bit_cast(uint2, a);
+  const uint2 y = __builtin_bit_cast(uint2, b);
+  return u32x4{x.x, x.y, y.x, y.y};
+}
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<BF16> {
+  using vec = bf16x8;
+  static __device__ __forceinline__ f32x16 run(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ vec from_bits(u32x4 v) { return __builtin_bit_cast(vec, v); }
+  // value rounded to the element type, and the element back in fp32
+  static __device__ __forceinline__ __bf16 narrow(float x) { return static_cast<__bf16>(x); }
+  static __device__ __forceinline__ float widen1(__bf16 x) { return static_cast<float>(x); }
+};
+
+template <>
+struct Mfma<F16> {
+  using vec = f16x8;
+  static __device__ __forceinline__ f32x16 run(vec a, vec b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ vec from_bits(u32x4 v) { return __builtin_bit_cast(vec, v); }
+  static __device__ __forceinline__ _Float16 narrow(float x) { return static_cast<_Float16>(x); }
+  static __device__ __forceinline__ float widen1(_Float16 x) { return static_cast<float>(x); }
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
+  using M = Mfma<T>;
+  using vec = typename M::vec;
+  constexpr int kSteps = D / 16;   // MFMA k-steps over the head dimension
+  constexpr int kDBlk = D / 32;    // 32-row blocks of O^T
+  constexpr int kPieces = D / 8;   // 16-byte pieces per cache row
+  constexpr int kPadK = 8;         // LDS row padding (elements) against bank conflicts
+  constexpr int kPadV = 16;
+
+  // Later query tiles see more keys (causal): dispatch them first.
+  const int qt = static_cast<int>(gridDim.x) - 1 - static_cast<int>(blockIdx.x);
+  const int h = blockIdx.y;
+  const int s = blockIdx.z;
+  int ctx = a.context_lens[s];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+  int q0 = a.query_start[s];
+  int n = a.query_start[s + 1] - q0;
+  q0 = q0 < 0 ? 0 : q0;
+  n = n < 0 ? 0 : n;
+  n = min(min(n, ctx), a.max_query_len);
+  n = min(n, a.total_queries - q0);
+  if (qt * kBM >= n) return;  // uniform over the workgroup
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;        // which 8-element half of a k-step this lane holds
+  const int col = lane & 31;         // query column (B operand / accumulator column)
+  const int first = ctx - n;         // position of the sequence's first query
+  const int my_q = qt * kBM + wave * kQW + col;
+  const bool q_ok = my_q < n;
+  const int my_pos = first + my_q;   // the query's position: it sees keys 0 .. my_pos
+  const int wg_last = first + min(n, (qt + 1) * kBM) - 1;   // last position in the workgroup
+  const int wave_first = first + qt * kBM + wave * kQW;     // first position of the wavefront
+  const int wave_last = first + min(n, qt * kBM + (wave + 1) * kQW) - 1;
+
+  const int64_t head_bytes = static_cast<int64_t>(h) * D * T::kBytes;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.num_heads) * D * T::kBytes;
+  const int64_t frame_bytes = static_cast<int64_t>(row_bytes) * a.block_size;
+  const int32_t* table_row = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
+  const uint32_t max_frame = static_cast<uint32_t>(a.num_blocks - 1);
+
+  // Q^T as the B operand: lane holds query `col`, head-dim elements
+  // 16 * step + 8 * half + [0, 8).
+  vec qb[kSteps];
+  {
+    const char* qrow = static_cast<const char*>(a.q) +
+                       ((static_cast<int64_t>(q0) + my_q) * a.num_heads + h) * D * T::kBytes;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (q_ok) v = load16(qrow + (16 * st + 8 * half) * T::kBytes);
+      qb[st] = M::from_bits(v);
+    }
+  }
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kBN][D + kPadK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kBN][D + kPadV];
+  // The workgroup's slice of the block table (frames of keys 0 .. wg_last),
+  // clamped into the pool, read once so that a tile's K/V loads need no
+  // dependent table read. Longer contexts read the table directly.
+  __shared__ uint32_t lds_tbl[kTableCache];
+  const int n_blk = wg_last / a.block_size + 1;
+  const bool tbl_in_lds = n_blk <= kTableCache;
+  if (tbl_in_lds) {
+    for (int b = threadIdx.x; b < n_blk; b += kWaves * 64)
+      lds_tbl[b] = min(static_cast<uint32_t>(table_row[b]), max_frame);
+  }
+  __syncthreads();
+
+  f32x16 o[kDBlk];
+#pragma unroll
+  for (int b = 0; b < kDBlk; ++b)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) o[b][t] = 0.f;
+  float m = kNegBig, l = 0.f;
+
+  const int n_tiles = (wg_last + kBN) / kBN;
+  // Each thread moves kPer 16-byte pieces of K and of V per tile. The next
+  // tile's pieces are fetched into registers while the current tile is
+  // computed, then written to LDS after the barrier.
+  constexpr int kPer = kBN * kPieces / (kWaves * 64);
+  static_assert(kBN * kPieces % (kWaves * 64) == 0, "tile must split evenly over the threads");
+  u32x4 pk[kPer], pv[kPer];
+  auto fetch = [&](const int k0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int piece = threadIdx.x + i * kWaves * 64;
+      const int tok = k0 + piece / kPieces;
+      const int c = piece % kPieces;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (tok <= wg_last) {
+        const int blk = tok / a.block_size;
+        const uint32_t f = tbl_in_lds ? lds_tbl[blk]
+                                      : min(static_cast<uint32_t>(table_row[blk]), max_frame);
+        const int64_t off = static_cast<int64_t>(f) * frame_bytes +
+                            static_cast<int64_t>(tok - blk * a.block_size) * row_bytes + head_bytes +
+                            16 * c;
+        kv = load16(static_cast<const char*>(a.k_cache) + off);
+        vv = load16(static_cast<const char*>(a.v_cache) + off);
+      }
+      pk[i] = kv;
+      pv[i] = vv;
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int piece = threadIdx.x + i * kWaves * 64;
+      const int key = piece / kPieces;
+      const int c = piece % kPieces;
+      *reinterpret_cast<u32x4*>(&lds_k[key][8 * c]) = pk[i];
+      *reinterpret_cast<u32x4*>(&lds_v[key][8 * c]) = pv[i];
+    }
+  };
+  fetch(0);
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    const int k0 = kt * kBN;
+    stage();
+    __syncthreads();
+    if (kt + 1 < n_tiles) fetch(k0 + kBN);
+
+    if (k0 <= wave_last) {  // the tile holds keys some query of this wavefront sees
+      // S^T = K Q^T: rows = keys of the tile, columns = this wavefront's queries
+      f32x16 st;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) st[t] = 0.f;
+#pragma unroll
+      for (int step = 0; step < kSteps; ++step) {
+        const u32x4 kbits = *reinterpret_cast<const u32x4*>(&lds_k[col][16 * step + 8 * half]);
+        st = M::run(M::from_bits(kbits), qb[step], st);
+      }
+      // causal mask + online softmax for the lane's query
+      const bool full = k0 + kBN - 1 <= wave_first;  // every key visible to every query
+      float x[16];
+      float tmax = kNegBig;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int key = k0 + (t % 4) + 8 * (t / 4) + 4 * half;
+        const bool vis = q_ok && (full || key <= my_pos);
+        x[t] = vis ? st[t] * a.scale_log2 : -__builtin_inff();
+        tmax = fmaxf(tmax, x[t]);
+      }
+      tmax = max_halves(tmax);
+      // Lazy rescaling: the reference maximum m moves (and O, l are rescaled)
+      // only when a query's maximum grows by more than kLazy (log2 units);
+      // otherwise weights are taken against the stale m and stay below
+      // 2^kLazy. The common factor 2^-m cancels in O / l, so the result is
+      // the same softmax; the O rescale, a multiply of every accumulator,
+      // becomes rare.
+      const bool grow = tmax > m + kLazy;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wavefront-uniform branch
+        const float m_new = grow ? tmax : m;
+        const float alpha = fast_exp2(m - m_new);
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < kDBlk; ++b)
+#pragma unroll
+          for (int t = 0; t < 16; ++t) o[b][t] *= alpha;
+        m = m_new;
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        x[t] = fast_exp2(x[t] - m);
+        psum += x[t];
+      }
+      psum = sum_halves(psum);
+      l += psum;
+
+      // P^T into the B-operand layout: for keys 16j .. 16j+15 the lower half
+      // of the wavefront needs keys 16j + [0,8), the upper half 16j + [8,16);
+      // the accumulator holds keys (t%4) + 8(t/4) + 4*half, so the lower
+      // half's elements 4-7 (of each 8) swap with the upper half's 0-3.
+#pragma unroll
+      for (int g = 0; g < 16; g += 8)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) swap_halves(x[g + i], x[g + i + 4]);
+      vec p_hi[2], p_lo[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const auto hi = M::narrow(x[8 * j + e]);
+          p_hi[j][e] = hi;
+          p_lo[j][e] = M::narrow(x[8 * j + e] - M::widen1(hi));
+        }
+      // O^T += V^T P^T. The V^T operand (8 consecutive keys per lane at one
+      // head-dim element) comes from the row-major V tile through transposing
+      // LDS reads: in each group of 16 lanes, a 64-bit transpose read hands
+      // lane l element j = (element l % 4 of the chunk lane 4j + l/4 points
+      // at), so lane c points at V[kb + c/4][d0 + 4 (c % 4)] and lane l
+      // receives V[kb + j][d0 + l], j = 0..3; two reads cover 8 keys.
+      const int grp16 = lane >> 4;
+      const int c16 = lane & 15;
+#pragma unroll
+      for (int b = 0; b < kDBlk; ++b) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int d0 = 32 * b + 16 * (grp16 & 1);
+          const int kb = 16 * j + 8 * (grp16 >> 1);
+          const v4i16 lo4 = tr_read(&lds_v[kb + (c16 >> 2)][d0 + 4 * (c16 & 3)]);
+          const v4i16 hi4 = tr_read(&lds_v[kb + 4 + (c16 >> 2)][d0 + 4 * (c16 & 3)]);
+          const vec va = M::from_bits(join(lo4, hi4));
+          o[b] = M::run(va, p_hi[j], o[b]);
+          o[b] = M::run(va, p_lo[j], o[b]);
+        }
+      }
+    }
+    __syncthreads();  // the next tile overwrites the staged rows
+  }
+
+  if (!q_ok) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int64_t orow = (static_cast<int64_t>(q0) + my_q) * a.num_heads + h;
+#pragma unroll
+  for (int b = 0; b < kDBlk; ++b)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int d = 32 * b + (t % 4) + 8 * (t / 4) + 4 * half;
+      const float r = o[b][t] * inv;
+      if (a.out_f32)
+        static_cast<float*>(a.out)[orow * D + d] = r;
+      else
+        static_cast<uint16_t*>(a.out)[orow * D + d] = static_cast<uint16_t>(narrow_bits(T{}, r));
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
+  dim3 grid((a.max_query_len + kBM - 1) / kBM, a.num_heads, a.num_seqs);
+  hipLaunchKernelGGL((prefill_kernel<T, D>), grid, dim3(kWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_supported(Dtype dt, int head_dim) {
+  return (dt == Dtype::BF16 || dt == Dtype::F16) && (head_dim == 64 || head_dim == 128);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, Dtype dt, int head_dim, hipStream_t stream) {
+  if (dt == Dtype::BF16) {
+    if (head_dim == 64) return launch_t<BF16, 64>(a, stream);
+    if (head_dim == 128) return launch_t<BF16, 128>(a, stream);
+  } else if (dt == Dtype::F16) {
+    if (head_dim == 64) return launch_t<F16, 64>(a, stream);
+    if (head_dim == 128) return launch_t<F16, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

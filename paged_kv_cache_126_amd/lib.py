@@ -20,7 +20,7 @@ STATUS = {0: "PA_OK", -1: "PA_EINVAL", -2: "PA_EALIGN", -3: "PA_EWORKSPACE", -4:
 EXPORTS = (
     "pa_status_string", "pa_abi_version", "kv_append", "kv_copy_blocks", "paged_attn_workspace_size",
     "paged_attn_partition_tokens", "paged_attn_decode", "paged_attn_decode_partitions",
-    "paged_attn_merge", "paged_gather",
+    "paged_attn_merge", "paged_attn_prefill", "paged_gather",
 )
 
 
@@ -43,6 +43,22 @@ class DecodeShape(ctypes.Structure):
         ("out_dtype", ctypes.c_int),
         ("partition_tokens", ctypes.c_int32),
         ("cache_policy", ctypes.c_int32),
+    ]
+
+
+class PrefillShape(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("max_context_len", ctypes.c_int32),
+        ("max_query_len", ctypes.c_int32),
+        ("total_queries", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int),
+        ("out_dtype", ctypes.c_int),
     ]
 
 
@@ -77,6 +93,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).restype = ctypes.c_int
     lib.paged_attn_merge.argtypes = [P, P, SH, P, SZ, P]
     lib.paged_attn_merge.restype = ctypes.c_int
+    lib.paged_attn_prefill.argtypes = [P, P, P, P, P, P, I32, F, P, ctypes.POINTER(PrefillShape), P]
+    lib.paged_attn_prefill.restype = ctypes.c_int
     lib.paged_gather.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32, I32, ctypes.c_int, P]
     lib.paged_gather.restype = ctypes.c_int
     _LIB = lib
@@ -208,6 +226,31 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_siz
     _check(fn, getattr(lib, fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                 _ptr(context_lens), int(block_size), float(scale), _ptr(out),
                                 ctypes.byref(shape), _ptr(workspace), ws_bytes, st))
+
+
+def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size: int,
+                       scale: float, out, max_context_len: int, max_query_len: int,
+                       stream=None) -> None:
+    """Causal attention of each sequence's last tokens into ``out`` [T, H, D];
+    see include/paged_attn.h."""
+    _dense(q, k_cache, v_cache, block_tables, context_lens, query_start, out)
+    T, H, D = q.shape
+    NB, B = k_cache.shape[0], k_cache.shape[1]
+    S = context_lens.shape[0]
+    if k_cache.shape[2:] != (H, D) or v_cache.shape != k_cache.shape or out.shape != (T, H, D):
+        raise ValueError("shape mismatch")
+    if q.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("q, k_cache and v_cache must share a dtype")
+    if query_start.shape != (S + 1,) or str(query_start.dtype) != "torch.int32":
+        raise TypeError("query_start must be int32 [S + 1]")
+    if str(block_tables.dtype) != "torch.int32" or str(context_lens.dtype) != "torch.int32":
+        raise TypeError("block_tables and context_lens must be int32")
+    shape = PrefillShape(S, H, D, B, NB, block_tables.shape[1], int(max_context_len),
+                         int(max_query_len), T, dtype_code(k_cache), dtype_code(out))
+    _check("paged_attn_prefill", load().paged_attn_prefill(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(query_start), int(block_size), float(scale), _ptr(out), ctypes.byref(shape),
+        _stream(stream)))
 
 
 def paged_gather(cache, block_tables, context_lens, out_row_start, out, max_context_len: int,

@@ -105,6 +105,65 @@ def run_gpu(w, partition_tokens: int = 0, out_dtype=None, phases: bool = False, 
     return (results, cache) if keep_cache else results
 
 
+def run_gpu_prefill(w, out_dtype=None):
+    """Play prefill workload ``w`` on cuda:0: write every token with kv_append,
+    then one paged_attn_prefill over each sequence's last query_lens tokens.
+    Returns (AttendPoint, query_start, out cpu tensor [T, H, D])."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+    from paged_kv_cache_126_amd.driver import DeviceCache, execute, plan
+
+    dev = torch.device("cuda:0")
+    events, _ = plan(w, pad=pad_frame_for(w))
+    cache = DeviceCache(w.NB, w.B, w.H, w.D, V.torch_dtype(w.dtype), dev, poison=True)
+    res = []
+
+    def on_attend(pt):
+        qs, ids = w.prefill_queries(pt.context_lens)
+        T = int(qs[-1])
+        q = V.draw_torch(w.seed, V.STREAM_Q, ids, w.H, w.D, w.dtype, dev).contiguous()
+        odt = torch.float32 if out_dtype is None else out_dtype
+        out = torch.full((T, w.H, w.D), float("nan"), dtype=odt, device=dev)
+        pkv.paged_attn_prefill(q, cache.k, cache.v, torch.from_numpy(pt.tables).to(dev),
+                               torch.from_numpy(pt.context_lens).to(dev),
+                               torch.from_numpy(qs.astype(np.int32)).to(dev), w.B, w.scale, out,
+                               int(pt.context_lens.max()), int(np.diff(qs).max()))
+        torch.cuda.synchronize()
+        res.append((pt, qs, out.cpu()))
+
+    execute(events, cache, rows_fn(w, dev), on_attend, chunk_rows=max(256, (1 << 25) // (w.H * w.D)))
+    torch.cuda.synchronize()
+    return res[-1]
+
+
+def oracle_prefill(w, pad):
+    """fp64 oracle output [T, H, D] of prefill workload ``w``."""
+    orc = oracle_default()
+    snap = obm.replay(w, pad_frame=pad)[0][-1]
+    k, v = oracle_caches(w, snap)
+    qs, ids = w.prefill_queries(snap.context_lens)
+    q = V.draw_np(w.seed, V.STREAM_Q, ids, w.H, w.D, w.dtype)
+    return snap, orc.paged_prefill(q, k, v, snap.tables, snap.context_lens, qs, w.B, w.scale, w.dtype)
+
+
+def oracle_prefill_sampled(w, context_lens, picks):
+    """fp64 outputs for sampled (seq, query index r, head): the contiguous
+    definition over tokens 0 .. position of the query."""
+    orc = oracle_default()
+    res = {}
+    for s, r, h in picks:
+        n = int(w.query_lens[s])
+        pos = int(context_lens[s]) - n + r
+        ids = w.idents(s, np.arange(pos + 1))
+        k = V.draw_np(w.seed, V.STREAM_K, ids, w.H, w.D, w.dtype, heads=[h])
+        v = V.draw_np(w.seed, V.STREAM_V, ids, w.H, w.D, w.dtype, heads=[h])
+        q = V.draw_np(w.seed, V.STREAM_Q, w.idents(s, [pos]), w.H, w.D, w.dtype, heads=[h])
+        o = orc.dense_attention(q, k, v, np.array([0, pos + 1], dtype=np.int64), w.scale, w.dtype)
+        res[(s, r, h)] = o[0, 0]
+    return res
+
+
 def oracle_caches(w, snap):
     """Host K/V caches built by the oracle's scatter from a replay snapshot."""
     orc = oracle_default()

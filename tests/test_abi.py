@@ -129,3 +129,37 @@ def test_copy_blocks_argument_errors():
     assert lib.kv_copy_blocks(p, p, p, -1, 32, 128, 16, 100, L.PA_BF16, None) == -1
     assert lib.kv_copy_blocks(p, p, ctypes.c_void_p((1 << 20) + 4), 3, 32, 128, 16, 100,
                               L.PA_BF16, None) == -2
+
+
+def prefill_shape(**kw):
+    base = dict(num_seqs=16, num_heads=32, head_dim=128, block_size=16, num_blocks=4096,
+                max_blocks_per_seq=128, max_context_len=2048, max_query_len=512,
+                total_queries=8192, kv_dtype=L.PA_BF16, out_dtype=L.PA_F32)
+    base.update(kw)
+    return L.PrefillShape(**base)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(kv_dtype=L.PA_F32, out_dtype=L.PA_F32), -1), (dict(head_dim=256), -1),
+    (dict(head_dim=32), -1), (dict(out_dtype=L.PA_F16), -1), (dict(max_context_len=4096), -1),
+    (dict(num_heads=0), -1), (dict(max_query_len=-1), -1),
+])
+def test_prefill_argument_errors(bad, code):
+    lib = pkv.load()
+    p = ctypes.c_void_p(1 << 20)
+    sh = prefill_shape(**bad)
+    assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, ctypes.byref(sh), None) == code
+
+
+def test_prefill_pointer_errors():
+    lib = pkv.load()
+    p = ctypes.c_void_p(1 << 20)
+    sh = prefill_shape()
+    assert lib.paged_attn_prefill(None, p, p, p, p, p, 16, 0.088, p, ctypes.byref(sh), None) == -1
+    assert lib.paged_attn_prefill(p, p, p, p, p, None, 16, 0.088, p, ctypes.byref(sh), None) == -1
+    assert lib.paged_attn_prefill(p, p, p, p, p, p, 32, 0.088, p, ctypes.byref(sh), None) == -1
+    assert lib.paged_attn_prefill(p, p, p, p, p, ctypes.c_void_p((1 << 20) + 2), 16, 0.088, p,
+                                  ctypes.byref(sh), None) == -2
+    assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, None, None) == -1
+    empty = prefill_shape(total_queries=0)
+    assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, ctypes.byref(empty), None) == 0

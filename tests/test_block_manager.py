@@ -145,11 +145,11 @@ def _idents_vec(w, e):
     return ids
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7])
 def test_plan_matches_oracle_replay(cfg):
     """Tables, lengths and the identity written to every slot equal the
     oracle block manager's replay, bit for bit, on every workload."""
-    w = configs.FULL[cfg]() if cfg in (1, 2, 4) else configs.small(cfg)
+    w = configs.FULL[cfg]() if cfg in (1, 2, 4, 6, 7) else configs.small(cfg)
     events, _ = plan(w)
     mine = _slot_idents(w, events)
     snaps, _, _ = obm.replay(w)

@@ -41,6 +41,7 @@ class Workload:
     frame_order: np.ndarray | None = None         # initial free list; None = 0..NB-1
     share_len: np.ndarray | None = None           # per seq: prompt positions shared with parent
     share_src: np.ndarray | None = None           # per seq: parent whose identities are shared
+    query_lens: np.ndarray | None = None          # prefill: per seq, its last tokens that are queries
     description: str = ""
 
     @property
@@ -72,6 +73,17 @@ class Workload:
     def q_idents(self, step_index: int) -> np.ndarray:
         """Query identities for the attention run ``step_index`` (0-based)."""
         return step_index * self.num_seqs + np.arange(self.num_seqs, dtype=np.int64)
+
+    def prefill_queries(self, context_lens) -> tuple:
+        """Prefill workloads: (query_start [S+1], identities [T]) of the query
+        tokens, each sequence's last query_lens[s] tokens in order. A query
+        token's value is drawn from the query stream under the token's own
+        identity."""
+        n = np.asarray(self.query_lens, dtype=np.int64)
+        start = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+        ids = np.concatenate([self.idents(s, np.arange(int(c) - int(n[s]), int(c)))
+                              for s, c in enumerate(np.asarray(context_lens))] or [np.zeros(0, np.int64)])
+        return start, ids
 
 
 def config1() -> Workload:
@@ -179,7 +191,47 @@ def config5(S: int = 256, H: int = 64, NB: int = 32768, cap: int = 8192) -> Work
     )
 
 
-FULL = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+def config6(S: int = 16, H: int = 32, chunk: int = 512, max_prefix: int = 1536,
+            NB: int = 4096) -> Workload:
+    """Chunked prefill: each sequence holds a cached prefix ~ U{0..max_prefix}
+    and appends a chunk of ``chunk`` tokens whose queries attend causally.
+
+    Draw order: ``prefix = integers(0, max_prefix + 1, S)``, then ``permutation(NB)``.
+    """
+    rng = np.random.default_rng(6)
+    prefix = rng.integers(0, max_prefix + 1, size=S)
+    order = rng.permutation(NB)
+    ctx = prefix + chunk
+    return Workload(
+        name="prefill_chunk512_bf16" if (S, H, chunk) == (16, 32, 512) else f"prefill_S{S}_H{H}_C{chunk}",
+        seed=6, dtype="bf16", H=H, D=128, B=16, NB=NB, num_seqs=S,
+        prefill=[(s, int(ctx[s])) for s in range(S)], frame_order=order,
+        query_lens=np.full(S, chunk, dtype=np.int64),
+        description=f"S={S}, H={H}, d=128, B=16, bf16, cached prefix U[0,{max_prefix}] + chunk of "
+                    f"{chunk} causal queries, permuted pool of {NB}",
+    )
+
+
+def config7(S: int = 8, H: int = 32, max_ctx: int = 2048, NB: int = 2048,
+            dtype: str = "f16") -> Workload:
+    """Whole-prompt prefill: ctx ~ U{1..max_ctx}; every token is a query.
+
+    Draw order: ``ctx = integers(1, max_ctx + 1, S)``, then ``permutation(NB)``.
+    """
+    rng = np.random.default_rng(7)
+    ctx = rng.integers(1, max_ctx + 1, size=S)
+    order = rng.permutation(NB)
+    return Workload(
+        name=f"prefill_full_{dtype}" if (S, H) == (8, 32) else f"prefill_full_S{S}_H{H}_{dtype}",
+        seed=7, dtype=dtype, H=H, D=128, B=16, NB=NB, num_seqs=S,
+        prefill=[(s, int(ctx[s])) for s in range(S)], frame_order=order,
+        query_lens=ctx.astype(np.int64),
+        description=f"S={S}, H={H}, d=128, B=16, {dtype}, whole prompts ctx U[1,{max_ctx}] as causal "
+                    f"queries, permuted pool of {NB}",
+    )
+
+
+FULL = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5, 6: config6, 7: config7}
 
 
 def small(cfg_id: int) -> Workload:
@@ -194,4 +246,8 @@ def small(cfg_id: int) -> Workload:
         return config4(prompts=3, H=4, NB=600)
     if cfg_id == 5:
         return config5(S=24, H=4, NB=4000)
+    if cfg_id == 6:
+        return config6(S=3, H=2, chunk=150, max_prefix=200, NB=200)
+    if cfg_id == 7:
+        return config7(S=3, H=2, max_ctx=300, NB=200, dtype="bf16")
     raise ValueError(cfg_id)
