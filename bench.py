@@ -167,6 +167,122 @@ def bench_prefill(args, w, pt, cache, dev):
     print(json.dumps(res), flush=True)
 
 
+def bench_prefix(args, w, dev):
+    """Prefix-sharing rounds: one step replays every round (write the rows
+    the block manager asks for with kv_append, then paged_attn_prefill over
+    them), once with prefix caching and once without."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+    from paged_kv_cache_126_amd.driver import DeviceCache, plan_prefix_rounds
+    from workloads import values as V
+
+    def prepare(caching):
+        t0 = time.perf_counter()
+        pool = None if caching else w.frames_without_caching
+        rounds, mgr = plan_prefix_rounds(w, caching, pool_frames=pool)
+        host_s = time.perf_counter() - t0
+        cache = DeviceCache(w.NB if caching else pool, w.B, w.H, w.D, V.torch_dtype(w.dtype), dev,
+                            poison=True)
+        launches = []
+        for rd in rounds:
+            wb = rd.writes
+            ids = torch.from_numpy(w.idents_rows(wb.seqs, wb.positions)).to(dev)
+            k_new = V.draw_torch(w.seed, V.STREAM_K, ids, w.H, w.D, w.dtype, dev).contiguous()
+            v_new = V.draw_torch(w.seed, V.STREAM_V, ids, w.H, w.D, w.dtype, dev).contiguous()
+            q = V.draw_torch(w.seed, V.STREAM_Q, ids, w.H, w.D, w.dtype, dev).contiguous()
+            T = int(rd.query_start[-1])
+            n = np.diff(rd.query_start).astype(np.int64)
+            ctx = rd.context_lens.astype(np.int64)
+            pairs = int(np.sum(n * (ctx - n) + n * (n + 1) // 2))
+            launches.append(dict(
+                k_new=k_new, v_new=v_new, slots=torch.from_numpy(wb.slots).to(dev), q=q,
+                out=torch.empty((T, w.H, w.D), dtype=torch.float32, device=dev),
+                bt=torch.from_numpy(rd.tables).to(dev), cl=torch.from_numpy(rd.context_lens).to(dev),
+                qs=torch.from_numpy(rd.query_start).to(dev), max_ctx=int(ctx.max()),
+                max_q=int(n.max()), rows=len(wb.slots), flops=4 * w.D * w.H * pairs))
+        return rounds, mgr, cache, launches, host_s
+
+    flush_buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def timed(cache, launches):
+        def step(evs=None):
+            for i, L in enumerate(launches):
+                if evs:
+                    evs[i][0].record()
+                if L["rows"]:
+                    pkv.kv_append(L["k_new"], L["v_new"], L["slots"], cache.k, cache.v)
+                if evs:
+                    evs[i][1].record()
+                pkv.paged_attn_prefill(L["q"], cache.k, cache.v, L["bt"], L["cl"], L["qs"], w.B,
+                                       w.scale, L["out"], L["max_ctx"], L["max_q"])
+                if evs:
+                    evs[i][2].record()
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        all_evs = []
+        for _ in range(args.steps):
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in launches]
+            if not args.no_flush:
+                torch.sum(flush_buf, dim=0, out=flush_sink)
+            step(evs)
+            all_evs.append(evs)
+        torch.cuda.synchronize()
+        step_ms = float(np.mean([e[0][0].elapsed_time(e[-1][2]) for e in all_evs]))
+        append_ms = float(np.mean([sum(r[0].elapsed_time(r[1]) for r in e) for e in all_evs]))
+        prefill_ms = float(np.mean([sum(r[1].elapsed_time(r[2]) for r in e) for e in all_evs]))
+        return step_ms, append_ms, prefill_ms
+
+    res = {}
+    for caching in (True, False):
+        rounds, mgr, cache, launches, host_s = prepare(caching)
+        step_ms, append_ms, prefill_ms = timed(cache, launches)
+        tokens = int(sum(int(rd.context_lens.sum()) for rd in rounds))
+        reused = int(sum(int(rd.reused.sum()) for rd in rounds))
+        res[caching] = dict(step_ms=step_ms, append_ms=append_ms, prefill_ms=prefill_ms,
+                            tokens=tokens, reused=reused, host_plan_s=host_s,
+                            rows=sum(L["rows"] for L in launches),
+                            flops=sum(L["flops"] for L in launches),
+                            evictions=getattr(mgr, "evictions", 0), frames=cache.k.shape[0])
+        log(f"[bench] prefix caching {'on' if caching else 'off'}: step {step_ms * 1e3:.1f} us "
+            f"(append {append_ms * 1e3:.1f}, prefill {prefill_ms * 1e3:.1f}), "
+            f"{reused}/{tokens} tokens reused, host plan {host_s * 1e3:.0f} ms")
+        del cache, launches
+    on, off = res[True], res[False]
+    value = on["tokens"] / (on["step_ms"] * 1e-3)
+    tflops = on["flops"] / (on["prefill_ms"] * 1e-3) / 1e12
+    out = {
+        "metric": "prefix-cached prefill: prompt tokens served per second (reused + computed)",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(on["step_ms"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "step": f"{w.rounds} rounds of (kv_append of the rows not reused, paged prefill over them)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "rounds": w.rounds,
+                   "prompt_tokens": on["tokens"], "reused_tokens": on["reused"],
+                   "written_rows": on["rows"], "evictions": on["evictions"],
+                   "frames": on["frames"], "cache_flush_between_steps": not args.no_flush},
+        "phases_us": {"append": round(on["append_ms"] * 1e3, 2),
+                      "prefill": round(on["prefill_ms"] * 1e3, 2)},
+        "without_caching": {"value": round(off["tokens"] / (off["step_ms"] * 1e-3), 1),
+                            "ms_per_step": round(off["step_ms"], 5),
+                            "append_us": round(off["append_ms"] * 1e3, 2),
+                            "prefill_us": round(off["prefill_ms"] * 1e3, 2),
+                            "written_rows": off["rows"], "frames": off["frames"]},
+        "speedup_vs_no_caching": round(off["step_ms"] / on["step_ms"], 3),
+        "host_plan_ms": round(on["host_plan_s"] * 1e3, 1),
+        "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_step": on["flops"]},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +324,9 @@ def main():
     else:
         w = configs.FULL[args.workload]()
     log(f"[bench] workload {w.name}: {w.description}")
+    if isinstance(w, configs.PrefixWorkload):
+        bench_prefix(args, w, dev)
+        return
 
     events, plan_mgr = plan(w)
     cache = DeviceCache(w.NB, w.B, w.H, w.D, V.torch_dtype(w.dtype), dev, poison=True)

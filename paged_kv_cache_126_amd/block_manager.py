@@ -23,6 +23,7 @@ the row index of the cache viewed as [NB * B, H, D].
 """
 from __future__ import annotations
 
+import hashlib
 from collections import deque
 from dataclasses import dataclass
 
@@ -100,6 +101,9 @@ class SeqManager:
         self._lens: dict = {}
 
     # ------------------------------------------------------------ lifecycle
+    def _allocate(self) -> int:
+        return self.pool.allocate()
+
     def init_sequence(self, sid, n_tokens: int) -> np.ndarray:
         """Allocate ceil(n_tokens / B) frames; return the n_tokens slots."""
         if sid in self._tables:
@@ -116,11 +120,11 @@ class SeqManager:
         off = t % self.B
         cow = (None, None, 0)
         if off == 0:
-            table.append(self.pool.allocate())
+            table.append(self._allocate())
         else:
             last = table[-1]
             if self.pool.ref[last] > 1:
-                new = self.pool.allocate()
+                new = self._allocate()
                 self.pool.free(last)
                 table[-1] = new
                 cow = (last, new, off)
@@ -183,3 +187,147 @@ def memory_efficiency(tokens: int, block_size: int) -> float:
     "Performance Analysis" figure: B = 4 and 7 tokens give 7 / 8)."""
     frames = -(-int(tokens) // int(block_size))
     return tokens / (frames * block_size) if frames else 1.0
+
+
+class PrefixCachingSeqManager(SeqManager):
+    """SeqManager that reuses frames of identical full blocks across requests.
+
+    "PagedAttention: Virtual Memory Guide for LLM Inference" ("2. Native
+    Synergy with RadixAttention and Prompt Caching"): a block is immutable
+    once filled, so a request whose prompt starts with the same tokens can
+    point at the frames already holding them. "Solving the LLM Memory Wall"
+    (algorithmic step 5): sequences sharing a prefix point to the same
+    physical block.
+
+    Policy:
+
+    * A full block is keyed by a chain digest over its tokens and the digest
+      of the block before it, so a key names the block's tokens together with
+      every token in front of them.
+    * The cache holds one reference on each frame it indexes. A block is
+      indexed when it fills (at request start for a prompt's full blocks, or
+      when an appended token completes it); a block whose key is already
+      indexed keeps its own frame and the index is left as it was.
+    * A new request reuses the longest run of leading full blocks whose keys
+      are indexed, stopping at the first miss; the partial last block is
+      never shared.
+    * Each indexed frame has a last-use time: when it was indexed or last
+      reused (one tick per event; a request's reuses in block order, then its
+      new entries in block order). When the free list is empty, the indexed
+      frame with the oldest last use among those referenced by the index
+      alone is dropped from the index and freed, then allocation proceeds.
+    * A request that cannot get all its frames takes none and changes
+      nothing.
+    """
+
+    def __init__(self, pool: BlockPool, block_size: int):
+        super().__init__(pool, block_size)
+        self._index: dict = {}          # digest -> frame
+        self._digest_of: dict = {}      # frame -> digest
+        self._last_use: dict = {}       # frame -> tick, for indexed frames
+        self._tick = 0
+        self._tokens: dict = {}         # sid -> token ids held
+        self._chain: dict = {}          # sid -> digests of its full blocks
+        self.hit_blocks = 0
+        self.miss_blocks = 0
+        self.evictions = 0
+
+    @staticmethod
+    def _digest(prev: bytes, tokens) -> bytes:
+        h = hashlib.blake2b(digest_size=16)
+        h.update(prev)
+        h.update(np.asarray(tokens, dtype=np.int64).tobytes())
+        return h.digest()
+
+    def _touch(self, frame: int) -> None:
+        self._tick += 1
+        self._last_use[frame] = self._tick
+
+    def _idle(self) -> list:
+        return [f for f in self._last_use if self.pool.ref[f] == 1]
+
+    def _allocate(self) -> int:
+        if self.pool.free_count == 0:
+            idle = self._idle()
+            if not idle:
+                raise MemoryError("frame pool exhausted and every cached frame is in use")
+            f = min(idle, key=self._last_use.__getitem__)
+            del self._index[self._digest_of.pop(f)]
+            del self._last_use[f]
+            self.pool.free(f)
+            self.evictions += 1
+        return self.pool.allocate()
+
+    def _register(self, sid, b: int) -> None:
+        """Block b of sid has just filled: key it, and index it if new."""
+        toks = self._tokens[sid][b * self.B:(b + 1) * self.B]
+        chain = self._chain[sid]
+        d = self._digest(chain[b - 1] if b > 0 else b"", toks)
+        chain.append(d)
+        if d not in self._index:
+            frame = self._tables[sid][b]
+            self._index[d] = frame
+            self._digest_of[frame] = d
+            self.pool.add_ref(frame)  # the index's own reference
+            self._touch(frame)
+
+    def init_sequence_tokens(self, sid, token_ids):
+        """Start a request with prompt ``token_ids``. Returns (positions,
+        slots) of the tokens whose K/V must be written: tokens of reused
+        blocks are already in the cache."""
+        if sid in self._tables:
+            raise KeyError(f"sequence {sid!r} exists")
+        toks = np.asarray(token_ids, dtype=np.int64).reshape(-1)
+        n, B = len(toks), self.B
+        hits, chain = [], []
+        prev = b""
+        for b in range(n // B):
+            d = self._digest(prev, toks[b * B:(b + 1) * B])
+            f = self._index.get(d)
+            if f is None:
+                break
+            hits.append(f)
+            chain.append(d)
+            prev = d
+        need = -(-n // B) - len(hits)
+        spare = sum(1 for f in self._idle() if f not in hits)
+        if need > self.pool.free_count + spare:
+            raise MemoryError(f"frame pool exhausted: need {need}, can free "
+                              f"{self.pool.free_count + spare}")
+        for f in hits:
+            self.pool.add_ref(f)
+            self._touch(f)
+        table = hits + [self._allocate() for _ in range(need)]
+        self.hit_blocks += len(hits)
+        self.miss_blocks += need
+        self._tables[sid] = table
+        self._lens[sid] = n
+        self._tokens[sid] = [int(t) for t in toks]
+        self._chain[sid] = chain
+        for b in range(len(hits), n // B):
+            self._register(sid, b)
+        pos = np.arange(len(hits) * B, n, dtype=np.int64)
+        return pos, self.slots(sid, pos)
+
+    def append_token_id(self, sid, token_id) -> AppendResult:
+        """Append one token; the block it completes is keyed and indexed."""
+        t = self._lens[sid]
+        r = self.append_token(sid)
+        self._tokens[sid].append(int(token_id))
+        if (t + 1) % self.B == 0:
+            self._register(sid, t // self.B)
+        return r
+
+    def fork(self, parent, child) -> None:
+        super().fork(parent, child)
+        self._tokens[child] = list(self._tokens[parent])
+        self._chain[child] = list(self._chain[parent])
+
+    def free_sequence(self, sid) -> None:
+        super().free_sequence(sid)
+        self._tokens.pop(sid, None)
+        self._chain.pop(sid, None)
+
+    @property
+    def cached_frames(self) -> int:
+        return len(self._index)

@@ -150,3 +150,54 @@ def execute(events, cache: DeviceCache, rows, on_attend, chunk_rows: int = 1 << 
                 cache.append(k_new, v_new, sl)
         else:
             on_attend(ev)
+
+
+@dataclass
+class PrefillRound:
+    """One round of requests of a prefix-sharing workload, planned on the host."""
+    seqs: list                # request (conversation) ids, in arrival order
+    writes: WriteBatch        # the K/V rows the round must write: every position not reused
+    tables: np.ndarray        # int32 [S, max_blocks]
+    context_lens: np.ndarray  # int32 [S]: prompt lengths
+    query_start: np.ndarray   # int32 [S + 1]: queries are the written positions, per request
+    reused: np.ndarray        # int64 [S]: leading prompt tokens found in the cache
+
+
+def plan_prefix_rounds(w, caching: bool = True, pad: int = -1, pool_frames: int | None = None):
+    """Host-only replay of a prefix-sharing workload (``w.rounds``,
+    ``w.requests(r)`` -> [(id, prompt_len)], ``w.tokens(id, positions)``).
+
+    With ``caching`` each request reuses the cached frames of its leading full
+    blocks and writes (and queries) only the rest; without it every request
+    takes fresh frames for its whole prompt. Requests of a round end before
+    the next round. ``pool_frames`` replaces the workload's pool by one of
+    that many frames in id order (a run without caching needs more).
+    Returns (rounds, manager)."""
+    from .block_manager import PrefixCachingSeqManager
+
+    pool = BlockPool(w.NB, w.frame_order) if pool_frames is None else BlockPool(pool_frames)
+    mgr = PrefixCachingSeqManager(pool, w.B) if caching else SeqManager(pool, w.B)
+    out = []
+    for r in range(w.rounds):
+        reqs = w.requests(r)
+        seqs, poss, slots, reused = [], [], [], []
+        for c, n in reqs:
+            if caching:
+                pos, sl = mgr.init_sequence_tokens(c, w.tokens(c, np.arange(n)))
+            else:
+                sl = mgr.init_sequence(c, n)
+                pos = np.arange(n, dtype=np.int64)
+            seqs.append(np.full(len(pos), c, dtype=np.int64))
+            poss.append(pos)
+            slots.append(np.asarray(sl, dtype=np.int64))
+            reused.append(n - len(pos))
+        ids = [c for c, _ in reqs]
+        counts = np.array([len(p) for p in poss], dtype=np.int64)
+        qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        out.append(PrefillRound(ids, WriteBatch(np.concatenate(seqs), np.concatenate(poss),
+                                                np.concatenate(slots)),
+                                mgr.tables(ids, pad), mgr.context_lens(ids), qs,
+                                np.array(reused, dtype=np.int64)))
+        for c in ids:
+            mgr.free_sequence(c)
+    return out, mgr

@@ -1,0 +1,212 @@
+"""Pins of a prefix-cache module (the oracle's :mod:`oracle.prefixcache`, or
+a copy with a planted mistake). Each ``pin_*`` takes the module, which
+exposes ``PrefixCache`` and ``replay_rounds``.
+
+The hand-worked example below was executed by hand from the rules stated in
+the oracle's header (full-prefix keys, longest leading run, one reference
+held by the cache, oldest-latest-event eviction, all-or-nothing requests).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from oracle.blockmgr import PhysicalBlockPool, SequenceGroupMemoryManager
+from workloads import configs
+
+# 6 frames handed out 0..5, B = 2. Each step: ("start", request, tokens,
+# expected reused tokens, expected table), with MemoryError for a request
+# that must fail and change nothing, or ("end", request).
+HAND_STEPS = [
+    ("start", "A", [1, 2, 3, 4, 5], 0, [0, 1, 2]),   # cold; (1,2)->0, (1,2,3,4)->1 cached
+    ("start", "B", [1, 2, 3, 9], 2, [0, 3]),         # first block reused; (1,2,3,9)->3
+    ("end", "A"),                                    # 1 stays cached, 2 is freed
+    ("start", "F", [3, 4, 5, 6], 0, [4, 5]),         # (3,4) equals block 1 of A but not its prefix
+    ("start", "G", [1, 2, 3, 4, 8], 4, [0, 1, 2]),   # reuses A's frames, one of them idle
+    ("start", "H", [5, 5, 5], MemoryError, None),    # nothing free, nothing evictable
+    ("end", "B"),
+    ("end", "F"),                                    # 3, 4 and 5 idle in the cache
+    ("start", "H", [5, 5, 5], 0, [3, 4]),            # evicts 3 (oldest), then 4
+    ("end", "G"),
+    ("end", "H"),
+    ("start", "J", [3, 4, 5, 6, 7], 0, [2, 4, 5]),   # (3,4) gone: no reuse although (3,4,5,6)
+                                                     # is cached; evicts 5, not 0 (0 was reused
+                                                     # after 5 was cached)
+]
+HAND_EVICTED = [3, 4, 5]
+HAND_FINAL = {0: (1, 2), 1: (1, 2, 3, 4), 3: (5, 5), 2: (3, 4), 4: (3, 4, 5, 6)}
+
+
+def check_invariants(pc, slot_ident=None):
+    """Reference counts = table uses + one for the cache; the free list and
+    the referenced frames partition the pool; cached prefixes are whole
+    blocks; a cached frame's slots hold the last block of its prefix."""
+    uses = {f: 0 for f in range(pc.pool.num_blocks)}
+    for t in pc.tables.values():
+        for f in t:
+            uses[f] += 1
+    for f in pc.prefix_of_frame:
+        uses[f] += 1
+    assert uses == pc.pool.ref_counts, "reference counts"
+    free = pc.pool.free_blocks
+    assert len(set(free)) == len(free)
+    assert set(free) == {f for f, n in uses.items() if n == 0}, "free list"
+    for prefix, f in pc.frame_of_prefix.items():
+        assert pc.prefix_of_frame[f] == prefix and len(prefix) % pc.B == 0, "cache keys"
+        if slot_ident is not None:
+            assert list(slot_ident[f * pc.B:(f + 1) * pc.B]) == list(prefix[-pc.B:]), "content"
+
+
+def pin_hand_worked_example(mod):
+    pc = mod.PrefixCache(6, 2)
+    for st in HAND_STEPS:
+        if st[0] == "end":
+            pc.end_request(st[1])
+            continue
+        _, sid, toks, reused, table = st
+        if reused is MemoryError:
+            before = (dict(pc.pool.ref_counts), list(pc.pool.free_blocks), dict(pc.frame_of_prefix),
+                      dict(pc.last_event))
+            try:
+                pc.start_request(sid, toks)
+            except MemoryError:
+                pass
+            else:
+                raise AssertionError(f"{sid} should not fit")
+            after = (dict(pc.pool.ref_counts), list(pc.pool.free_blocks), dict(pc.frame_of_prefix),
+                     dict(pc.last_event))
+            assert before == after, "a failed request changed the state"
+            continue
+        got = pc.start_request(sid, toks)
+        assert got == reused, (sid, got)
+        assert pc.tables[sid] == table, (sid, pc.tables[sid])
+        check_invariants(pc)
+    assert pc.evicted == HAND_EVICTED, pc.evicted
+    assert pc.pool.free_blocks == []
+    assert {f: p for p, f in pc.frame_of_prefix.items()} == HAND_FINAL
+
+
+def random_ops(seed, n_ops=400):
+    """A random stream of request starts, token appends and request ends
+    over a vocabulary of 1 to 3 tokens, B in 1..3, a pool of 3 to 11 frames."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 4))
+    NB = int(rng.integers(3, 12))
+    vocab = int(rng.integers(1, 4))
+    ops, live = [], []
+    for i in range(n_ops):
+        u = rng.random()
+        if u < 0.4 or not live:
+            ops.append(("start", i, rng.integers(0, vocab, size=int(rng.integers(0, 4 * B + 2))).tolist()))
+            live.append(i)
+        elif u < 0.7:
+            ops.append(("append", live[int(rng.integers(0, len(live)))], int(rng.integers(0, vocab))))
+        else:
+            ops.append(("end", live.pop(int(rng.integers(0, len(live))))))
+    return B, NB, ops
+
+
+def pin_random_streams_keep_invariants(mod):
+    """Under random streams: the invariants hold after every step, every
+    reused position already holds the request's own token, and a failed
+    start or append leaves the state as it was."""
+    for seed in range(12):
+        B, NB, ops = random_ops(seed)
+        pc = mod.PrefixCache(NB, B)
+        slot_ident = np.full(NB * B, -1, dtype=np.int64)
+        for op in ops:
+            state = (dict(pc.pool.ref_counts), list(pc.pool.free_blocks))
+            try:
+                if op[0] == "start":
+                    k = pc.start_request(op[1], op[2])
+                    assert k % B == 0 and k <= len(op[2])
+                    pos = np.arange(len(op[2]))
+                    slots = pc.slots(op[1], pos)
+                    toks = np.asarray(op[2], dtype=np.int64)
+                    assert np.array_equal(slot_ident[slots[:k]], toks[:k]), "reused wrong content"
+                    slot_ident[slots[k:]] = toks[k:]
+                elif op[0] == "append" and op[1] in pc.tables:
+                    slot_ident[pc.append(op[1], op[2])] = op[2]
+                elif op[0] == "end" and op[1] in pc.tables:
+                    pc.end_request(op[1])
+            except MemoryError:
+                assert state == (dict(pc.pool.ref_counts), list(pc.pool.free_blocks))
+            check_invariants(pc, slot_ident)
+
+
+def pin_reuse_is_maximal(mod):
+    """With a pool large enough that nothing is evicted, a request reuses
+    every leading full block whose prefix some earlier request held."""
+    rng = np.random.default_rng(5)
+    B = 2
+    pc = mod.PrefixCache(400, B)
+    seen = set()
+    for i in range(60):
+        toks = rng.integers(0, 2, size=int(rng.integers(0, 12))).tolist()
+        expect = 0
+        while expect + B <= len(toks) and tuple(toks[:expect + B]) in seen:
+            expect += B
+        assert pc.start_request(i, toks) == expect, (i, toks)
+        for b in range(len(toks) // B):
+            seen.add(tuple(toks[:(b + 1) * B]))
+        if rng.random() < 0.5:
+            pc.end_request(i)
+    assert not pc.evicted
+
+
+def pin_caching_off_is_demand_paging(mod):
+    w = configs.small(8)
+    NB = w.frames_without_caching
+    rounds, _ = mod.replay_rounds(w, caching=False, pool_frames=NB)
+    mgr = SequenceGroupMemoryManager(PhysicalBlockPool(NB), w.B)
+    for rd in rounds:
+        assert not rd.reused.any()
+        for i, (c, n) in enumerate(zip(rd.seqs, rd.context_lens)):
+            mgr.init_sequence(c, int(n))
+            t = mgr.block_tables[c]
+            assert list(rd.tables[i, :len(t)]) == t
+        for c in rd.seqs:
+            mgr.free_sequence(c)
+
+
+def pin_rounds_hold_every_prompt(mod):
+    """After each round of the small prefix workload every position of every
+    request, reused or written, reads back its own identity through the
+    request's table; some positions are reused and some frames evicted."""
+    w = configs.small(8)
+    rounds, pc = mod.replay_rounds(w)
+    assert any(rd.reused.any() for rd in rounds) and pc.evicted
+    for rd in rounds:
+        for i, c in enumerate(rd.seqs):
+            n = int(rd.context_lens[i])
+            pos = np.arange(n)
+            slots = rd.tables[i][pos // w.B].astype(np.int64) * w.B + pos % w.B
+            assert np.array_equal(rd.slot_ident[slots], w.idents(c, pos))
+            assert rd.reused[i] % w.B == 0 and rd.reused[i] <= n - n % w.B
+
+
+ALL = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+def run_all(mod) -> list:
+    failed = []
+    for pin in ALL:
+        try:
+            pin(mod)
+        except Exception as exc:  # noqa: BLE001
+            failed.append((pin.__name__, f"{type(exc).__name__}: {exc}"[:200]))
+    return failed
+
+
+if __name__ == "__main__":
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("mutant_prefixcache", sys.argv[1])
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[spec.name] = mod
+    spec.loader.exec_module(mod)
+    failed = run_all(mod)
+    for name, why in failed:
+        print(name, why)
+    sys.exit(len(failed))

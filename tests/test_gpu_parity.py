@@ -13,8 +13,9 @@ import numpy as np
 import pytest
 
 from tests.gpu_support import (TOL, max_err, oracle_caches, oracle_outputs, oracle_prefill,
-                               oracle_prefill_sampled, oracle_sampled, pad_frame_for, require_gpu,
-                               run_gpu, run_gpu_prefill, sample_pairs, say)
+                               oracle_prefill_sampled, oracle_prefix_rounds, oracle_prefix_sampled,
+                               oracle_sampled, pad_frame_for, require_gpu, run_gpu,
+                               run_gpu_prefill, run_gpu_prefix, sample_pairs, say)
 from workloads import configs
 from workloads import values as V
 
@@ -348,3 +349,73 @@ def test_prefill_narrow_output_within_one_ulp():
     pt, qs, out = run_gpu_prefill(w, out_dtype=torch.bfloat16)
     _, ref = oracle_prefill(w, pad_frame_for(w))
     assert _narrow_ok(out, ref, w.dtype)
+
+
+def test_prefix_cache_small_parity():
+    """Prefix caching across rounds of requests: each round writes only the
+    positions its requests do not reuse, then prefills them through tables
+    that point at cached frames. Tables and caches bit for bit, outputs
+    within tolerance, against the oracle's own prefix cache and scatter."""
+    import torch
+
+    w = configs.small(8)
+    say(f"[gpu] prefix cache {w.name}: {w.description}")
+    gpu = run_gpu_prefix(w, snapshot_caches=True)
+    ref = oracle_prefix_rounds(w)
+    tview = torch.int32 if w.dtype == "f32" else torch.int16
+    view = np.int32 if w.dtype == "f32" else np.int16
+    for r, ((rd, out, (k, v)), (ord_, qs, oref, (ok, ov))) in enumerate(zip(gpu, ref)):
+        assert rd.seqs == ord_.seqs
+        assert np.array_equal(rd.tables, ord_.tables) and np.array_equal(rd.reused, ord_.reused)
+        assert np.array_equal(rd.query_start, qs)
+        assert np.array_equal(k.view(tview).numpy(), ok.view(view))
+        assert np.array_equal(v.view(tview).numpy(), ov.view(view))
+        err = max_err(out.numpy(), oref)
+        say(f"  round {r}: {len(rd.seqs)} requests, {int(rd.reused.sum())} of "
+            f"{int(rd.context_lens.sum())} tokens reused, max-abs err {err:.3e}")
+        assert err <= TOL[w.dtype]
+    assert any(rd.reused.any() for rd, _, _ in gpu)
+
+
+def test_prefix_cache_matches_uncached_run():
+    """The same rounds without caching (every prompt written and queried in
+    full) give the same outputs at the positions the cached run queries."""
+    w = configs.small(8)
+    say(f"[gpu] prefix cache {w.name}: cached vs uncached")
+    a = run_gpu_prefix(w)
+    b = run_gpu_prefix(w, caching=False, pool_frames=w.frames_without_caching)
+    ref = oracle_prefix_rounds(w, caching=False, pool_frames=w.frames_without_caching)
+    for (ra, oa, _), (rb, ob, _), (_, qs_ref, oref, _) in zip(a, b, ref):
+        assert not rb.reused.any()
+        assert max_err(ob.numpy(), oref) <= TOL[w.dtype]
+        for i in range(len(ra.seqs)):
+            lo = int(ra.reused[i])
+            n = int(ra.context_lens[i]) - lo
+            x = oa.numpy()[ra.query_start[i]:ra.query_start[i] + n]
+            y = ob.numpy()[rb.query_start[i] + lo:rb.query_start[i] + lo + n]
+            assert max_err(x, y) <= TOL[w.dtype]
+
+
+def test_prefix_cache_full_size_sampled():
+    """The full workload (64 conversations over 8 system prompts, 4 rounds,
+    frames evicted under pool pressure): sampled outputs of every round
+    against the contiguous definition over each conversation's tokens."""
+    w = configs.FULL[8]()
+    say(f"[gpu] prefix cache {w.name}: {w.description}")
+    gpu = run_gpu_prefix(w)
+    rng = np.random.default_rng(908)
+    for r, (rd, out, _) in enumerate(gpu):
+        o = out.numpy()
+        assert np.all(np.isfinite(o))
+        picks = []
+        for i in {0, len(rd.seqs) - 1, int(rng.integers(len(rd.seqs))), int(np.argmax(rd.reused))}:
+            lo, hi = int(rd.reused[i]), int(rd.context_lens[i])
+            for pos in {lo, hi - 1, int(rng.integers(lo, hi))}:
+                for h in (0, w.H - 1):
+                    picks.append((i, pos, h))
+        ref = oracle_prefix_sampled(w, [(rd.seqs[i], pos, h) for i, pos, h in picks])
+        err = max(max_err(o[rd.query_start[i] + pos - int(rd.reused[i]), h], ref[(rd.seqs[i], pos, h)])
+                  for i, pos, h in picks)
+        say(f"  round {r}: {int(rd.reused.sum())} of {int(rd.context_lens.sum())} tokens reused, "
+            f"{len(picks)} sampled outputs, max-abs err {err:.3e}")
+        assert err <= TOL[w.dtype]

@@ -15,6 +15,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ORACLE_C = os.path.join(ROOT, "oracle", "oracle.c")
 BLOCKMGR = os.path.join(ROOT, "oracle", "blockmgr.py")
+PREFIXCACHE = os.path.join(ROOT, "oracle", "prefixcache.py")
 
 C_MUTANTS = {
     "offset_in_block": ("int64_t off = i % B;", "int64_t off = (i + 1) % B;"),
@@ -58,12 +59,39 @@ PY_MUTANTS = {
 }
 
 
+# Prefix cache (oracle/prefixcache.py). A value may list several (find,
+# replace) pairs for one mistake made in more than one place.
+PC_MUTANTS = {
+    "key_block_only": [("prefix = tuple(self.tokens[sid][:(b + 1) * self.B])",
+                        "prefix = tuple(self.tokens[sid][b * self.B:(b + 1) * self.B])"),
+                       ("f = self.frame_of_prefix.get(tuple(toks[:(b + 1) * B]))",
+                        "f = self.frame_of_prefix.get(tuple(toks[b * B:(b + 1) * B]))")],
+    "mru_eviction": ("if self.last_event[f] < self.last_event[victim]:",
+                     "if self.last_event[f] > self.last_event[victim]:"),
+    "reuse_not_an_event": ("self.pool.add_reference(f)\n            self._event(f)",
+                           "self.pool.add_reference(f)"),
+    "no_stop_at_miss": ("            if f is None:\n                break",
+                        "            if f is None:\n                continue"),
+    "cache_holds_no_ref": ("self.prefix_of_frame[frame] = prefix\n        self.pool.add_reference(frame)",
+                           "self.prefix_of_frame[frame] = prefix"),
+    "partial_block_cached": ("for b in range(len(reused), len(toks) // B):",
+                             "for b in range(len(reused), (len(toks) + B - 1) // B):"),
+    "failure_not_atomic": ("if fresh > self.pool.free_count + len(evictable):", "if False:"),
+    "evict_in_use": ("if self.pool.ref_counts[f] == 1]", "if self.pool.ref_counts[f] >= 1]"),
+    "entry_replaces_existing": ("if not self.enabled or prefix in self.frame_of_prefix:",
+                                "if not self.enabled:"),
+}
+
+
 def _mutate(src_path, find, repl, dst_path):
     with open(src_path) as f:
         src = f.read()
-    assert src.count(find) == 1, f"mutation anchor not unique: {find!r}"
+    pairs = find if isinstance(find, list) else [(find, repl)]
+    for a, b in pairs:
+        assert src.count(a) == 1, f"mutation anchor not unique: {a!r}"
+        src = src.replace(a, b)
     with open(dst_path, "w") as f:
-        f.write(src.replace(find, repl))
+        f.write(src)
 
 
 def _run_c_mutant(name, tmp):
@@ -88,12 +116,25 @@ def _run_py_mutant(name, tmp):
     return r.returncode, r.stdout + r.stderr
 
 
+def _run_pc_mutant(name, tmp):
+    m = PC_MUTANTS[name]
+    find, repl = (m, None) if isinstance(m, list) else m
+    dst = os.path.join(tmp, f"prefixcache_{name}.py")
+    _mutate(PREFIXCACHE, find, repl, dst)
+    r = subprocess.run([sys.executable, "-m", "tests.prefixcache_pins", dst], cwd=ROOT,
+                       capture_output=True, text=True, timeout=300)
+    return r.returncode, r.stdout + r.stderr
+
+
+RUNNERS = {"c": _run_c_mutant, "py": _run_py_mutant, "pc": _run_pc_mutant}
+
+
 def test_every_oracle_mutant_is_caught(tmp_path):
     tmp = str(tmp_path)
-    jobs = [("c", n) for n in C_MUTANTS] + [("py", n) for n in PY_MUTANTS]
+    jobs = ([("c", n) for n in C_MUTANTS] + [("py", n) for n in PY_MUTANTS]
+            + [("pc", n) for n in PC_MUTANTS])
     with ThreadPoolExecutor(max_workers=6) as ex:
-        futs = {(k, n): ex.submit(_run_c_mutant if k == "c" else _run_py_mutant, n, tmp)
-                for k, n in jobs}
+        futs = {(k, n): ex.submit(RUNNERS[k], n, tmp) for k, n in jobs}
     survivors = []
     for (k, n), fut in futs.items():
         rc, out = fut.result()
@@ -109,5 +150,8 @@ def test_unmutated_oracle_passes_pin_runner():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     r = subprocess.run([sys.executable, "-m", "tests.blockmgr_pins", BLOCKMGR], cwd=ROOT,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    r = subprocess.run([sys.executable, "-m", "tests.prefixcache_pins", PREFIXCACHE], cwd=ROOT,
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr

@@ -1,0 +1,157 @@
+"""Prefix caching of full blocks across requests: the oracle's prefix cache
+pinned by a hand-worked example and by invariants, the product's block
+manager checked against it, and the oracle's round replay checked against
+the contiguous attention definition.
+
+The reuse follows "PagedAttention: Virtual Memory Guide for LLM Inference"
+("2. Native Synergy with RadixAttention and Prompt Caching") and "Solving
+the LLM Memory Wall" (algorithmic step 5); the keying, lookup and eviction
+rules are readings stated in oracle/prefixcache.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from oracle.prefixcache import PrefixCache, replay_rounds
+from paged_kv_cache_126_amd.block_manager import BlockPool, PrefixCachingSeqManager
+from paged_kv_cache_126_amd.driver import plan_prefix_rounds
+from workloads import configs as C
+
+from tests import prefixcache_pins as pins
+from oracle import prefixcache
+
+
+@pytest.mark.parametrize("pin", pins.ALL, ids=lambda f: f.__name__)
+def test_oracle_prefix_cache_pin(pin):
+    pin(prefixcache)
+
+
+def test_hand_worked_example_product():
+    mgr = PrefixCachingSeqManager(BlockPool(6), 2)
+    for st in pins.HAND_STEPS:
+        if st[0] == "end":
+            mgr.free_sequence(st[1])
+            continue
+        _, sid, toks, reused, table = st
+        if reused is MemoryError:
+            before = (mgr.pool.ref.copy(), mgr.pool.free_list(), mgr.cached_frames)
+            with pytest.raises(MemoryError):
+                mgr.init_sequence_tokens(sid, toks)
+            after = (mgr.pool.ref.copy(), mgr.pool.free_list(), mgr.cached_frames)
+            assert np.array_equal(before[0], after[0]) and before[1:] == after[1:]
+            continue
+        pos, slots = mgr.init_sequence_tokens(sid, toks)
+        assert len(toks) - len(pos) == reused, sid
+        assert mgr.block_table(sid) == table, sid
+        assert np.array_equal(slots, [table[p // 2] * 2 + p % 2 for p in pos])
+    assert mgr.evictions == len(pins.HAND_EVICTED)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_product_matches_oracle(seed):
+    """Random request streams over a tiny vocabulary (equal block contents
+    after different prefixes are common), with the pool under pressure."""
+    B, NB, ops = pins.random_ops(seed)
+    pc = PrefixCache(NB, B)
+    mgr = PrefixCachingSeqManager(BlockPool(NB), B)
+    slot_ident = np.full(NB * B, -1, dtype=np.int64)
+    failures = 0
+    for op in ops:
+        if op[0] == "start":
+            _, sid, toks = op
+            try:
+                k = pc.start_request(sid, toks)
+            except MemoryError:
+                failures += 1
+                with pytest.raises(MemoryError):
+                    mgr.init_sequence_tokens(sid, toks)
+                continue
+            pos, slots = mgr.init_sequence_tokens(sid, toks)
+            assert len(toks) - len(pos) == k
+            assert np.array_equal(slots, pc.slots(sid, pos))
+            slot_ident[slots] = np.asarray(toks, dtype=np.int64)[pos]
+        elif op[0] == "append":
+            _, sid, tok = op
+            if sid not in pc.tables:
+                continue
+            try:
+                slot = pc.append(sid, tok)
+            except MemoryError:
+                failures += 1
+                with pytest.raises(MemoryError):
+                    mgr.append_token_id(sid, tok)
+                continue
+            r = mgr.append_token_id(sid, tok)
+            assert r.slot == slot and r.cow_src is None
+            slot_ident[slot] = tok
+        else:
+            if op[1] in pc.tables:
+                pc.end_request(op[1])
+            mgr.free_sequence(op[1])
+        for sid, t in pc.tables.items():
+            assert mgr.block_table(sid) == t
+        assert mgr.pool.free_list() == pc.pool.free_blocks
+        assert [int(x) for x in mgr.pool.ref] == [pc.pool.ref_counts[f] for f in range(NB)]
+        pins.check_invariants(pc, slot_ident)
+    assert mgr.cached_frames == len(pc.frame_of_prefix)
+    assert mgr.evictions == len(pc.evicted)
+
+
+def test_random_streams_exercise_every_branch():
+    """The random streams above do reach reuse, eviction and failure."""
+    reuse = evict = fail = 0
+    for seed in range(40):
+        B, NB, ops = pins.random_ops(seed)
+        pc = PrefixCache(NB, B)
+        for op in ops:
+            try:
+                if op[0] == "start":
+                    reuse += pc.start_request(op[1], op[2]) > 0
+                elif op[0] == "append" and op[1] in pc.tables:
+                    pc.append(op[1], op[2])
+                elif op[0] == "end" and op[1] in pc.tables:
+                    pc.end_request(op[1])
+            except MemoryError:
+                fail += 1
+        evict += len(pc.evicted)
+    assert reuse > 50 and evict > 50 and fail > 10
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_round_replay_product_matches_oracle(full):
+    w = C.config8() if full else C.small(8)
+    ours, mgr = plan_prefix_rounds(w)
+    theirs, pc = replay_rounds(w)
+    assert len(ours) == len(theirs) == w.rounds
+    for a, b in zip(ours, theirs):
+        assert a.seqs == b.seqs
+        assert np.array_equal(a.tables, b.tables)
+        assert np.array_equal(a.context_lens, b.context_lens)
+        assert np.array_equal(a.reused, b.reused)
+        # the written rows are exactly the positions not reused
+        slots = np.nonzero(b.slot_ident >= 0)[0]
+        assert set(a.writes.slots.tolist()) <= set(slots.tolist())
+        assert np.array_equal(b.slot_ident[a.writes.slots], w.idents_rows(a.writes.seqs,
+                                                                          a.writes.positions))
+    assert mgr.evictions == len(pc.evicted) and mgr.evictions > 0
+    assert mgr.pool.free_list() == pc.pool.free_blocks
+
+
+def test_round_prefill_through_cache_equals_contiguous_definition():
+    """The oracle's paged prefill over a replayed round equals causal
+    attention over each conversation's tokens laid out contiguously."""
+    from tests.gpu_support import oracle_prefix_rounds, oracle_prefix_sampled
+
+    w = C.small(8)
+    res = oracle_prefix_rounds(w)
+    for rd, qs, out, _ in res:
+        picks = []
+        for i, c in enumerate(rd.seqs):
+            for pos in range(int(rd.reused[i]), int(rd.context_lens[i])):
+                picks.append((c, pos, (pos + i) % w.H))
+        ref = oracle_prefix_sampled(w, picks)
+        for i, c in enumerate(rd.seqs):
+            for j, pos in enumerate(range(int(rd.reused[i]), int(rd.context_lens[i]))):
+                h = (pos + i) % w.H
+                np.testing.assert_allclose(out[qs[i] + j, h], ref[(c, pos, h)], rtol=0, atol=1e-12)

@@ -1,4 +1,4 @@
-"""The five seeded synthetic decode workloads, as plain data.
+"""The seeded synthetic workloads, as plain data.
 
 Each workload is a *schedule*: which sequences are prefilled with how many
 tokens, which are forked from which, which sequences append one token at each
@@ -14,7 +14,7 @@ identified by ``step * num_seqs + seq``. Values themselves come from
 :mod:`workloads.values`.
 
 The structure draws use ``numpy.random.default_rng(seed)`` with seed equal to
-the workload number (1-5), in the order documented per workload.
+the workload number (1-8), in the order documented per workload.
 """
 from __future__ import annotations
 
@@ -250,4 +250,127 @@ def small(cfg_id: int) -> Workload:
         return config6(S=3, H=2, chunk=150, max_prefix=200, NB=200)
     if cfg_id == 7:
         return config7(S=3, H=2, max_ctx=300, NB=200, dtype="bf16")
+    if cfg_id == 8:
+        return config8(P=2, C=6, R=4, H=2, sys_min=20, sys_max=60, turn_min=5, turn_max=40,
+                       p_active=0.6, NB=28)
     raise ValueError(cfg_id)
+
+
+@dataclass
+class PrefixWorkload:
+    """Rounds of requests whose prompts share leading tokens.
+
+    Conversation ``c`` opens with system prompt ``conv_sys[c]`` (shared by
+    every conversation that uses it). In round ``r`` each conversation with
+    ``active[c, r]`` grows by ``turn_len[c, r]`` tokens and sends one request
+    whose prompt is its whole history so far; requests of a round arrive in
+    conversation order and all end before the next round. A conversation
+    that sits a round out keeps its history, and its cached blocks may be
+    evicted meanwhile.
+
+    Token ids double as value identities: position ``i`` of a conversation
+    whose system prompt ``p`` is longer than ``i`` holds ``p * stride + i``,
+    any later position ``(P + c) * stride + i``. Equal token prefixes thus
+    hold equal values, as the K/V of a real model would. A query token's
+    value is drawn from the query stream under its own identity.
+
+    Structure draws use ``numpy.random.default_rng(seed)``: ``sys_len``,
+    then ``conv_sys``, then ``turn_len``, then ``active``, then the pool
+    order.
+    """
+
+    name: str
+    seed: int
+    dtype: str
+    H: int
+    D: int
+    B: int
+    NB: int
+    sys_len: np.ndarray       # int64 [P]
+    conv_sys: np.ndarray      # int64 [C]
+    turn_len: np.ndarray      # int64 [C, R]
+    active: np.ndarray        # bool [C, R]
+    frame_order: np.ndarray | None = None
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def num_seqs(self) -> int:
+        return int(len(self.conv_sys))
+
+    @property
+    def rounds(self) -> int:
+        return int(self.turn_len.shape[1])
+
+    def prompt_len(self, c: int, r: int) -> int:
+        """History of conversation ``c`` once round ``r`` is done."""
+        grown = self.turn_len[c, :r + 1] * self.active[c, :r + 1]
+        return int(self.sys_len[self.conv_sys[c]] + grown.sum())
+
+    @property
+    def stride(self) -> int:
+        return max(self.prompt_len(c, self.rounds - 1) for c in range(self.num_seqs)) + 1
+
+    def tokens(self, c: int, positions) -> np.ndarray:
+        """Token ids (= value identities) of conversation ``c`` at ``positions``."""
+        pos = np.asarray(positions, dtype=np.int64)
+        p = int(self.conv_sys[c])
+        P = len(self.sys_len)
+        own = (P + c) * self.stride + pos
+        return np.where(pos < self.sys_len[p], p * self.stride + pos, own)
+
+    def idents(self, c: int, positions) -> np.ndarray:
+        return self.tokens(c, positions)
+
+    def idents_rows(self, convs, positions) -> np.ndarray:
+        """Identities of rows given as parallel (conversation, position) arrays."""
+        convs = np.asarray(convs, dtype=np.int64)
+        out = np.empty(len(convs), dtype=np.int64)
+        for c in np.unique(convs):
+            m = convs == c
+            out[m] = self.idents(int(c), np.asarray(positions)[m])
+        return out
+
+    @property
+    def frames_without_caching(self) -> int:
+        """Frames the busiest round takes when nothing is shared."""
+        return max(sum(-(-n // self.B) for _, n in self.requests(r)) for r in range(self.rounds))
+
+    def requests(self, r: int) -> list:
+        """[(conversation, prompt length)] of round ``r`` in arrival order."""
+        return [(c, self.prompt_len(c, r)) for c in range(self.num_seqs) if self.active[c, r]]
+
+
+def config8(P: int = 8, C: int = 64, R: int = 4, H: int = 32, sys_min: int = 512,
+            sys_max: int = 1536, turn_min: int = 32, turn_max: int = 256, p_active: float = 0.75,
+            NB: int = 2304, dtype: str = "bf16") -> PrefixWorkload:
+    """Prefix caching across requests: C conversations over P shared system
+    prompts, R rounds of multi-turn requests, each a whole-history prompt;
+    each conversation takes part in a round with probability p_active
+    (every conversation in round 0)."""
+    rng = np.random.default_rng(8)
+    sys_len = rng.integers(sys_min, sys_max + 1, size=P).astype(np.int64)
+    conv_sys = rng.integers(0, P, size=C).astype(np.int64)
+    turn_len = rng.integers(turn_min, turn_max + 1, size=(C, R)).astype(np.int64)
+    active = rng.random((C, R)) < p_active
+    active[:, 0] = True
+    order = rng.permutation(NB)
+    full = (P, C, R, H) == (8, 64, 4, 32)
+    return PrefixWorkload(
+        name=f"prefix_cache_{dtype}" if full else f"prefix_cache_P{P}_C{C}_R{R}_H{H}",
+        seed=8, dtype=dtype, H=H, D=128, B=16, NB=NB, sys_len=sys_len, conv_sys=conv_sys,
+        turn_len=turn_len, active=active, frame_order=order,
+        description=f"{C} conversations over {P} system prompts U[{sys_min},{sys_max}], {R} rounds "
+                    f"of turns U[{turn_min},{turn_max}], whole-history prompts, H={H}, d=128, "
+                    f"B=16, {dtype}, permuted pool of {NB}",
+    )
+
+
+FULL[8] = config8
