@@ -35,18 +35,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
+KERNEL_SOURCES = {"paged_decode": ("paged_decode.hip", "pa_device.h", "pa_launch.h"),
+                  "paged_prefill": ("paged_prefill.hip", "pa_device.h", "pa_launch.h")}
+
+
+def kernel_source_digest(kind: str = "paged_decode") -> str:
     h = hashlib.sha256()
-    for f in ("paged_decode.hip", "pa_device.h", "pa_launch.h"):
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "paged_kv_cache_126_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, digest: str):
-    """HBM bytes per partition-kernel launch from committed rocprofv3 counter
-    runs, if they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_paged_decode_{workload}.json")
+def measured_traffic(workload: str, digest: str, kind: str = "paged_decode"):
+    """HBM bytes per kernel launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kind}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -127,6 +131,9 @@ def bench_prefill(args, w, pt, cache, dev):
     ctx = pt.context_lens.astype(np.int64)
     pairs = int(np.sum(n * (ctx - n) + n * (n + 1) // 2))
     flops = 4 * w.D * w.H * pairs
+    # bytes a single pass must move: every visible K and V row once, q in, out (fp32) back
+    compulsory = w.H * w.D * (2 * w.elem_bytes * int(ctx.sum()) + (w.elem_bytes + 4) * T)
+    digest = kernel_source_digest("paged_prefill")
     flush_buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
 
@@ -136,18 +143,26 @@ def bench_prefill(args, w, pt, cache, dev):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for e0, e1 in evs:
+    # pass 1: plain launches between stream events (the step time); pass 2:
+    # the kernel stamping its own start and end (its duration)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e0, e1, _, _ in evs:
         if not args.no_flush:
             torch.sum(flush_buf, dim=0, out=flush_sink)
         e0.record()
         step()
         e1.record()
+    for _, _, k0, k1 in evs:
+        if not args.no_flush:
+            torch.sum(flush_buf, dim=0, out=flush_sink)
+        with pkv.kernel_timing(k0, k1):
+            step()
     torch.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
-    tflops = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] prefill {args.steps} steps: {ms * 1e3:.1f} us, {tflops:.1f} TFLOP/s")
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    kms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    tflops = flops / (kms * 1e-3) / 1e12
+    log(f"[bench] prefill {args.steps} steps: {ms * 1e3:.1f} us (kernel alone {kms * 1e3:.1f}), "
+        f"{tflops:.1f} TFLOP/s")
     res = {
         "metric": "paged prefill attention: TFLOP/s (% of MFMA peak) + us/step",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -160,8 +175,11 @@ def bench_prefill(args, w, pt, cache, dev):
         "us_per_step": round(ms * 1e3, 2),
         "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "algorithmic_flops_per_launch": flops},
+                     "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name, digest, "paged_prefill"),
+                     "algorithmic_flops_per_launch": flops, "launch_us": round(kms * 1e3, 2),
+                     "compulsory_bytes_per_launch": compulsory},
+        "kernel_source_digest": digest,
         "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
@@ -207,7 +225,7 @@ def bench_prefix(args, w, dev):
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
 
     def timed(cache, launches):
-        def step(evs=None):
+        def step(evs=None, stamp=False):
             for i, L in enumerate(launches):
                 if evs:
                     evs[i][0].record()
@@ -215,34 +233,46 @@ def bench_prefix(args, w, dev):
                     pkv.kv_append(L["k_new"], L["v_new"], L["slots"], cache.k, cache.v)
                 if evs:
                     evs[i][1].record()
-                pkv.paged_attn_prefill(L["q"], cache.k, cache.v, L["bt"], L["cl"], L["qs"], w.B,
-                                       w.scale, L["out"], L["max_ctx"], L["max_q"])
+                if stamp:
+                    with pkv.kernel_timing(evs[i][3], evs[i][4]):  # the kernel's own start and end
+                        pkv.paged_attn_prefill(L["q"], cache.k, cache.v, L["bt"], L["cl"], L["qs"],
+                                               w.B, w.scale, L["out"], L["max_ctx"], L["max_q"])
+                else:
+                    pkv.paged_attn_prefill(L["q"], cache.k, cache.v, L["bt"], L["cl"], L["qs"], w.B,
+                                           w.scale, L["out"], L["max_ctx"], L["max_q"])
                 if evs:
                     evs[i][2].record()
 
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
+        # pass 1: plain launches (step and phase times); pass 2: the prefill
+        # kernel stamping its own start and end (its duration)
         all_evs = []
-        for _ in range(args.steps):
-            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in launches]
-            if not args.no_flush:
-                torch.sum(flush_buf, dim=0, out=flush_sink)
-            step(evs)
-            all_evs.append(evs)
+        for stamp in (False, True):
+            for _ in range(args.steps):
+                evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in launches]
+                if not args.no_flush:
+                    torch.sum(flush_buf, dim=0, out=flush_sink)
+                step(evs, stamp)
+                all_evs.append((stamp, evs))
         torch.cuda.synchronize()
+        kern_evs = [e for st, e in all_evs if st]
+        all_evs = [e for st, e in all_evs if not st]
         step_ms = float(np.mean([e[0][0].elapsed_time(e[-1][2]) for e in all_evs]))
         append_ms = float(np.mean([sum(r[0].elapsed_time(r[1]) for r in e) for e in all_evs]))
         prefill_ms = float(np.mean([sum(r[1].elapsed_time(r[2]) for r in e) for e in all_evs]))
-        return step_ms, append_ms, prefill_ms
+        kernel_ms = float(np.mean([sum(r[3].elapsed_time(r[4]) for r in e) for e in kern_evs]))
+        return step_ms, append_ms, prefill_ms, kernel_ms
 
     res = {}
     for caching in (True, False):
         rounds, mgr, cache, launches, host_s = prepare(caching)
-        step_ms, append_ms, prefill_ms = timed(cache, launches)
+        step_ms, append_ms, prefill_ms, kernel_ms = timed(cache, launches)
         tokens = int(sum(int(rd.context_lens.sum()) for rd in rounds))
         reused = int(sum(int(rd.reused.sum()) for rd in rounds))
         res[caching] = dict(step_ms=step_ms, append_ms=append_ms, prefill_ms=prefill_ms,
+                            kernel_ms=kernel_ms,
                             tokens=tokens, reused=reused, host_plan_s=host_s,
                             rows=sum(L["rows"] for L in launches),
                             flops=sum(L["flops"] for L in launches),
@@ -253,7 +283,7 @@ def bench_prefix(args, w, dev):
         del cache, launches
     on, off = res[True], res[False]
     value = on["tokens"] / (on["step_ms"] * 1e-3)
-    tflops = on["flops"] / (on["prefill_ms"] * 1e-3) / 1e12
+    tflops = on["flops"] / (on["kernel_ms"] * 1e-3) / 1e12
     out = {
         "metric": "prefix-cached prefill: prompt tokens served per second (reused + computed)",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -277,7 +307,8 @@ def bench_prefix(args, w, dev):
         "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "algorithmic_flops_per_step": on["flops"]},
+                     "algorithmic_flops_per_step": on["flops"],
+                     "launch_us_per_step": round(on["kernel_ms"] * 1e3, 2)},
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
@@ -324,6 +355,15 @@ def main():
     else:
         w = configs.FULL[args.workload]()
     log(f"[bench] workload {w.name}: {w.description}")
+    if args.copy_calibration > 0:
+        # a plain device copy of known size, for scaling hardware byte counters
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy of {args.copy_calibration} bytes done")
     if isinstance(w, configs.PrefixWorkload):
         bench_prefix(args, w, dev)
         return
@@ -385,14 +425,6 @@ def main():
     # Cache flush between steps: read a 2 GiB buffer (8x the 256 MB last-level
     # cache). A read leaves clean lines; a write would leave dirty lines whose
     # write-back competes with the timed step.
-    if args.copy_calibration > 0:
-        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"[bench] calibration copy of {args.copy_calibration} bytes done")
     flush_buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
 
@@ -406,8 +438,14 @@ def main():
             cache.append(*append_args)
             if evs is not None:
                 evs[3].record()
-        pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
-                              args.partition_tokens, phase="partitions", cache_policy=policy)
+        if evs is not None and len(evs) > 4:
+            # evs[4], evs[5]: the partition kernel's own start and end
+            with pkv.kernel_timing(evs[4], evs[5]):
+                pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
+                                      args.partition_tokens, phase="partitions", cache_policy=policy)
+        else:
+            pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
+                                  args.partition_tokens, phase="partitions", cache_policy=policy)
         if evs is not None:
             evs[1].record()
         pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
@@ -422,6 +460,7 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
 
+    # Pass 1 (the step time): plain launches bracketed by stream events.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -431,14 +470,25 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # Pass 2 (the kernel's duration): the same steps with the partition
+    # kernel stamping its own start and end. Kept apart because a stamped
+    # launch adds dispatch work that the stream events of pass 1 would count.
+    kevs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush()
+        step(kevs[i])
+    torch.cuda.synchronize()
     part_start = 3 if append_args is not None else 0
     append_ms = np.array([e[0].elapsed_time(e[3]) for e in evs]) if append_args else np.zeros(1)
     part_ms = np.array([e[part_start].elapsed_time(e[1]) for e in evs])
+    kern_ms = np.array([e[4].elapsed_time(e[5]) for e in kevs])  # kernel alone, no dispatch gap
     merge_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
     ms = float(step_ms.mean())
     log(f"[bench] {args.steps} steps: step {ms * 1e3:.1f} us (median {np.median(step_ms) * 1e3:.1f}), "
-        f"partition kernel {part_ms.mean() * 1e3:.1f} us, merge {merge_ms.mean() * 1e3:.1f} us"
+        f"partition kernel {part_ms.mean() * 1e3:.1f} us (kernel alone {kern_ms.mean() * 1e3:.1f}), "
+        f"merge {merge_ms.mean() * 1e3:.1f} us"
         + (f", kv_append {append_ms.mean() * 1e3:.1f} us" if append_args else ""))
 
     # Copy-on-write frame copies (shared-prefix workload): the step's copies,
@@ -482,7 +532,9 @@ def main():
     gbs = kv_bytes / (ms * 1e-3) / 1e9
     # The roofline counts the bytes the method must move: each distinct cache
     # row once (equal to kv_bytes unless sequences share frames).
-    part_gbs = kv_bytes_unique / (part_ms.mean() * 1e-3) / 1e9
+    # Duration: the partition kernel's own start-to-end stamps (the same
+    # interval rocprofv3's kernel trace reports), averaged over the timed steps.
+    part_gbs = kv_bytes_unique / (kern_ms.mean() * 1e-3) / 1e9
     digest = kernel_source_digest()
     traffic = measured_traffic(w.name, digest)
     res = {
@@ -512,6 +564,7 @@ def main():
         "warm_us_per_step": round(warm_ms * 1e3, 2),
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "kernels_us": {"partition": round(float(part_ms.mean()) * 1e3, 2),
+                       "partition_kernel_alone": round(float(kern_ms.mean()) * 1e3, 2),
                        "merge": round(float(merge_ms.mean()) * 1e3, 2),
                        "kv_append": round(float(append_ms.mean()) * 1e3, 2) if append_args else None},
         "roofline": {
@@ -519,6 +572,7 @@ def main():
             "achieved": round(part_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(part_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": kv_bytes_unique,
+            "launch_us": round(float(kern_ms.mean()) * 1e3, 2),
         },
         "kernel_source_digest": digest,
         "cow_frame_copies": cow,

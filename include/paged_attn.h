@@ -253,6 +253,19 @@ pa_status paged_gather(const void* cache, const int32_t* block_tables,
                        int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                        pa_dtype dtype, void* stream);
 
+/*
+ * pa_set_launch_events: kernel-accurate timing, for benchmarks and
+ * profilers. While set on a thread, every launch that thread makes of the
+ * decode partition kernel (paged_attn_decode, paged_attn_decode_partitions)
+ * or of the prefill kernel (paged_attn_prefill) stamps `start` with the
+ * kernel's own start time and `stop` with its end time (hipEvent_t handles
+ * owned by the caller, created with timing enabled; either may be NULL).
+ * An event plainly recorded on the stream around a launch also counts the
+ * dispatch gap before the kernel starts; these do not. Other kernels are
+ * unaffected. Pass NULL, NULL to return to plain launches. Never fails.
+ */
+pa_status pa_set_launch_events(void* start, void* stop);
+
 #ifdef __cplusplus
 }
 #endif

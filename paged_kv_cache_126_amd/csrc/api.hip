@@ -7,6 +7,15 @@
 #include "paged_attn.h"
 #include "pa_launch.h"
 
+namespace pa {
+
+LaunchEvents& launch_events() {
+  static thread_local LaunchEvents ev;
+  return ev;
+}
+
+}  // namespace pa
+
 namespace {
 
 // Default partition size: the largest of 2048, 1024, 512 tokens that still
@@ -316,6 +325,11 @@ pa_status paged_gather(const void* cache, const int32_t* block_tables,
                                     num_seqs, row_bytes, block_size, num_blocks,
                                     max_blocks_per_seq, max_context_len,
                                     static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_set_launch_events(void* start, void* stop) {
+  pa::launch_events() = {static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)};
+  return PA_OK;
 }
 
 }  // extern "C"

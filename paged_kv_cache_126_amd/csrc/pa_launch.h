@@ -2,10 +2,31 @@
 // the C ABI layer and the kernel translation units).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace pa {
+
+// Timing events for the attention kernels' launches on the calling thread
+// (both null: plain launches). Set through pa_set_launch_events.
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+// Launch `kernel`; with launch events set, through hipExtLaunchKernelGGL so
+// the events take the kernel's own start and end time stamps.
+template <typename K, typename... Args>
+inline hipError_t launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  const LaunchEvents& ev = launch_events();
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  return hipGetLastError();
+}
 
 // Everything one decode launch needs, passed to the kernels by value.
 struct DecodeArgs {

@@ -298,10 +298,8 @@ template <typename T, int D, int BT>
 hipError_t launch_part(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.num_heads, a.max_parts, a.num_seqs);
   if (a.stream_loads)
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, BT, true>), grid, dim3(kNW * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, BT, false>), grid, dim3(kNW * 64), 0, stream, a);
-  return hipGetLastError();
+    return launch_timed(decode_partition_kernel<T, D, BT, true>, grid, dim3(kNW * 64), stream, a);
+  return launch_timed(decode_partition_kernel<T, D, BT, false>, grid, dim3(kNW * 64), stream, a);
 }
 
 // Block sizes with a uniform-frame specialisation; other sizes take the

@@ -340,8 +340,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
 template <typename T, int D>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   dim3 grid((a.max_query_len + kBM - 1) / kBM, a.num_heads, a.num_seqs);
-  hipLaunchKernelGGL((prefill_kernel<T, D>), grid, dim3(kWaves * 64), 0, stream, a);
-  return hipGetLastError();
+  return launch_timed(prefill_kernel<T, D>, grid, dim3(kWaves * 64), stream, a);
 }
 
 }  // namespace

@@ -20,7 +20,7 @@ STATUS = {0: "PA_OK", -1: "PA_EINVAL", -2: "PA_EALIGN", -3: "PA_EWORKSPACE", -4:
 EXPORTS = (
     "pa_status_string", "pa_abi_version", "kv_append", "kv_copy_blocks", "paged_attn_workspace_size",
     "paged_attn_partition_tokens", "paged_attn_decode", "paged_attn_decode_partitions",
-    "paged_attn_merge", "paged_attn_prefill", "paged_gather",
+    "paged_attn_merge", "paged_attn_prefill", "paged_gather", "pa_set_launch_events",
 )
 
 
@@ -97,6 +97,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attn_prefill.restype = ctypes.c_int
     lib.paged_gather.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32, I32, ctypes.c_int, P]
     lib.paged_gather.restype = ctypes.c_int
+    lib.pa_set_launch_events.argtypes = [P, P]
+    lib.pa_set_launch_events.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -263,3 +265,26 @@ def paged_gather(cache, block_tables, context_lens, out_row_start, out, max_cont
                                                _ptr(out_row_start), _ptr(out), S, H, D, B, NB,
                                                block_tables.shape[1], int(max_context_len),
                                                dtype_code(cache), _stream(stream)))
+
+
+class kernel_timing:
+    """Context manager: attention-kernel launches made inside it stamp
+    ``start`` / ``stop`` (torch.cuda.Event with timing enabled) with the
+    kernel's own start and end, so ``start.elapsed_time(stop)`` is the
+    kernel's duration without the dispatch gap. With several launches inside,
+    the events hold the last one's."""
+
+    def __init__(self, start, stop):
+        self.start, self.stop = start, stop
+
+    def __enter__(self):
+        # torch creates the underlying HIP event on first record
+        for e in (self.start, self.stop):
+            if not e.cuda_event:
+                e.record()
+        load().pa_set_launch_events(self.start.cuda_event, self.stop.cuda_event)
+        return self
+
+    def __exit__(self, *exc):
+        load().pa_set_launch_events(None, None)
+        return False

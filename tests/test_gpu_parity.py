@@ -419,3 +419,37 @@ def test_prefix_cache_full_size_sampled():
         say(f"  round {r}: {int(rd.reused.sum())} of {int(rd.context_lens.sum())} tokens reused, "
             f"{len(picks)} sampled outputs, max-abs err {err:.3e}")
         assert err <= TOL[w.dtype]
+
+
+def test_kernel_timing_events_leave_results_unchanged():
+    """Launches stamped with kernel-timing events give the same bits as plain
+    launches, and the stamps bracket a positive duration inside the
+    stream-recorded events around the call."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+
+    w = configs.small(2)
+    say(f"[gpu] {w.name}: kernel-timing events")
+    res, cache = run_gpu(w, keep_cache=True)
+    pt = res[-1][0]
+    dev = cache.k.device
+    q = V.draw_torch(w.seed, V.STREAM_Q, w.q_idents(pt.step), w.H, w.D, w.dtype, dev).contiguous()
+    out = torch.empty((w.num_seqs, w.H, w.D), dtype=torch.float32, device=dev)
+    bt = torch.from_numpy(pt.tables).to(dev)
+    cl = torch.from_numpy(pt.context_lens).to(dev)
+    max_ctx = int(pt.context_lens.max())
+    ws = pkv.alloc_workspace(pkv.lib.make_shape(q, cache.k, bt, max_ctx, pkv.lib.PA_F32, 0,
+                                                pt.cache_policy), dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    with pkv.kernel_timing(ev[1], ev[2]):
+        pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
+                              cache_policy=pt.cache_policy)
+    ev[3].record()
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), res[-1][1].numpy())
+    outer = ev[0].elapsed_time(ev[3])
+    inner = ev[1].elapsed_time(ev[2])
+    say(f"  stream events {outer * 1e3:.1f} us, kernel stamps {inner * 1e3:.1f} us")
+    assert 0 < inner <= outer
