@@ -109,6 +109,8 @@ struct Mfma<F16> {
   static __device__ __forceinline__ float widen1(_Float16 x) { return static_cast<float>(x); }
 };
 
+constexpr int kXcds = 8;  // accelerator complex dies of the MI355X
+
 template <typename T, int D>
 __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
   using M = Mfma<T>;
@@ -119,10 +121,24 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
   constexpr int kPadK = 8;         // LDS row padding (elements) against bank conflicts
   constexpr int kPadV = 16;
 
-  // Later query tiles see more keys (causal): dispatch them first.
-  const int qt = static_cast<int>(gridDim.x) - 1 - static_cast<int>(blockIdx.x);
-  const int h = blockIdx.y;
-  const int s = blockIdx.z;
+  // Work item of this workgroup. Workgroups go to the 8 XCDs round-robin by
+  // linear id, and each XCD has its own L2; the query tiles of one (head,
+  // sequence) read the same keys, so they are kept on one XCD, back to back.
+  // Within a (head, sequence), later query tiles see more keys (causal) and
+  // are dispatched first.
+  const int ntiles = static_cast<int>(gridDim.x);
+  const int ngroups = static_cast<int>(gridDim.y * gridDim.z);
+  int tile = blockIdx.x;
+  int group = blockIdx.y + gridDim.y * blockIdx.z;
+  if (ngroups % kXcds == 0) {
+    const int lin = tile + ntiles * group;
+    const int idx = lin / kXcds;
+    group = (idx / ntiles) * kXcds + lin % kXcds;
+    tile = idx % ntiles;
+  }
+  const int qt = ntiles - 1 - tile;
+  const int h = group % static_cast<int>(gridDim.y);
+  const int s = group / static_cast<int>(gridDim.y);
   int ctx = a.context_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
   int q0 = a.query_start[s];
