@@ -26,10 +26,18 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
+# Per-file additions. The prefill kernel's matrix accumulators stay in the
+# general register file (MFMA "VGPR form"): with them in the accumulation
+# registers the compiler copied all of O between the two files on every key
+# tile, and the combined register count allowed only two wavefronts per SIMD.
+FILE_FLAGS = {
+    "paged_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -111,8 +111,12 @@ struct Mfma<F16> {
 
 constexpr int kXcds = 8;  // accelerator complex dies of the MI355X
 
+// Three wavefronts per SIMD (at most 168 registers per lane): the kernel
+// fits without spilling once the accumulators live in the general register
+// file, and the third wavefront hides the LDS and global-load latency.
 template <typename T, int D>
-__global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void prefill_kernel(PrefillArgs a) {
   using M = Mfma<T>;
   using vec = typename M::vec;
   constexpr int kSteps = D / 16;   // MFMA k-steps over the head dimension
