@@ -12,8 +12,8 @@
 // Work decomposition. One workgroup per (query tile of 128, head, sequence);
 // each of its 4 wavefronts owns 32 consecutive queries. The workgroup walks
 // the keys in tiles of 32: the tile's K and V rows are staged in LDS
-// row-major (the next tile is fetched into registers meanwhile), then every
-// wavefront
+// row-major, double-buffered (the next tile is fetched into registers
+// meanwhile), then every wavefront
 //   1. forms S^T = K Q^T (32 keys x 32 queries) with D/16 MFMA 32x32x16
 //      steps; Q^T stays in registers as the B operand, so each lane owns one
 //      query column and 16 of the tile's keys,
@@ -185,8 +185,8 @@ void prefill_kernel(PrefillArgs a) {
     }
   }
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kBN][D + kPadK];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kBN][D + kPadV];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_kb[2][kBN][D + kPadK];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_vb[2][kBN][D + kPadV];
   // The workgroup's slice of the block table (frames of keys 0 .. wg_last),
   // clamped into the pool, read once so that a tile's K/V loads need no
   // dependent table read. Longer contexts read the table directly.
@@ -207,9 +207,11 @@ void prefill_kernel(PrefillArgs a) {
   float m = kNegBig, l = 0.f;
 
   const int n_tiles = (wg_last + kBN) / kBN;
-  // Each thread moves kPer 16-byte pieces of K and of V per tile. The next
-  // tile's pieces are fetched into registers while the current tile is
-  // computed, then written to LDS after the barrier.
+  // Each thread moves kPer 16-byte pieces of K and of V per tile. The LDS
+  // tiles are double-buffered: the next tile's pieces are fetched into
+  // registers while the current tile is computed, then written to the other
+  // buffer (last read one tile earlier, before the previous barrier), so one
+  // barrier per tile suffices.
   constexpr int kPer = kBN * kPieces / (kWaves * 64);
   static_assert(kBN * kPieces % (kWaves * 64) == 0, "tile must split evenly over the threads");
   u32x4 pk[kPer], pv[kPer];
@@ -234,7 +236,9 @@ void prefill_kernel(PrefillArgs a) {
       pv[i] = vv;
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](const int buf) {
+    auto& lds_k = lds_kb[buf];
+    auto& lds_v = lds_vb[buf];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int piece = threadIdx.x + i * kWaves * 64;
@@ -245,11 +249,13 @@ void prefill_kernel(PrefillArgs a) {
     }
   };
   fetch(0);
+  stage(0);
+  __syncthreads();
   for (int kt = 0; kt < n_tiles; ++kt) {
     const int k0 = kt * kBN;
-    stage();
-    __syncthreads();
     if (kt + 1 < n_tiles) fetch(k0 + kBN);
+    auto& lds_k = lds_kb[kt & 1];
+    auto& lds_v = lds_vb[kt & 1];
 
     if (k0 <= wave_last) {  // the tile holds keys some query of this wavefront sees
       // S^T = K Q^T: rows = keys of the tile, columns = this wavefront's queries
@@ -264,15 +270,24 @@ void prefill_kernel(PrefillArgs a) {
       // causal mask + online softmax for the lane's query
       const bool full = k0 + kBN - 1 <= wave_first;  // every key visible to every query
       float x[16];
-      float tmax = kNegBig;
+      float tmax = -__builtin_inff();
+      if (full) {  // wavefront-uniform: no mask
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int key = k0 + (t % 4) + 8 * (t / 4) + 4 * half;
-        const bool vis = q_ok && (full || key <= my_pos);
-        x[t] = vis ? st[t] * a.scale_log2 : -__builtin_inff();
-        tmax = fmaxf(tmax, x[t]);
+        for (int t = 0; t < 16; ++t) {
+          x[t] = st[t];
+          tmax = fmaxf(tmax, x[t]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int key = k0 + (t % 4) + 8 * (t / 4) + 4 * half;
+          x[t] = (q_ok && key <= my_pos) ? st[t] : -__builtin_inff();
+          tmax = fmaxf(tmax, x[t]);
+        }
       }
-      tmax = max_halves(tmax);
+      // raw scores so far; the scale (> 0, order-preserving) is applied to the
+      // maximum here and folded into the exponent's fma below
+      tmax = max_halves(tmax) * a.scale_log2;
       // Lazy rescaling: the reference maximum m moves (and O, l are rescaled)
       // only when a query's maximum grows by more than kLazy (log2 units);
       // otherwise weights are taken against the stale m and stay below
@@ -293,7 +308,7 @@ void prefill_kernel(PrefillArgs a) {
       float psum = 0.f;
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        x[t] = fast_exp2(x[t] - m);
+        x[t] = fast_exp2(__builtin_fmaf(x[t], a.scale_log2, -m));
         psum += x[t];
       }
       psum = sum_halves(psum);
@@ -338,7 +353,8 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
     }
-    __syncthreads();  // the next tile overwrites the staged rows
+    if (kt + 1 < n_tiles) stage((kt + 1) & 1);
+    __syncthreads();
   }
 
   if (!q_ok) return;
