@@ -60,10 +60,78 @@ def measured_traffic(workload: str, digest: str, kind: str = "paged_decode"):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _compact_caches(w, tables, ctx, slot_ident):
+    """Host K/V caches holding only the frames ``tables`` use, renumbered
+    compactly (a relabelling of frames leaves attention unchanged), filled by
+    the oracle side's own replay (``slot_ident``). Returns (k, v, tables)."""
+    from oracle.oracle import STORAGE
+    from workloads import values as V
+
+    used = np.unique(np.concatenate([tables[i, :-(-int(c) // w.B)] for i, c in enumerate(ctx)]))
+    remap = {int(f): i for i, f in enumerate(used)}
+    tab = np.vectorize(lambda f: remap.get(int(f), 0))(tables).astype(np.int32)
+    nb = len(used)
+    nan = V.nan_bits(w.dtype)
+    k = np.full((nb, w.B, w.H, w.D), nan, dtype=STORAGE[w.dtype])
+    v = k.copy()
+    slots_all = (used[:, None] * w.B + np.arange(w.B)[None, :]).reshape(-1)
+    ids = slot_ident[slots_all]
+    keep = ids >= 0
+    new_slots = np.arange(nb * w.B, dtype=np.int64)[keep]
+    k.reshape(nb * w.B, w.H, w.D)[new_slots] = V.draw_np(w.seed, V.STREAM_K, ids[keep], w.H, w.D, w.dtype)
+    v.reshape(nb * w.B, w.H, w.D)[new_slots] = V.draw_np(w.seed, V.STREAM_V, ids[keep], w.H, w.D, w.dtype)
+    return k, v, tab
+
+
+def _time_bounded(fn, budget_s: float, max_runs: int = 50):
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= max_runs:
+            break
+    return float(np.median(times)), len(times)
+
+
+def cpu_baseline_prefill(w, budget_s: float = 12.0):
+    """The fp64 oracle's paged prefill on a bounded sample of a prefill
+    workload: the sequence with the fewest visible (query, key) pairs, all
+    heads, through the oracle side's own replay."""
+    from oracle import blockmgr as obm
+    from oracle.oracle import default
+    from workloads import values as V
+
+    orc = default()
+    snap = obm.replay(w)[0][-1]
+    n = np.asarray(w.query_lens, dtype=np.int64)
+    ctx = snap.context_lens.astype(np.int64)
+    pairs = n * (ctx - n) + n * (n + 1) // 2
+    sample = np.sort(np.argsort(pairs, kind="stable")[:1])
+    k, v, tab = _compact_caches(w, snap.tables[sample], snap.context_lens[sample], snap.slot_ident)
+    sub_n = n[sample]
+    qs = np.concatenate([[0], np.cumsum(sub_n)]).astype(np.int32)
+    ids = np.concatenate([w.idents(int(si), np.arange(int(ctx[si] - n[si]), int(ctx[si])))
+                          for si in sample])
+    q = V.draw_np(w.seed, V.STREAM_Q, ids, w.H, w.D, w.dtype)
+    sub_ctx = snap.context_lens[sample]
+    t, runs = _time_bounded(
+        lambda: orc.paged_prefill(q, k, v, tab, sub_ctx, qs, w.B, w.scale, w.dtype), budget_s, 20)
+    flops = 4 * w.D * w.H * int(pairs[sample].sum())
+    return {
+        "value": flops / t / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(), "kind": "oracle",
+        "sample": f"{len(sample)} of {w.num_seqs} sequences (all {w.H} heads, "
+                  f"{int(sub_n.sum())} queries, {int(pairs[sample].sum())} visible pairs), "
+                  f"fp64 C oracle, median of {runs} runs",
+        "seconds_per_sample": t,
+    }
+
+
 def cpu_baseline(w, tables, ctx, budget_s: float = 12.0):
     """The fp64 oracle on a bounded sample of the same workload (host cores)."""
     from oracle import blockmgr as obm
-    from oracle.oracle import STORAGE, default
+    from oracle.oracle import default
     from workloads import values as V
 
     orc = default()
@@ -71,39 +139,17 @@ def cpu_baseline(w, tables, ctx, budget_s: float = 12.0):
     sample = np.sort(rng.choice(w.num_seqs, size=min(16, w.num_seqs), replace=False))
     snaps, _, _ = obm.replay(w)
     snap = snaps[-1]
-    # compact the sample's frames (a relabelling of frames leaves the result
-    # unchanged) so the host cache holds only what the sample reads
-    sub_tables = snap.tables[sample]
     sub_ctx = snap.context_lens[sample]
-    used = np.unique(np.concatenate([sub_tables[i, :-(-int(c) // w.B)] for i, c in enumerate(sub_ctx)]))
-    remap = {int(f): i for i, f in enumerate(used)}
-    tab = np.vectorize(lambda f: remap.get(int(f), 0))(sub_tables).astype(np.int32)
-    nb = len(used)
-    nan = V.nan_bits(w.dtype)
-    k = np.full((nb, w.B, w.H, w.D), nan, dtype=STORAGE[w.dtype])
-    v = k.copy()
-    slots_all = (used[:, None] * w.B + np.arange(w.B)[None, :]).reshape(-1)
-    ids = snap.slot_ident[slots_all]
-    keep = ids >= 0
-    new_slots = np.arange(nb * w.B, dtype=np.int64)[keep]
-    k.reshape(nb * w.B, w.H, w.D)[new_slots] = V.draw_np(w.seed, V.STREAM_K, ids[keep], w.H, w.D, w.dtype)
-    v.reshape(nb * w.B, w.H, w.D)[new_slots] = V.draw_np(w.seed, V.STREAM_V, ids[keep], w.H, w.D, w.dtype)
+    k, v, tab = _compact_caches(w, snap.tables[sample], sub_ctx, snap.slot_ident)
     q = V.draw_np(w.seed, V.STREAM_Q, w.q_idents(0)[sample], w.H, w.D, w.dtype)
-    times = []
-    t_start = time.perf_counter()
-    while True:
-        t0 = time.perf_counter()
-        orc.paged_decode(q, k, v, tab, sub_ctx, w.B, w.scale, w.dtype)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 50:
-            break
+    t, runs = _time_bounded(lambda: orc.paged_decode(q, k, v, tab, sub_ctx, w.B, w.scale, w.dtype),
+                            budget_s)
     kv_bytes = 2 * w.H * w.D * w.elem_bytes * int(sub_ctx.sum())
-    t = float(np.median(times))
     return {
         "value": kv_bytes / t / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
         "sample": f"{len(sample)} of {w.num_seqs} sequences (all {w.H} heads, "
                   f"{int(sub_ctx.sum())} tokens, {kv_bytes / 1e6:.1f} MB of KV), fp64 C oracle, "
-                  f"median of {len(times)} runs",
+                  f"median of {runs} runs",
         "seconds_per_sample": t,
     }
 
@@ -182,6 +228,9 @@ def bench_prefill(args, w, pt, cache, dev):
         "kernel_source_digest": digest,
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        res["cpu_baseline"] = cpu_baseline_prefill(w)
     print(json.dumps(res), flush=True)
 
 
