@@ -1,0 +1,87 @@
+"""GPU parity over the shapes the kernels accept beyond the named workloads:
+every decode head dimension, block sizes on the compiled fast paths and off
+them, each storage dtype, and prefill at both head dimensions with block
+sizes from 1 to 64, sequences with no queries, and a context whose block
+table is too long to stage in LDS (the direct table-read path).
+
+Each case is a small seeded workload (random context lengths, a permuted
+frame pool) written through the product block manager and kv_append, and
+compared element by element with the fp64 oracle on the oracle's own replay.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from tests.gpu_support import (TOL, max_err, oracle_outputs, oracle_prefill, pad_frame_for,
+                               require_gpu, run_gpu, run_gpu_prefill, say)
+from workloads.configs import Workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def shape_workload(dtype, D, B, ctx, H=3, query_lens=None, seed=9, spare=4):
+    ctx = [int(c) for c in ctx]
+    rng = np.random.default_rng(seed)
+    NB = sum(-(-c // B) for c in ctx) + spare
+    return Workload(
+        name=f"shape_{dtype}_D{D}_B{B}", seed=seed, dtype=dtype, H=H, D=D, B=B, NB=NB,
+        num_seqs=len(ctx), prefill=[(s, c) for s, c in enumerate(ctx)],
+        frame_order=rng.permutation(NB),
+        query_lens=None if query_lens is None else np.asarray(query_lens, dtype=np.int64),
+        description=f"{dtype}, D={D}, B={B}, H={H}, ctx {ctx}")
+
+
+DECODE_CASES = [
+    # (dtype, D, B): fast-path block sizes 8 / 32 / 64, off-path 1 / 7 / 24
+    ("bf16", 64, 8), ("f16", 256, 64), ("bf16", 32, 7), ("f32", 128, 16), ("f16", 128, 1),
+    ("bf16", 16, 32), ("f32", 64, 24), ("f16", 32, 64),
+]
+
+
+@pytest.mark.parametrize("dtype,D,B", DECODE_CASES)
+@pytest.mark.parametrize("pt", [0, 1 << 6])
+def test_decode_shapes(dtype, D, B, pt):
+    rng = np.random.default_rng(D * 131 + B)
+    ctx = list(rng.integers(1, 400, size=5)) + [1, B, B + 1]
+    w = shape_workload(dtype, D, B, ctx)
+    # pt = 64 forces several partitions per sequence (the library rounds it
+    # up to a whole number of the kernel's chunks); 0 takes its default
+    say(f"[gpu] decode {w.description}, partition tokens {pt or 'default'}")
+    part = pt
+    res = run_gpu(w, partition_tokens=part)
+    ref = oracle_outputs(w, pad_frame_for(w))
+    for (pt_, out), (snap, o) in zip(res, ref):
+        assert np.array_equal(pt_.tables, snap.tables)
+        err = max_err(out.numpy(), o)
+        say(f"  max-abs err {err:.3e} (tol {TOL[dtype]})")
+        assert err <= TOL[dtype]
+
+
+PREFILL_CASES = [
+    # (dtype, D, B, contexts, query lengths)
+    ("bf16", 64, 16, [300, 45, 129, 1], [300, 0, 20, 1]),
+    ("f16", 64, 8, [257, 130, 64], [100, 130, 64]),
+    ("f16", 128, 64, [200, 513, 31], [200, 129, 0]),
+    ("bf16", 128, 7, [150, 99, 260], [40, 99, 260]),
+    # B = 1 and 2,200 keys: 2,200 table entries, more than the kernel stages in LDS
+    ("bf16", 128, 1, [2200, 40], [130, 40]),
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,ctx,qlens", PREFILL_CASES)
+def test_prefill_shapes(dtype, D, B, ctx, qlens):
+    w = shape_workload(dtype, D, B, ctx, H=2, query_lens=qlens, seed=10)
+    say(f"[gpu] prefill {w.description}, queries {qlens}")
+    pt, qs, out = run_gpu_prefill(w)
+    snap, ref = oracle_prefill(w, pad_frame_for(w))
+    assert np.array_equal(pt.tables, snap.tables)
+    assert int(qs[-1]) == sum(qlens)
+    err = max_err(out.numpy(), ref)
+    say(f"  {int(qs[-1])} queries, max-abs err {err:.3e} (tol {TOL[dtype]})")
+    assert err <= TOL[dtype]
