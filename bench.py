@@ -245,9 +245,12 @@ def bench_prefix(args, w, dev):
     from workloads import values as V
 
     def prepare(caching):
-        t0 = time.perf_counter()
         pool = None if caching else w.frames_without_caching
-        rounds, mgr = plan_prefix_rounds(w, caching, pool_frames=pool)
+        t0 = time.perf_counter()
+        plan_prefix_rounds(w, caching, pool_frames=pool, native=False)  # Python manager, for reference
+        host_py_s = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        rounds, mgr = plan_prefix_rounds(w, caching, pool_frames=pool)   # C++ manager
         host_s = time.perf_counter() - t0
         cache = DeviceCache(w.NB if caching else pool, w.B, w.H, w.D, V.torch_dtype(w.dtype), dev,
                             poison=True)
@@ -268,7 +271,7 @@ def bench_prefix(args, w, dev):
                 bt=torch.from_numpy(rd.tables).to(dev), cl=torch.from_numpy(rd.context_lens).to(dev),
                 qs=torch.from_numpy(rd.query_start).to(dev), max_ctx=int(ctx.max()),
                 max_q=int(n.max()), rows=len(wb.slots), flops=4 * w.D * w.H * pairs))
-        return rounds, mgr, cache, launches, host_s
+        return rounds, mgr, cache, launches, (host_s, host_py_s)
 
     flush_buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
@@ -316,19 +319,20 @@ def bench_prefix(args, w, dev):
 
     res = {}
     for caching in (True, False):
-        rounds, mgr, cache, launches, host_s = prepare(caching)
+        rounds, mgr, cache, launches, (host_s, host_py_s) = prepare(caching)
         step_ms, append_ms, prefill_ms, kernel_ms = timed(cache, launches)
         tokens = int(sum(int(rd.context_lens.sum()) for rd in rounds))
         reused = int(sum(int(rd.reused.sum()) for rd in rounds))
         res[caching] = dict(step_ms=step_ms, append_ms=append_ms, prefill_ms=prefill_ms,
                             kernel_ms=kernel_ms,
-                            tokens=tokens, reused=reused, host_plan_s=host_s,
+                            tokens=tokens, reused=reused, host_plan_s=host_s, host_plan_py_s=host_py_s,
                             rows=sum(L["rows"] for L in launches),
                             flops=sum(L["flops"] for L in launches),
                             evictions=getattr(mgr, "evictions", 0), frames=cache.k.shape[0])
         log(f"[bench] prefix caching {'on' if caching else 'off'}: step {step_ms * 1e3:.1f} us "
             f"(append {append_ms * 1e3:.1f}, prefill {prefill_ms * 1e3:.1f}), "
-            f"{reused}/{tokens} tokens reused, host plan {host_s * 1e3:.0f} ms")
+            f"{reused}/{tokens} tokens reused, host plan {host_s * 1e3:.1f} ms "
+            f"(Python manager {host_py_s * 1e3:.0f} ms)")
         del cache, launches
     on, off = res[True], res[False]
     value = on["tokens"] / (on["step_ms"] * 1e-3)
@@ -352,7 +356,9 @@ def bench_prefix(args, w, dev):
                             "prefill_us": round(off["prefill_ms"] * 1e3, 2),
                             "written_rows": off["rows"], "frames": off["frames"]},
         "speedup_vs_no_caching": round(off["step_ms"] / on["step_ms"], 3),
-        "host_plan_ms": round(on["host_plan_s"] * 1e3, 1),
+        "host_plan_ms": {"native": round(on["host_plan_s"] * 1e3, 2),
+                         "python": round(on["host_plan_py_s"] * 1e3, 2),
+                         "what": "block manager + slot lists for all rounds, before timing"},
         "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
@@ -417,7 +423,12 @@ def main():
         bench_prefix(args, w, dev)
         return
 
-    events, plan_mgr = plan(w)
+    t0 = time.perf_counter()
+    plan(w, native=False)  # Python manager, for reference
+    host_py_s = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    events, plan_mgr = plan(w)  # C++ manager
+    host_s = time.perf_counter() - t0
     cache = DeviceCache(w.NB, w.B, w.H, w.D, V.torch_dtype(w.dtype), dev, poison=True)
     points = []
 
@@ -548,7 +559,7 @@ def main():
     cow_pairs = [e.pairs for e in events if isinstance(e, CopyBlocks)]
     if cow_pairs:
         pairs = np.concatenate(cow_pairs).copy()
-        spare = plan_mgr.pool.free_list()[-len(pairs):]
+        spare = plan_mgr.free_list()[-len(pairs):]
         if len(spare) == len(pairs):
             pairs[:, 1] = spare
             pairs_dev = torch.from_numpy(pairs).to(dev)
@@ -625,6 +636,9 @@ def main():
         },
         "kernel_source_digest": digest,
         "cow_frame_copies": cow,
+        "host_plan_ms": {"native": round(host_s * 1e3, 2), "python": round(host_py_s * 1e3, 2),
+                         "what": "block manager replay of the whole schedule (prefill, forks, "
+                                 "decode steps) before timing"},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample")

@@ -131,6 +131,29 @@ class SeqManager:
         self._lens[sid] = t + 1
         return AppendResult(table[-1] * self.B + off, *cow)
 
+    def append_tokens(self, sids, token_ids=None):
+        """Append one token to each listed sequence, in order. Returns
+        (slots int64 [n], cow int64 [n, 3]: source frame, new frame, rows
+        to copy, or -1, -1, 0)."""
+        sids = list(sids)
+        slots = np.empty(len(sids), dtype=np.int64)
+        cow = np.tile(np.array([-1, -1, 0], dtype=np.int64), (len(sids), 1))
+        for i, sid in enumerate(sids):
+            r = (self.append_token(sid) if token_ids is None
+                 else self.append_token_id(sid, token_ids[i]))
+            slots[i] = r.slot
+            if r.cow_src is not None:
+                cow[i] = (r.cow_src, r.cow_dst, r.cow_rows)
+        return slots, cow
+
+    @property
+    def ref(self) -> np.ndarray:
+        """Reference count of every frame."""
+        return self.pool.ref
+
+    def free_list(self) -> list:
+        return self.pool.free_list()
+
     def fork(self, parent, child) -> None:
         if child in self._tables:
             raise KeyError(f"sequence {child!r} exists")
@@ -243,6 +266,13 @@ class PrefixCachingSeqManager(SeqManager):
         self._tick += 1
         self._last_use[frame] = self._tick
 
+    def init_sequence(self, sid, n_tokens: int) -> np.ndarray:
+        raise RuntimeError("a prefix-caching manager needs the prompt's token ids: "
+                           "use init_sequence_tokens")
+
+    def append_token(self, sid) -> AppendResult:
+        raise RuntimeError("a prefix-caching manager needs each token's id: use append_token_id")
+
     def _idle(self) -> list:
         return [f for f in self._last_use if self.pool.ref[f] == 1]
 
@@ -312,7 +342,7 @@ class PrefixCachingSeqManager(SeqManager):
     def append_token_id(self, sid, token_id) -> AppendResult:
         """Append one token; the block it completes is keyed and indexed."""
         t = self._lens[sid]
-        r = self.append_token(sid)
+        r = SeqManager.append_token(self, sid)
         self._tokens[sid].append(int(token_id))
         if (t + 1) % self.B == 0:
             self._register(sid, t // self.B)

@@ -49,11 +49,23 @@ class AttendPoint:
         return PA_CACHE_REUSE if self.shared_frames else PA_CACHE_STREAM
 
 
-def plan(schedule, pad: int = -1, max_blocks: int | None = None):
+def make_manager(num_frames: int, block_size: int, order=None, prefix_caching: bool = False,
+                 native: bool = True):
+    """A block manager: the C++ one (native) or the Python one, same rules."""
+    if native:
+        from .native_blocks import NativeBlockManager
+
+        return NativeBlockManager(num_frames, block_size, order, prefix_caching)
+    from .block_manager import PrefixCachingSeqManager
+
+    pool = BlockPool(num_frames, order)
+    return PrefixCachingSeqManager(pool, block_size) if prefix_caching else SeqManager(pool, block_size)
+
+
+def plan(schedule, pad: int = -1, max_blocks: int | None = None, native: bool = True):
     """Host-only replay. Returns (events, manager); each event is a
     WriteBatch or an AttendPoint, in the order a serving loop issues them."""
-    pool = BlockPool(schedule.NB, schedule.frame_order)
-    mgr = SeqManager(pool, schedule.B)
+    mgr = make_manager(schedule.NB, schedule.B, schedule.frame_order, native=native)
     B = schedule.B
     sids = list(range(schedule.num_seqs))
     events = []
@@ -73,7 +85,7 @@ def plan(schedule, pad: int = -1, max_blocks: int | None = None):
         nonlocal n_attend
         flush()
         events.append(AttendPoint(n_attend, mgr.tables(sids, pad, max_blocks), mgr.context_lens(sids),
-                                  bool(mgr.pool.ref.max() > 1)))
+                                  bool(mgr.ref.max() > 1)))
         n_attend += 1
 
     for s, n in schedule.prefill:
@@ -88,14 +100,23 @@ def plan(schedule, pad: int = -1, max_blocks: int | None = None):
     else:
         flush()
     for k, step in enumerate(schedule.steps):
-        for s in step:
-            t = mgr.context_len(s)
-            r = mgr.append_token(s)
-            if r.cow_src is not None:
-                copies.append((r.cow_src, r.cow_dst))  # copy-on-write of the shared frame
-            seqs.append(np.array([s], dtype=np.int64))
-            poss.append(np.array([t], dtype=np.int64))
-            slots.append(np.array([r.slot], dtype=np.int64))
+        if len(step):
+            step = np.asarray(step, dtype=np.int64)
+            # position of each appended token: the sequence's length before
+            # the step plus its earlier appearances in the step
+            uniq, inv = np.unique(step, return_inverse=True)
+            base = mgr.context_lens(uniq.tolist()).astype(np.int64)[inv]
+            seen = {}
+            rank = np.empty(len(step), dtype=np.int64)
+            for i, sq in enumerate(step.tolist()):
+                rank[i] = seen.get(sq, 0)
+                seen[sq] = rank[i] + 1
+            sl, cow = mgr.append_tokens(step.tolist())
+            for src, dst, _ in cow[cow[:, 0] >= 0]:
+                copies.append((int(src), int(dst)))  # copy-on-write of the shared frame
+            seqs.append(step)
+            poss.append(base + rank)
+            slots.append(sl)
         if k in schedule.attend_after:
             attend()
         else:
@@ -163,7 +184,8 @@ class PrefillRound:
     reused: np.ndarray        # int64 [S]: leading prompt tokens found in the cache
 
 
-def plan_prefix_rounds(w, caching: bool = True, pad: int = -1, pool_frames: int | None = None):
+def plan_prefix_rounds(w, caching: bool = True, pad: int = -1, pool_frames: int | None = None,
+                       native: bool = True):
     """Host-only replay of a prefix-sharing workload (``w.rounds``,
     ``w.requests(r)`` -> [(id, prompt_len)], ``w.tokens(id, positions)``).
 
@@ -173,10 +195,10 @@ def plan_prefix_rounds(w, caching: bool = True, pad: int = -1, pool_frames: int 
     the next round. ``pool_frames`` replaces the workload's pool by one of
     that many frames in id order (a run without caching needs more).
     Returns (rounds, manager)."""
-    from .block_manager import PrefixCachingSeqManager
-
-    pool = BlockPool(w.NB, w.frame_order) if pool_frames is None else BlockPool(pool_frames)
-    mgr = PrefixCachingSeqManager(pool, w.B) if caching else SeqManager(pool, w.B)
+    if pool_frames is None:
+        mgr = make_manager(w.NB, w.B, w.frame_order, caching, native)
+    else:
+        mgr = make_manager(pool_frames, w.B, None, caching, native)
     out = []
     for r in range(w.rounds):
         reqs = w.requests(r)

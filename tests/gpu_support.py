@@ -58,7 +58,7 @@ def pad_frame_for(w) -> int:
     from paged_kv_cache_126_amd.driver import plan
 
     _, mgr = plan(w)
-    fl = mgr.pool.free_list()
+    fl = mgr.free_list()
     return fl[-1] if fl else -1
 
 

@@ -11,10 +11,11 @@ from paged_kv_cache_126_amd import lib as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+BLOCKS_HEADER = os.path.join(ROOT, "include", "paged_blocks.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
 
@@ -26,10 +27,19 @@ def test_header_declares_the_boundary():
     assert set(names) == set(L.EXPORTS)
 
 
+def test_blocks_header_declares_the_host_manager():
+    names = declared_functions(BLOCKS_HEADER)
+    for n in ("pb_create", "pb_destroy", "pb_init_sequence", "pb_init_sequence_tokens",
+              "pb_append_tokens", "pb_fork", "pb_free_sequence", "pb_block_tables"):
+        assert n in names
+    assert len(names) == 12
+
+
 def test_library_exports_every_declared_symbol():
     lib = pkv.load()
-    for name in declared_functions():
-        assert hasattr(lib, name), name
+    for header in (HEADER, BLOCKS_HEADER):
+        for name in declared_functions(header):
+            assert hasattr(lib, name), name
     assert lib.pa_abi_version() == 1
 
 

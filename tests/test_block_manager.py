@@ -36,7 +36,7 @@ def test_worked_example_tables_and_free_list():
             assert table == state["tables"][r], (state["after"], r)
             fill = [min(w.B, int(p.context_lens[s]) - b * w.B) for b in range(len(table))]
             assert fill == state["fill"][r]
-    fl = mgr.pool.free_list()
+    fl = mgr.free_list()
     last = g["states"][-1]
     assert fl[:3] == last["free_head"] and fl[-1:] == last["free_tail"]
     assert len(fl) == last["free_count"]

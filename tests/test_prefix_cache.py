@@ -91,8 +91,8 @@ def test_random_product_matches_oracle(seed):
             mgr.free_sequence(op[1])
         for sid, t in pc.tables.items():
             assert mgr.block_table(sid) == t
-        assert mgr.pool.free_list() == pc.pool.free_blocks
-        assert [int(x) for x in mgr.pool.ref] == [pc.pool.ref_counts[f] for f in range(NB)]
+        assert mgr.free_list() == pc.pool.free_blocks
+        assert [int(x) for x in mgr.ref] == [pc.pool.ref_counts[f] for f in range(NB)]
         pins.check_invariants(pc, slot_ident)
     assert mgr.cached_frames == len(pc.frame_of_prefix)
     assert mgr.evictions == len(pc.evicted)
@@ -135,7 +135,7 @@ def test_round_replay_product_matches_oracle(full):
         assert np.array_equal(b.slot_ident[a.writes.slots], w.idents_rows(a.writes.seqs,
                                                                           a.writes.positions))
     assert mgr.evictions == len(pc.evicted) and mgr.evictions > 0
-    assert mgr.pool.free_list() == pc.pool.free_blocks
+    assert mgr.free_list() == pc.pool.free_blocks
 
 
 def test_round_prefill_through_cache_equals_contiguous_definition():

@@ -18,6 +18,7 @@ the workload number (1-8), in the order documented per workload.
 """
 from __future__ import annotations
 
+import functools
 import math
 from dataclasses import dataclass, field
 
@@ -314,7 +315,7 @@ class PrefixWorkload:
         grown = self.turn_len[c, :r + 1] * self.active[c, :r + 1]
         return int(self.sys_len[self.conv_sys[c]] + grown.sum())
 
-    @property
+    @functools.cached_property
     def stride(self) -> int:
         return max(self.prompt_len(c, self.rounds - 1) for c in range(self.num_seqs)) + 1
 
