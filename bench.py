@@ -342,7 +342,8 @@ def bench_prefix(args, w, dev):
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(on["step_ms"], 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
-        "step": f"{w.rounds} rounds of (kv_append of the rows not reused, paged prefill over them)",
+        "step": f"{w.rounds} rounds of (kv_append of the rows not reused, paged prefill over them); "
+                "the rounds' decode steps are planned but not timed",
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "rounds": w.rounds,
                    "prompt_tokens": on["tokens"], "reused_tokens": on["reused"],

@@ -138,13 +138,21 @@ class PrefixCache:
 
 
 @dataclass
+class DecodePoint:
+    seqs: list                # conversations that appended a token in this step, in order
+    tables: np.ndarray        # int32 [len(seqs), max_blocks] after the step
+    context_lens: np.ndarray  # int32 [len(seqs)]: lengths after the step
+
+
+@dataclass
 class Round:
     seqs: list                # conversations of the round, in arrival order
-    tables: np.ndarray        # int32 [S, max_blocks], padded
+    tables: np.ndarray        # int32 [S, max_blocks], padded (after the prefill)
     context_lens: np.ndarray  # int32 [S]: prompt lengths
     reused: np.ndarray        # int64 [S]: leading tokens found in the cache
     slot_ident: np.ndarray    # int64 [NB * B]: identity in each slot after the round's writes
-    free_list: list
+    free_list: list           # after the round's requests ended
+    decode: list              # DecodePoint per decode step of the round
 
 
 def replay_rounds(w, pad_frame: int = -1, caching: bool = True, pool_frames: int | None = None):
@@ -152,8 +160,13 @@ def replay_rounds(w, pad_frame: int = -1, caching: bool = True, pool_frames: int
 
     Each request writes the identities of its positions from ``reused`` on;
     with ``caching`` off nothing is reused and every request writes its
-    whole prompt. ``pool_frames`` replaces the workload's pool by one of that
-    many frames in id order."""
+    whole prompt. Then the round's decode steps append one generated token
+    per listed request (its token id is the next position's). Attention at
+    a decode step only reads positions written by then, and a frame is
+    reallocated within a round only after eviction, when no request of the
+    round references it; so one snapshot of the slots after the round serves
+    every attention point of the round. ``pool_frames`` replaces the
+    workload's pool by one of that many frames in id order."""
     if pool_frames is None:
         pc = PrefixCache(w.NB, w.B, w.frame_order, enabled=caching)
     else:
@@ -168,14 +181,26 @@ def replay_rounds(w, pad_frame: int = -1, caching: bool = True, pool_frames: int
             reused.append(k)
             pos = np.arange(k, n)
             slot_ident[pc.slots(c, pos)] = w.idents(c, pos)
-        mb = max(1, max(len(pc.tables[c]) for c, _ in reqs))
-        tables = np.full((len(reqs), mb), pad_frame, dtype=np.int32)
-        for i, (c, _) in enumerate(reqs):
-            tables[i, :len(pc.tables[c])] = pc.tables[c]
-        rounds.append(Round([c for c, _ in reqs], tables,
-                            np.array([n for _, n in reqs], dtype=np.int32),
-                            np.array(reused, dtype=np.int64), slot_ident.copy(),
-                            list(pc.pool.free_blocks)))
-        for c, _ in reqs:
+        def table_of(seqs):
+            mb = max(1, max(len(pc.tables[c]) for c in seqs))
+            t = np.full((len(seqs), mb), pad_frame, dtype=np.int32)
+            for i, c in enumerate(seqs):
+                t[i, :len(pc.tables[c])] = pc.tables[c]
+            return t
+
+        seqs = [c for c, _ in reqs]
+        tables = table_of(seqs)
+        decode = []
+        for step in w.decode_steps(r):
+            for c in step:
+                pos = len(pc.tokens[c])
+                slot = pc.append(c, int(w.tokens(c, [pos])[0]))
+                slot_ident[slot] = w.idents(c, [pos])[0]
+            decode.append(DecodePoint(list(step), table_of(step),
+                                      np.array([len(pc.tokens[c]) for c in step], dtype=np.int32)))
+        for c in seqs:
             pc.end_request(c)
+        rounds.append(Round(seqs, tables, np.array([n for _, n in reqs], dtype=np.int32),
+                            np.array(reused, dtype=np.int64), slot_ident.copy(),
+                            list(pc.pool.free_blocks), decode))
     return rounds, pc

@@ -174,6 +174,14 @@ def execute(events, cache: DeviceCache, rows, on_attend, chunk_rows: int = 1 << 
 
 
 @dataclass
+class DecodeStep:
+    """One decode step of a round: one generated token per listed request."""
+    writes: WriteBatch        # the step's K/V rows (one per request)
+    tables: np.ndarray        # int32 [len(seqs), max_blocks] after the appends
+    context_lens: np.ndarray  # int32 [len(seqs)]
+
+
+@dataclass
 class PrefillRound:
     """One round of requests of a prefix-sharing workload, planned on the host."""
     seqs: list                # request (conversation) ids, in arrival order
@@ -182,6 +190,7 @@ class PrefillRound:
     context_lens: np.ndarray  # int32 [S]: prompt lengths
     query_start: np.ndarray   # int32 [S + 1]: queries are the written positions, per request
     reused: np.ndarray        # int64 [S]: leading prompt tokens found in the cache
+    decode: list = None       # DecodeStep per decode step after the prefill
 
 
 def plan_prefix_rounds(w, caching: bool = True, pad: int = -1, pool_frames: int | None = None,
@@ -216,10 +225,17 @@ def plan_prefix_rounds(w, caching: bool = True, pad: int = -1, pool_frames: int 
         ids = [c for c, _ in reqs]
         counts = np.array([len(p) for p in poss], dtype=np.int64)
         qs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-        out.append(PrefillRound(ids, WriteBatch(np.concatenate(seqs), np.concatenate(poss),
-                                                np.concatenate(slots)),
-                                mgr.tables(ids, pad), mgr.context_lens(ids), qs,
-                                np.array(reused, dtype=np.int64)))
+        rd = PrefillRound(ids, WriteBatch(np.concatenate(seqs), np.concatenate(poss),
+                                          np.concatenate(slots)),
+                          mgr.tables(ids, pad), mgr.context_lens(ids), qs,
+                          np.array(reused, dtype=np.int64), [])
+        for step in (w.decode_steps(r) if hasattr(w, "decode_steps") else []):
+            pos = mgr.context_lens(step).astype(np.int64)
+            toks = np.array([int(w.tokens(c, [p])[0]) for c, p in zip(step, pos)], dtype=np.int64)
+            sl, _ = mgr.append_tokens(step, toks if caching else None)
+            rd.decode.append(DecodeStep(WriteBatch(np.asarray(step, dtype=np.int64), pos, sl),
+                                        mgr.tables(step, pad), mgr.context_lens(step)))
+        out.append(rd)
         for c in ids:
             mgr.free_sequence(c)
     return out, mgr

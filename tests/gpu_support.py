@@ -225,9 +225,11 @@ __all__ = ["TOL", "say", "require_gpu", "run_gpu", "oracle_outputs", "oracle_sam
 
 def run_gpu_prefix(w, caching: bool = True, pool_frames=None, snapshot_caches: bool = False):
     """Play prefix-sharing workload ``w`` on cuda:0, round by round: write the
-    rows the block manager asks for with kv_append, then one
-    paged_attn_prefill over the written positions. Returns a list of
-    (PrefillRound, out cpu tensor [T, H, D], (k, v) cpu caches or None)."""
+    rows the block manager asks for with kv_append, one paged_attn_prefill
+    over the written positions, then the round's decode steps (kv_append of
+    the step's tokens, paged_attn_decode over the step's requests). Returns
+    a list of (PrefillRound, prefill out cpu tensor [T, H, D], (k, v) cpu
+    caches after the round or None, [decode out cpu tensor per step])."""
     import torch
 
     import paged_kv_cache_126_amd as pkv
@@ -254,14 +256,35 @@ def run_gpu_prefix(w, caching: bool = True, pool_frames=None, snapshot_caches: b
                                torch.from_numpy(rd.query_start).to(dev), w.B, w.scale, out,
                                int(rd.context_lens.max()), int(np.diff(rd.query_start).max()))
         torch.cuda.synchronize()
+        pout = out.cpu()
+        douts = []
+        for st in rd.decode or []:
+            wb = st.writes
+            k_new, v_new = rows(wb.seqs, wb.positions)
+            cache.append(k_new, v_new, torch.from_numpy(wb.slots).to(dev))
+            ids = torch.from_numpy(w.idents_rows(wb.seqs, wb.positions)).to(dev)
+            qd = V.draw_torch(w.seed, V.STREAM_Q, ids, w.H, w.D, w.dtype, dev).contiguous()
+            bt = torch.from_numpy(st.tables).to(dev)
+            cl = torch.from_numpy(st.context_lens).to(dev)
+            dout = torch.full((len(wb.seqs), w.H, w.D), float("nan"), dtype=torch.float32,
+                              device=dev)
+            max_ctx = int(st.context_lens.max())
+            shape = pkv.lib.make_shape(qd, cache.k, bt, max_ctx, pkv.lib.PA_F32, 0,
+                                       pkv.lib.PA_CACHE_REUSE)
+            ws = pkv.alloc_workspace(shape, dev)
+            pkv.paged_attn_decode(qd, cache.k, cache.v, bt, cl, w.B, w.scale, dout, max_ctx, ws,
+                                  cache_policy=pkv.lib.PA_CACHE_REUSE)
+            douts.append(dout.cpu())
+        torch.cuda.synchronize()
         snap = (cache.k.cpu(), cache.v.cpu()) if snapshot_caches else None
-        res.append((rd, out.cpu(), snap))
+        res.append((rd, pout, snap, douts))
     return res
 
 
-def oracle_prefix_rounds(w, caching: bool = True, pool_frames=None):
+def oracle_prefix_rounds(w, caching: bool = True, pool_frames=None, with_decode: bool = True):
     """The oracle's rounds of ``w`` with fp64 outputs [T, H, D] over the
-    positions each request writes, and its host caches after each round."""
+    positions each request writes, its host caches after each round, and
+    (with_decode) the fp64 decode outputs of every decode step."""
     from oracle.prefixcache import replay_rounds
 
     orc = oracle_default()
@@ -276,7 +299,14 @@ def oracle_prefix_rounds(w, caching: bool = True, pool_frames=None):
                               for i, c in enumerate(rd.seqs)])
         q = V.draw_np(w.seed, V.STREAM_Q, ids, w.H, w.D, w.dtype)
         out = orc.paged_prefill(q, k, v, rd.tables, rd.context_lens, qs, w.B, w.scale, w.dtype)
-        res.append((rd, qs, out, (k, v)))
+        douts = []
+        if with_decode:
+            for pt in rd.decode:
+                qids = np.array([w.idents(c, [int(n) - 1])[0] for c, n in zip(pt.seqs, pt.context_lens)])
+                qd = V.draw_np(w.seed, V.STREAM_Q, qids, w.H, w.D, w.dtype)
+                douts.append(orc.paged_decode(qd, k, v, pt.tables, pt.context_lens, w.B, w.scale,
+                                              w.dtype))
+        res.append((rd, qs, out, (k, v), douts))
     return res
 
 

@@ -156,34 +156,58 @@ def pin_reuse_is_maximal(mod):
 
 
 def pin_caching_off_is_demand_paging(mod):
+    """With the cache off, a round's prompts take ceil(L / B) frames each and
+    its decode steps append by the t mod B rule: the oracle's plain block
+    manager gives the same tables at every point."""
     w = configs.small(8)
     NB = w.frames_without_caching
     rounds, _ = mod.replay_rounds(w, caching=False, pool_frames=NB)
     mgr = SequenceGroupMemoryManager(PhysicalBlockPool(NB), w.B)
+    assert any(rd.decode for rd in rounds)
     for rd in rounds:
         assert not rd.reused.any()
         for i, (c, n) in enumerate(zip(rd.seqs, rd.context_lens)):
             mgr.init_sequence(c, int(n))
             t = mgr.block_tables[c]
             assert list(rd.tables[i, :len(t)]) == t
+        for pt in rd.decode:
+            for i, c in enumerate(pt.seqs):
+                mgr.append_token(c)
+            for i, c in enumerate(pt.seqs):
+                t = mgr.block_tables[c]
+                assert list(pt.tables[i, :len(t)]) == t and pt.context_lens[i] == mgr.seq_lens[c]
         for c in rd.seqs:
             mgr.free_sequence(c)
 
 
 def pin_rounds_hold_every_prompt(mod):
     """After each round of the small prefix workload every position of every
-    request, reused or written, reads back its own identity through the
-    request's table; some positions are reused and some frames evicted."""
+    request, reused or written, prompt or generated, reads back its own
+    identity through the request's table at every attention point; some
+    positions are reused and some frames evicted; a later round reuses
+    blocks that generated tokens completed."""
     w = configs.small(8)
     rounds, pc = mod.replay_rounds(w)
     assert any(rd.reused.any() for rd in rounds) and pc.evicted
-    for rd in rounds:
+
+    def check(seqs, tables, lens, slot_ident):
+        for i, c in enumerate(seqs):
+            pos = np.arange(int(lens[i]))
+            slots = tables[i][pos // w.B].astype(np.int64) * w.B + pos % w.B
+            assert np.array_equal(slot_ident[slots], w.idents(c, pos))
+
+    reused_generated = False
+    for r, rd in enumerate(rounds):
+        check(rd.seqs, rd.tables, rd.context_lens, rd.slot_ident)
+        for pt in rd.decode:
+            check(pt.seqs, pt.tables, pt.context_lens, rd.slot_ident)
         for i, c in enumerate(rd.seqs):
             n = int(rd.context_lens[i])
-            pos = np.arange(n)
-            slots = rd.tables[i][pos // w.B].astype(np.int64) * w.B + pos % w.B
-            assert np.array_equal(rd.slot_ident[slots], w.idents(c, pos))
             assert rd.reused[i] % w.B == 0 and rd.reused[i] <= n - n % w.B
+            for k in range(r):  # a generated token of an earlier round lies in the reused blocks
+                if w.active[c, k] and w.gen(c, k) > 0 and w.prompt_len(c, k) < rd.reused[i]:
+                    reused_generated = True
+    assert reused_generated
 
 
 ALL = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

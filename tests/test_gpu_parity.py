@@ -354,9 +354,11 @@ def test_prefill_narrow_output_within_one_ulp():
 
 def test_prefix_cache_small_parity():
     """Prefix caching across rounds of requests: each round writes only the
-    positions its requests do not reuse, then prefills them through tables
-    that point at cached frames. Tables and caches bit for bit, outputs
-    within tolerance, against the oracle's own prefix cache and scatter."""
+    positions its requests do not reuse, prefills them through tables that
+    point at cached frames, then generates tokens with decode steps (blocks
+    the generated tokens fill are cached for later rounds). Tables and caches
+    bit for bit, prefill and decode outputs within tolerance, against the
+    oracle's own prefix cache and scatter."""
     import torch
 
     w = configs.small(8)
@@ -365,17 +367,24 @@ def test_prefix_cache_small_parity():
     ref = oracle_prefix_rounds(w)
     tview = torch.int32 if w.dtype == "f32" else torch.int16
     view = np.int32 if w.dtype == "f32" else np.int16
-    for r, ((rd, out, (k, v)), (ord_, qs, oref, (ok, ov))) in enumerate(zip(gpu, ref)):
+    for r, ((rd, out, (k, v), douts), (ord_, qs, oref, (ok, ov), drefs)) in enumerate(zip(gpu, ref)):
         assert rd.seqs == ord_.seqs
         assert np.array_equal(rd.tables, ord_.tables) and np.array_equal(rd.reused, ord_.reused)
         assert np.array_equal(rd.query_start, qs)
         assert np.array_equal(k.view(tview).numpy(), ok.view(view))
         assert np.array_equal(v.view(tview).numpy(), ov.view(view))
         err = max_err(out.numpy(), oref)
+        assert len(douts) == len(drefs) == len(ord_.decode)
+        derr = 0.0
+        for st, pt, d, dr in zip(rd.decode, ord_.decode, douts, drefs):
+            assert np.array_equal(st.tables, pt.tables)
+            assert np.array_equal(st.context_lens, pt.context_lens)
+            derr = max(derr, max_err(d.numpy(), dr))
         say(f"  round {r}: {len(rd.seqs)} requests, {int(rd.reused.sum())} of "
-            f"{int(rd.context_lens.sum())} tokens reused, max-abs err {err:.3e}")
-        assert err <= TOL[w.dtype]
-    assert any(rd.reused.any() for rd, _, _ in gpu)
+            f"{int(rd.context_lens.sum())} tokens reused, prefill max-abs err {err:.3e}, "
+            f"{len(douts)} decode steps, max-abs err {derr:.3e}")
+        assert err <= TOL[w.dtype] and derr <= TOL[w.dtype]
+    assert any(g[0].reused.any() for g in gpu)
 
 
 def test_prefix_cache_matches_uncached_run():
@@ -386,9 +395,11 @@ def test_prefix_cache_matches_uncached_run():
     a = run_gpu_prefix(w)
     b = run_gpu_prefix(w, caching=False, pool_frames=w.frames_without_caching)
     ref = oracle_prefix_rounds(w, caching=False, pool_frames=w.frames_without_caching)
-    for (ra, oa, _), (rb, ob, _), (_, qs_ref, oref, _) in zip(a, b, ref):
+    for (ra, oa, _, da), (rb, ob, _, db), (_, qs_ref, oref, _, dref) in zip(a, b, ref):
         assert not rb.reused.any()
         assert max_err(ob.numpy(), oref) <= TOL[w.dtype]
+        for x, y, z in zip(da, db, dref):  # decode steps: cached, uncached, oracle
+            assert max_err(x.numpy(), z) <= TOL[w.dtype] and max_err(y.numpy(), z) <= TOL[w.dtype]
         for i in range(len(ra.seqs)):
             lo = int(ra.reused[i])
             n = int(ra.context_lens[i]) - lo
@@ -398,16 +409,29 @@ def test_prefix_cache_matches_uncached_run():
 
 
 def test_prefix_cache_full_size_sampled():
-    """The full workload (64 conversations over 8 system prompts, 4 rounds,
-    frames evicted under pool pressure): sampled outputs of every round
-    against the contiguous definition over each conversation's tokens."""
+    """The full workload (64 conversations over 8 system prompts, 4 rounds
+    of prompts and generated tokens, frames evicted under pool pressure):
+    sampled prefill outputs of every round, and sampled decode outputs of
+    its first and last decode step, against the contiguous definition over
+    each conversation's tokens."""
     w = configs.FULL[8]()
     say(f"[gpu] prefix cache {w.name}: {w.description}")
     gpu = run_gpu_prefix(w)
     rng = np.random.default_rng(908)
-    for r, (rd, out, _) in enumerate(gpu):
+    for r, (rd, out, _, douts) in enumerate(gpu):
         o = out.numpy()
         assert np.all(np.isfinite(o))
+        for si in sorted({0, len(rd.decode) - 1}):
+            st, d = rd.decode[si], douts[si].numpy()
+            assert np.all(np.isfinite(d))
+            rows = sorted({0, len(st.context_lens) - 1, int(rng.integers(len(st.context_lens)))})
+            dpicks = [(int(st.writes.seqs[j]), int(st.context_lens[j]) - 1, h)
+                      for j in rows for h in (0, w.H - 1)]
+            dref = oracle_prefix_sampled(w, dpicks)
+            derr = max(max_err(d[j, h], dref[(int(st.writes.seqs[j]), int(st.context_lens[j]) - 1, h)])
+                       for j in rows for h in (0, w.H - 1))
+            say(f"  round {r} decode step {si}: {len(dpicks)} sampled outputs, max-abs err {derr:.3e}")
+            assert derr <= TOL[w.dtype]
         picks = []
         for i in {0, len(rd.seqs) - 1, int(rng.integers(len(rd.seqs))), int(np.argmax(rd.reused))}:
             lo, hi = int(rd.reused[i]), int(rd.context_lens[i])

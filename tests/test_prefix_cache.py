@@ -134,6 +134,13 @@ def test_round_replay_product_matches_oracle(full):
         assert set(a.writes.slots.tolist()) <= set(slots.tolist())
         assert np.array_equal(b.slot_ident[a.writes.slots], w.idents_rows(a.writes.seqs,
                                                                           a.writes.positions))
+        assert len(a.decode) == len(b.decode)
+        for x, y in zip(a.decode, b.decode):
+            assert list(x.writes.seqs) == y.seqs
+            assert np.array_equal(x.tables, y.tables)
+            assert np.array_equal(x.context_lens, y.context_lens)
+            assert np.array_equal(b.slot_ident[x.writes.slots],
+                                  w.idents_rows(x.writes.seqs, x.writes.positions))
     assert mgr.evictions == len(pc.evicted) and mgr.evictions > 0
     assert mgr.free_list() == pc.pool.free_blocks
 
@@ -145,7 +152,13 @@ def test_round_prefill_through_cache_equals_contiguous_definition():
 
     w = C.small(8)
     res = oracle_prefix_rounds(w)
-    for rd, qs, out, _ in res:
+    for rd, qs, out, _, douts in res:
+        # decode steps: the last token's query over the whole conversation so far
+        for pt, d in zip(rd.decode, douts):
+            picks = [(c, int(n) - 1, (i + 1) % w.H) for i, (c, n) in enumerate(zip(pt.seqs, pt.context_lens))]
+            ref = oracle_prefix_sampled(w, picks)
+            for i, (c, pos, h) in enumerate(picks):
+                np.testing.assert_allclose(d[i, h], ref[(c, pos, h)], rtol=0, atol=1e-12)
         picks = []
         for i, c in enumerate(rd.seqs):
             for pos in range(int(rd.reused[i]), int(rd.context_lens[i])):

@@ -253,7 +253,7 @@ def small(cfg_id: int) -> Workload:
         return config7(S=3, H=2, max_ctx=300, NB=200, dtype="bf16")
     if cfg_id == 8:
         return config8(P=2, C=6, R=4, H=2, sys_min=20, sys_max=60, turn_min=5, turn_max=40,
-                       p_active=0.6, NB=28)
+                       p_active=0.6, gen_min=2, gen_max=12, NB=36)
     raise ValueError(cfg_id)
 
 
@@ -265,9 +265,13 @@ class PrefixWorkload:
     every conversation that uses it). In round ``r`` each conversation with
     ``active[c, r]`` grows by ``turn_len[c, r]`` tokens and sends one request
     whose prompt is its whole history so far; requests of a round arrive in
-    conversation order and all end before the next round. A conversation
-    that sits a round out keeps its history, and its cached blocks may be
-    evicted meanwhile.
+    conversation order. After the round's prefill each request generates
+    ``gen_len[c, r]`` tokens, one per decode step (step g appends a token to
+    every request with more than g to generate, in conversation order, then
+    decode attention runs over the round's requests); the generated tokens
+    join the conversation's history. All requests end before the next round.
+    A conversation that sits a round out keeps its history, and its cached
+    blocks may be evicted meanwhile.
 
     Token ids double as value identities: position ``i`` of a conversation
     whose system prompt ``p`` is longer than ``i`` holds ``p * stride + i``,
@@ -276,8 +280,8 @@ class PrefixWorkload:
     value is drawn from the query stream under its own identity.
 
     Structure draws use ``numpy.random.default_rng(seed)``: ``sys_len``,
-    then ``conv_sys``, then ``turn_len``, then ``active``, then the pool
-    order.
+    then ``conv_sys``, then ``turn_len``, then ``active``, then ``gen_len``,
+    then the pool order.
     """
 
     name: str
@@ -291,6 +295,7 @@ class PrefixWorkload:
     conv_sys: np.ndarray      # int64 [C]
     turn_len: np.ndarray      # int64 [C, R]
     active: np.ndarray        # bool [C, R]
+    gen_len: np.ndarray | None = None  # int64 [C, R]: tokens generated per round (None: 0)
     frame_order: np.ndarray | None = None
     description: str = ""
 
@@ -310,14 +315,24 @@ class PrefixWorkload:
     def rounds(self) -> int:
         return int(self.turn_len.shape[1])
 
+    def gen(self, c: int, r: int) -> int:
+        return 0 if self.gen_len is None else int(self.gen_len[c, r])
+
+    def history(self, c: int, r: int) -> int:
+        """Tokens of conversation ``c`` once round ``r`` is done (r = -1:
+        before the first round)."""
+        grown = self.turn_len[c, :r + 1].copy()
+        if self.gen_len is not None:
+            grown = grown + self.gen_len[c, :r + 1]
+        return int(self.sys_len[self.conv_sys[c]] + (grown * self.active[c, :r + 1]).sum())
+
     def prompt_len(self, c: int, r: int) -> int:
-        """History of conversation ``c`` once round ``r`` is done."""
-        grown = self.turn_len[c, :r + 1] * self.active[c, :r + 1]
-        return int(self.sys_len[self.conv_sys[c]] + grown.sum())
+        """Prompt of conversation ``c``'s request in round ``r``."""
+        return self.history(c, r - 1) + int(self.turn_len[c, r])
 
     @functools.cached_property
     def stride(self) -> int:
-        return max(self.prompt_len(c, self.rounds - 1) for c in range(self.num_seqs)) + 1
+        return max(self.history(c, self.rounds - 1) for c in range(self.num_seqs)) + 1
 
     def tokens(self, c: int, positions) -> np.ndarray:
         """Token ids (= value identities) of conversation ``c`` at ``positions``."""
@@ -342,7 +357,14 @@ class PrefixWorkload:
     @property
     def frames_without_caching(self) -> int:
         """Frames the busiest round takes when nothing is shared."""
-        return max(sum(-(-n // self.B) for _, n in self.requests(r)) for r in range(self.rounds))
+        return max(sum(-(-(n + self.gen(c, r)) // self.B) for c, n in self.requests(r))
+                   for r in range(self.rounds))
+
+    def decode_steps(self, r: int) -> list:
+        """Per decode step of round ``r``: the conversations appending a token."""
+        reqs = [c for c, _ in self.requests(r)]
+        steps = max((self.gen(c, r) for c in reqs), default=0)
+        return [[c for c in reqs if self.gen(c, r) > g] for g in range(steps)]
 
     def requests(self, r: int) -> list:
         """[(conversation, prompt length)] of round ``r`` in arrival order."""
@@ -351,26 +373,29 @@ class PrefixWorkload:
 
 def config8(P: int = 8, C: int = 64, R: int = 4, H: int = 32, sys_min: int = 512,
             sys_max: int = 1536, turn_min: int = 32, turn_max: int = 256, p_active: float = 0.75,
-            NB: int = 2304, dtype: str = "bf16") -> PrefixWorkload:
+            gen_min: int = 16, gen_max: int = 64, NB: int = 2816,
+            dtype: str = "bf16") -> PrefixWorkload:
     """Prefix caching across requests: C conversations over P shared system
-    prompts, R rounds of multi-turn requests, each a whole-history prompt;
-    each conversation takes part in a round with probability p_active
-    (every conversation in round 0)."""
+    prompts, R rounds of multi-turn requests, each a whole-history prompt
+    followed by gen_len ~ U{gen_min..gen_max} generated tokens; each
+    conversation takes part in a round with probability p_active (every
+    conversation in round 0)."""
     rng = np.random.default_rng(8)
     sys_len = rng.integers(sys_min, sys_max + 1, size=P).astype(np.int64)
     conv_sys = rng.integers(0, P, size=C).astype(np.int64)
     turn_len = rng.integers(turn_min, turn_max + 1, size=(C, R)).astype(np.int64)
     active = rng.random((C, R)) < p_active
     active[:, 0] = True
+    gen_len = rng.integers(gen_min, gen_max + 1, size=(C, R)).astype(np.int64)
     order = rng.permutation(NB)
     full = (P, C, R, H) == (8, 64, 4, 32)
     return PrefixWorkload(
         name=f"prefix_cache_{dtype}" if full else f"prefix_cache_P{P}_C{C}_R{R}_H{H}",
         seed=8, dtype=dtype, H=H, D=128, B=16, NB=NB, sys_len=sys_len, conv_sys=conv_sys,
-        turn_len=turn_len, active=active, frame_order=order,
+        turn_len=turn_len, active=active, gen_len=gen_len, frame_order=order,
         description=f"{C} conversations over {P} system prompts U[{sys_min},{sys_max}], {R} rounds "
-                    f"of turns U[{turn_min},{turn_max}], whole-history prompts, H={H}, d=128, "
-                    f"B=16, {dtype}, permuted pool of {NB}",
+                    f"of turns U[{turn_min},{turn_max}] + generated U[{gen_min},{gen_max}], "
+                    f"whole-history prompts, H={H}, d=128, B=16, {dtype}, permuted pool of {NB}",
     )
 
 
