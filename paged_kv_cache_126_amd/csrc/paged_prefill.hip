@@ -215,6 +215,10 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int kPer = kBN * kPieces / (kWaves * 64);
   static_assert(kBN * kPieces % (kWaves * 64) == 0, "tile must split evenly over the threads");
   u32x4 pk[kPer], pv[kPer];
+  // Block sizes that are powers of two (the common case) split a token
+  // position into (block, offset) with a shift and a mask.
+  const bool pow2_block = (a.block_size & (a.block_size - 1)) == 0;
+  const int block_shift = __builtin_ctz(static_cast<unsigned>(a.block_size));
   auto fetch = [&](const int k0) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -223,12 +227,20 @@ void prefill_kernel(PrefillArgs a) {
       const int c = piece % kPieces;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (tok <= wg_last) {
-        const int blk = tok / a.block_size;
+        int blk, inb;
+        if (pow2_block) {
+          blk = tok >> block_shift;
+          inb = tok & (a.block_size - 1);
+        } else {
+          blk = tok / a.block_size;
+          inb = tok - blk * a.block_size;
+        }
         const uint32_t f = tbl_in_lds ? lds_tbl[blk]
                                       : min(static_cast<uint32_t>(table_row[blk]), max_frame);
-        const int64_t off = static_cast<int64_t>(f) * frame_bytes +
-                            static_cast<int64_t>(tok - blk * a.block_size) * row_bytes + head_bytes +
-                            16 * c;
+        // offset inside the frame fits 32 bits (frames are under 2^31 bytes)
+        const uint32_t in_frame = static_cast<uint32_t>(inb) * row_bytes +
+                                  static_cast<uint32_t>(head_bytes) + 16u * c;
+        const int64_t off = static_cast<int64_t>(f) * frame_bytes + in_frame;
         kv = load16(static_cast<const char*>(a.k_cache) + off);
         vv = load16(static_cast<const char*>(a.v_cache) + off);
       }
