@@ -380,6 +380,9 @@ def main():
     ap.add_argument("--block-size", type=int, default=0,
                     help="workloads 2 and 3: tokens per frame (default 16; the pool keeps its "
                          "slot count)")
+    ap.add_argument("--permuted-pool", action="store_true",
+                    help="workload 5: a seeded permuted frame pool instead of first in, first out "
+                         "in id order (the sensitivity variant)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -406,8 +409,13 @@ def main():
     if args.block_size and args.workload not in (2, 3):
         print("--block-size applies to workloads 2 and 3 only", file=sys.stderr)
         sys.exit(2)
+    if args.permuted_pool and args.workload != 5:
+        print("--permuted-pool applies to workload 5 only", file=sys.stderr)
+        sys.exit(2)
     if args.block_size:
         w = {2: configs.config2, 3: configs.config3}[args.workload](B=args.block_size)
+    elif args.permuted_pool:
+        w = configs.config5(permuted=True)
     else:
         w = configs.FULL[args.workload]()
     log(f"[bench] workload {w.name}: {w.description}")
@@ -552,6 +560,26 @@ def main():
         f"merge {merge_ms.mean() * 1e3:.1f} us"
         + (f", kv_append {append_ms.mean() * 1e3:.1f} us" if append_args else ""))
 
+    # Streaming-read ceiling: the same non-temporal 16-byte loads over a
+    # buffer of the step's K/V size, no arithmetic (pa_stream_read), cold.
+    ceil_buf = torch.ones(kv_bytes_unique // 2, dtype=torch.int16, device=dev)
+    ceil_sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        pkv.lib.stream_read(ceil_buf, ceil_sink)
+    cevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(20)]
+    for c0, c1 in cevs:
+        if not args.no_flush:
+            flush()
+        with pkv.kernel_timing(c0, c1):
+            pkv.lib.stream_read(ceil_buf, ceil_sink)
+    torch.cuda.synchronize()
+    ceil_us = float(np.mean([c0.elapsed_time(c1) for c0, c1 in cevs])) * 1e3
+    ceil_gbs = kv_bytes_unique / ceil_us / 1e3
+    del ceil_buf
+    log(f"[bench] streaming-read ceiling over {kv_bytes_unique / 1e9:.3f} GB: {ceil_us:.1f} us, "
+        f"{ceil_gbs:.0f} GB/s")
+
     # Copy-on-write frame copies (shared-prefix workload): the step's copies,
     # redirected to frames the schedule never uses so the cache stays intact.
     from paged_kv_cache_126_amd.driver import CopyBlocks
@@ -634,6 +662,10 @@ def main():
             "frac": round(part_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": kv_bytes_unique,
             "launch_us": round(float(kern_ms.mean()) * 1e3, 2),
+            "read_ceiling": {"GB/s": round(ceil_gbs, 1), "us": round(ceil_us, 2),
+                             "what": "pa_stream_read: the same non-temporal 16-byte loads over "
+                                     "as many bytes, in order, nothing else"},
+            "frac_of_read_ceiling": round(part_gbs / ceil_gbs, 4),
         },
         "kernel_source_digest": digest,
         "cow_frame_copies": cow,

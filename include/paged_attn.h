@@ -254,10 +254,23 @@ pa_status paged_gather(const void* cache, const int32_t* block_tables,
                        pa_dtype dtype, void* stream);
 
 /*
+ * pa_stream_read: benchmark support, not part of the attention path. Reads
+ * `bytes` bytes (a multiple of 16; buf 16-byte aligned, device memory) with
+ * the non-temporal 16-byte loads the decode kernel uses and no other work,
+ * so its bandwidth is the ceiling those loads can reach on the device.
+ * `sink` (device uint32) is written only in a practically impossible case;
+ * it keeps the loads from being optimised away. Stamps the launch events of
+ * pa_set_launch_events like the attention kernels. bytes == 0 queues
+ * nothing.
+ */
+pa_status pa_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+/*
  * pa_set_launch_events: kernel-accurate timing, for benchmarks and
  * profilers. While set on a thread, every launch that thread makes of the
- * decode partition kernel (paged_attn_decode, paged_attn_decode_partitions)
- * or of the prefill kernel (paged_attn_prefill) stamps `start` with the
+ * decode partition kernel (paged_attn_decode, paged_attn_decode_partitions),
+ * of the prefill kernel (paged_attn_prefill) or of pa_stream_read's kernel
+ * stamps `start` with the
  * kernel's own start time and `stop` with its end time (hipEvent_t handles
  * owned by the caller, created with timing enabled; either may be NULL).
  * An event plainly recorded on the stream around a launch also counts the

@@ -327,6 +327,13 @@ pa_status paged_gather(const void* cache, const int32_t* block_tables,
                                     static_cast<hipStream_t>(stream)));
 }
 
+pa_status pa_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0 || (bytes > 0 && (!buf || !sink))) return PA_EINVAL;
+  if (bytes == 0) return PA_OK;
+  if (!aligned(buf, 16)) return PA_EALIGN;
+  return from_hip(pa::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 pa_status pa_set_launch_events(void* start, void* stop) {
   pa::launch_events() = {static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)};
   return PA_OK;

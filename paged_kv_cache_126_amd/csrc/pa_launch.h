@@ -100,4 +100,7 @@ hipError_t launch_gather(const void* cache, const int32_t* block_tables,
                          int64_t num_blocks, int32_t max_blocks, int32_t max_ctx,
                          hipStream_t stream);
 
+// Streaming-read bandwidth probe (benchmark support).
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace pa

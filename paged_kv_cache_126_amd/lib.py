@@ -21,6 +21,7 @@ EXPORTS = (
     "pa_status_string", "pa_abi_version", "kv_append", "kv_copy_blocks", "paged_attn_workspace_size",
     "paged_attn_partition_tokens", "paged_attn_decode", "paged_attn_decode_partitions",
     "paged_attn_merge", "paged_attn_prefill", "paged_gather", "pa_set_launch_events",
+    "pa_stream_read",
 )
 
 
@@ -99,6 +100,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_gather.restype = ctypes.c_int
     lib.pa_set_launch_events.argtypes = [P, P]
     lib.pa_set_launch_events.restype = ctypes.c_int
+    lib.pa_stream_read.argtypes = [P, I64, P, P]
+    lib.pa_stream_read.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -288,3 +291,11 @@ class kernel_timing:
     def __exit__(self, *exc):
         load().pa_set_launch_events(None, None)
         return False
+
+
+def stream_read(buf, sink, stream=None) -> None:
+    """Streaming-read bandwidth probe over a dense device tensor ``buf``
+    (see pa_stream_read); ``sink`` is a device int32/uint32 scalar tensor."""
+    _dense(buf)
+    _check("pa_stream_read", load().pa_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
+                                                   _ptr(sink), _stream(stream)))

@@ -173,3 +173,11 @@ def test_prefill_pointer_errors():
     assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, None, None) == -1
     empty = prefill_shape(total_queries=0)
     assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, ctypes.byref(empty), None) == 0
+
+
+def test_stream_read_argument_errors():
+    lib = pkv.load()
+    assert lib.pa_stream_read(None, 0, None, None) == 0          # nothing to do
+    assert lib.pa_stream_read(None, 17, None, None) == -1        # not a multiple of 16
+    assert lib.pa_stream_read(None, 32, None, None) == -1        # null buffer
+    assert lib.pa_stream_read(ctypes.c_void_p(8), 32, ctypes.c_void_p(16), None) == -2  # misaligned

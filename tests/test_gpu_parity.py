@@ -478,3 +478,40 @@ def test_kernel_timing_events_leave_results_unchanged():
     inner = ev[1].elapsed_time(ev[2])
     say(f"  stream events {outer * 1e3:.1f} us, kernel stamps {inner * 1e3:.1f} us")
     assert 0 < inner <= outer
+
+
+@pytest.mark.parametrize("make", [
+    lambda: configs.config2(S=8, H=4, NB=2000, seed=101),
+    lambda: configs.config2(S=8, H=4, NB=2000, seed=102),
+    lambda: configs.config5(S=24, H=4, NB=4000, seed=101),
+    lambda: configs.config5(S=24, H=4, NB=4000, seed=102),
+    lambda: configs.config5(S=24, H=4, NB=4000, permuted=True),
+], ids=["cfg2_seed101", "cfg2_seed102", "cfg5_seed101", "cfg5_seed102", "cfg5_permuted"])
+def test_robustness_seeds_and_permuted_pool(make):
+    """The decode workloads under other seeds (structure and values) and the
+    batch-256 step on a permuted pool: element-wise against the oracle."""
+    w = make()
+    say(f"[gpu] {w.name}: {w.description}")
+    gpu = run_gpu(w)
+    ref = oracle_outputs(w, pad_frame_for(w))
+    for (pt, out), (snap, o) in zip(gpu, ref):
+        assert np.array_equal(pt.tables, snap.tables)
+        err = max_err(out.numpy(), o)
+        say(f"  max-abs err {err:.3e}")
+        assert err <= TOL[w.dtype]
+
+
+def test_stream_read_probe_runs_and_leaves_sink():
+    """The streaming-read probe reads the whole buffer without touching
+    anything else (its sink stays as it was for ordinary data)."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+
+    dev = torch.device("cuda:0")
+    for n in (16, 4096 * 16 + 48, 1 << 24):
+        buf = torch.ones(n // 2, dtype=torch.int16, device=dev)
+        sink = torch.full((1,), 7, dtype=torch.int32, device=dev)
+        pkv.lib.stream_read(buf, sink)
+        torch.cuda.synchronize()
+        assert int(sink.item()) == 7

@@ -101,21 +101,24 @@ def config1() -> Workload:
 
 
 def config2(S: int = 64, H: int = 32, NB: int | None = None, max_ctx: int = 2048,
-            B: int = 16) -> Workload:
+            B: int = 16, seed: int = 2) -> Workload:
     """Decode batch 64, bf16, ctx ~ U{1..2048}, permuted 20k-frame pool.
 
     Draw order: ``ctx = integers(1, max_ctx + 1, S)``, then ``permutation(NB)``.
     Another block size keeps the pool's slot count (NB = 20000 * 16 / B).
+    Another seed (structure and values) gives a robustness variant.
     """
     NB = NB if NB is not None else 20000 * 16 // B
-    rng = np.random.default_rng(2)
+    rng = np.random.default_rng(seed)
     ctx = rng.integers(1, max_ctx + 1, size=S)
     order = rng.permutation(NB)
     name = "cfg2_batch64_bf16" if (S, H) == (64, 32) else f"cfg2_S{S}_H{H}"
     if B != 16:
         name += f"_B{B}"
+    if seed != 2:
+        name += f"_seed{seed}"
     return Workload(
-        name=name, seed=2, dtype="bf16", H=H, D=128, B=B, NB=NB, num_seqs=S,
+        name=name, seed=seed, dtype="bf16", H=H, D=128, B=B, NB=NB, num_seqs=S,
         prefill=[(s, int(ctx[s])) for s in range(S)], frame_order=order,
         description=f"S={S}, H={H}, d=128, B={B}, bf16, ctx U[1,{max_ctx}], permuted pool of {NB}",
     )
@@ -173,22 +176,32 @@ def config4(prompts: int = 64, n: int = 4, prompt_len: int = 1000, H: int = 32,
     )
 
 
-def config5(S: int = 256, H: int = 64, NB: int = 32768, cap: int = 8192) -> Workload:
+def config5(S: int = 256, H: int = 64, NB: int = 32768, cap: int = 8192, seed: int = 5,
+            permuted: bool = False) -> Workload:
     """Large-model decode step: lognormal contexts, append then attend.
 
-    Draw order: ``z = standard_normal(S)``; ``ctx = clip(rint(exp(ln 1000 + 0.8 z)), 1, cap)``.
+    Draw order: ``z = standard_normal(S)``; ``ctx = clip(rint(exp(ln 1000 + 0.8 z)), 1, cap)``;
+    with ``permuted``, then ``permutation(NB)`` for the pool (the sensitivity
+    variant; the default pool is first in, first out in id order).
     ``ctx`` counts the token appended by the step, so the prefill is ctx - 1.
+    Another seed (structure and values) gives a robustness variant.
     """
-    rng = np.random.default_rng(5)
+    rng = np.random.default_rng(seed)
     z = rng.standard_normal(S)
     ctx = np.clip(np.rint(np.exp(np.log(1000.0) + 0.8 * z)), 1, cap).astype(np.int64)
+    order = rng.permutation(NB) if permuted else None
+    name = "cfg5_batch256_f16" if (S, H) == (256, 64) else f"cfg5_S{S}_H{H}"
+    if permuted:
+        name += "_permuted"
+    if seed != 5:
+        name += f"_seed{seed}"
     return Workload(
-        name="cfg5_batch256_f16" if (S, H) == (256, 64) else f"cfg5_S{S}_H{H}",
-        seed=5, dtype="f16", H=H, D=128, B=16, NB=NB, num_seqs=S,
+        name=name, seed=seed, dtype="f16", H=H, D=128, B=16, NB=NB, num_seqs=S,
         prefill=[(s, int(ctx[s]) - 1) for s in range(S)],
-        steps=[list(range(S))], attend_after=[0],
+        steps=[list(range(S))], attend_after=[0], frame_order=order,
         description=f"S={S}, H={H}, d=128, B=16, fp16, lognormal ctx (median 1000, sigma 0.8, "
-                    f"cap {cap}); append one token then attend; FIFO pool of {NB}",
+                    f"cap {cap}); append one token then attend; "
+                    f"{'permuted' if permuted else 'FIFO'} pool of {NB}",
     )
 
 
