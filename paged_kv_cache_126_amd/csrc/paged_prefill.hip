@@ -86,27 +86,26 @@ __device__ __forceinline__ u32x4 join(v4i16 a, v4i16 b) {
 template <typename T>
 struct Mfma;
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 template <>
 struct Mfma<BF16> {
   using vec = bf16x8;
+  using pair = __bf16 __attribute__((ext_vector_type(2)));  // two weights, rounded together
   static __device__ __forceinline__ f32x16 run(vec a, vec b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ vec from_bits(u32x4 v) { return __builtin_bit_cast(vec, v); }
-  // value rounded to the element type, and the element back in fp32
-  static __device__ __forceinline__ __bf16 narrow(float x) { return static_cast<__bf16>(x); }
-  static __device__ __forceinline__ float widen1(__bf16 x) { return static_cast<float>(x); }
 };
 
 template <>
 struct Mfma<F16> {
   using vec = f16x8;
+  using pair = _Float16 __attribute__((ext_vector_type(2)));
   static __device__ __forceinline__ f32x16 run(vec a, vec b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ vec from_bits(u32x4 v) { return __builtin_bit_cast(vec, v); }
-  static __device__ __forceinline__ _Float16 narrow(float x) { return static_cast<_Float16>(x); }
-  static __device__ __forceinline__ float widen1(_Float16 x) { return static_cast<float>(x); }
 };
 
 constexpr int kXcds = 8;  // accelerator complex dies of the MI355X
@@ -334,14 +333,21 @@ void prefill_kernel(PrefillArgs a) {
       for (int g = 0; g < 16; g += 8)
 #pragma unroll
         for (int i = 0; i < 4; ++i) swap_halves(x[g + i], x[g + i + 4]);
+      // P = hi + lo per pair of weights: hi rounded to the element type, lo
+      // the rounded residual (x - hi is exact in fp32)
       vec p_hi[2], p_lo[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const auto hi = M::narrow(x[8 * j + e]);
-          p_hi[j][e] = hi;
-          p_lo[j][e] = M::narrow(x[8 * j + e] - M::widen1(hi));
+        for (int e = 0; e < 8; e += 2) {
+          const f32x2 xv = {x[8 * j + e], x[8 * j + e + 1]};
+          const auto hp = __builtin_convertvector(xv, typename M::pair);
+          const f32x2 hw = __builtin_convertvector(hp, f32x2);
+          const auto lp = __builtin_convertvector(f32x2{xv.x - hw.x, xv.y - hw.y}, typename M::pair);
+          p_hi[j][e] = hp.x;
+          p_hi[j][e + 1] = hp.y;
+          p_lo[j][e] = lp.x;
+          p_lo[j][e + 1] = lp.y;
         }
       // O^T += V^T P^T. The V^T operand (8 consecutive keys per lane at one
       // head-dim element) comes from the row-major V tile through transposing
@@ -351,18 +357,22 @@ void prefill_kernel(PrefillArgs a) {
       // receives V[kb + j][d0 + l], j = 0..3; two reads cover 8 keys.
       const int grp16 = lane >> 4;
       const int c16 = lane & 15;
+      auto v_operand = [&](const int b, const int j) {
+        const int d0 = 32 * b + 16 * (grp16 & 1);
+        const int kb = 16 * j + 8 * (grp16 >> 1);
+        const v4i16 lo4 = tr_read(&lds_v[kb + (c16 >> 2)][d0 + 4 * (c16 & 3)]);
+        const v4i16 hi4 = tr_read(&lds_v[kb + 4 + (c16 >> 2)][d0 + 4 * (c16 & 3)]);
+        return M::from_bits(join(lo4, hi4));
+      };
+      // the next V operand is read while the current one's two MFMAs run
+      vec va_next = v_operand(0, 0);
 #pragma unroll
-      for (int b = 0; b < kDBlk; ++b) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int d0 = 32 * b + 16 * (grp16 & 1);
-          const int kb = 16 * j + 8 * (grp16 >> 1);
-          const v4i16 lo4 = tr_read(&lds_v[kb + (c16 >> 2)][d0 + 4 * (c16 & 3)]);
-          const v4i16 hi4 = tr_read(&lds_v[kb + 4 + (c16 >> 2)][d0 + 4 * (c16 & 3)]);
-          const vec va = M::from_bits(join(lo4, hi4));
-          o[b] = M::run(va, p_hi[j], o[b]);
-          o[b] = M::run(va, p_lo[j], o[b]);
-        }
+      for (int n = 0; n < 2 * kDBlk; ++n) {
+        const int b = n / 2, j = n % 2;
+        const vec va = va_next;
+        if (n + 1 < 2 * kDBlk) va_next = v_operand((n + 1) / 2, (n + 1) % 2);
+        o[b] = M::run(va, p_hi[j], o[b]);
+        o[b] = M::run(va, p_lo[j], o[b]);
       }
     }
     if (kt + 1 < n_tiles) stage((kt + 1) & 1);
