@@ -298,8 +298,19 @@ def bench_prefix(args, w, dev):
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        # pass 1: plain launches (step and phase times); pass 2: the prefill
-        # kernel stamping its own start and end (its duration)
+        # pass 0: the step time, events around the whole step only (events
+        # recorded between kernels cost stream time themselves)
+        sevs = []
+        for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if not args.no_flush:
+                torch.sum(flush_buf, dim=0, out=flush_sink)
+            e0.record()
+            step()
+            e1.record()
+            sevs.append((e0, e1))
+        # pass 1: events between the phases (the breakdown); pass 2: the
+        # prefill kernel stamping its own start and end (its duration)
         all_evs = []
         for stamp in (False, True):
             for _ in range(args.steps):
@@ -311,7 +322,7 @@ def bench_prefix(args, w, dev):
         torch.cuda.synchronize()
         kern_evs = [e for st, e in all_evs if st]
         all_evs = [e for st, e in all_evs if not st]
-        step_ms = float(np.mean([e[0][0].elapsed_time(e[-1][2]) for e in all_evs]))
+        step_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in sevs]))
         append_ms = float(np.mean([sum(r[0].elapsed_time(r[1]) for r in e) for e in all_evs]))
         prefill_ms = float(np.mean([sum(r[1].elapsed_time(r[2]) for r in e) for e in all_evs]))
         kernel_ms = float(np.mean([sum(r[3].elapsed_time(r[4]) for r in e) for e in kern_evs]))
@@ -384,6 +395,9 @@ def main():
                     help="workload 5: a seeded permuted frame pool instead of first in, first out "
                          "in id order (the sensitivity variant)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--ungrouped", action="store_true",
+                    help="time paged_attn_decode even where sequences share frames (by default "
+                         "forked sequences go through paged_attn_decode_grouped)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run one plain device-to-device copy of BYTES (a known-size "
@@ -480,7 +494,17 @@ def main():
     cl = torch.from_numpy(pt.context_lens).to(dev)
     out = torch.empty((w.num_seqs, w.H, w.D), dtype=torch.float32, device=dev)
     max_ctx = int(pt.context_lens.max())
-    policy = pt.cache_policy
+    policy = ungrouped_policy = pt.cache_policy
+    # Forks of one prompt share their leading frames: the grouped pass reads
+    # each shared row once for the whole group (so streaming loads suit it).
+    from paged_kv_cache_126_amd.driver import share_groups
+
+    group_start, group_shared = share_groups(pt.tables, pt.context_lens, w.B)
+    grouped = not args.ungrouped and bool((group_shared > 0).any())
+    groups = None
+    if grouped:
+        groups = (torch.from_numpy(group_start).to(dev), torch.from_numpy(group_shared).to(dev))
+        policy = pkv.lib.PA_CACHE_STREAM
     shape = pkv.lib.make_shape(q, cache.k, bt, max_ctx, pkv.lib.PA_F32, args.partition_tokens, policy)
     ws = pkv.alloc_workspace(shape, dev)
     part_tokens = pkv.partition_tokens(shape)
@@ -500,25 +524,40 @@ def main():
     def flush():
         torch.sum(flush_buf, dim=0, out=flush_sink)
 
-    def step(evs=None):
+    def attend(phase, pol):
+        if phase == "grouped":
+            pkv.paged_attn_decode_grouped(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx,
+                                          groups[0], groups[1], ws, args.partition_tokens,
+                                          cache_policy=pol)
+        else:
+            pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
+                                  args.partition_tokens, phase=phase, cache_policy=pol)
+
+    def step(evs=None, use_groups=grouped, phases=False):
+        """One step: [kv_append,] then the partition pass and the merge pass
+        (the grouped call queues both). evs[0] start, evs[2] end; with
+        `phases`, also evs[3] after the append and evs[1] after the
+        partition pass (after both for the grouped call); with six events,
+        evs[4], evs[5] the partition kernel's own start and end. Events
+        recorded between kernels cost stream time themselves, so the step
+        time comes from steps timed with the first two only."""
         if evs is not None:
             evs[0].record()
         if append_args is not None:
             cache.append(*append_args)
-            if evs is not None:
+            if phases:
                 evs[3].record()
+        first = "grouped" if use_groups else "partitions"
+        pol = policy if use_groups else ungrouped_policy
         if evs is not None and len(evs) > 4:
-            # evs[4], evs[5]: the partition kernel's own start and end
             with pkv.kernel_timing(evs[4], evs[5]):
-                pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
-                                      args.partition_tokens, phase="partitions", cache_policy=policy)
+                attend(first, pol)
         else:
-            pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
-                                  args.partition_tokens, phase="partitions", cache_policy=policy)
-        if evs is not None:
+            attend(first, pol)
+        if phases:
             evs[1].record()
-        pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, max_ctx, ws,
-                              args.partition_tokens, phase="merge", cache_policy=policy)
+        if not use_groups:
+            attend("merge", pol)
         if evs is not None:
             evs[2].record()
 
@@ -539,6 +578,13 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # Pass 1b (the breakdown): events between the phases as well.
+    pevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush()
+        step(pevs[i], phases=True)
+    torch.cuda.synchronize()
     # Pass 2 (the kernel's duration): the same steps with the partition
     # kernel stamping its own start and end. Kept apart because a stamped
     # launch adds dispatch work that the stream events of pass 1 would count.
@@ -548,16 +594,34 @@ def main():
             flush()
         step(kevs[i])
     torch.cuda.synchronize()
+    # Context for the grouped call: the same steps through paged_attn_decode.
+    ungrouped_ctx = None
+    if grouped:
+        uevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            if not args.no_flush:
+                flush()
+            step(uevs[i], use_groups=False)
+        torch.cuda.synchronize()
+        ums = float(np.mean([e[0].elapsed_time(e[2]) for e in uevs]))
+        ungrouped_ctx = {"us_per_step": round(ums * 1e3, 2),
+                         "GB/s": round(kv_bytes / (ums * 1e-3) / 1e9, 1),
+                         "cache_policy": "reuse" if ungrouped_policy else "stream",
+                         "what": "the same steps through paged_attn_decode (every sequence "
+                                 "reads its own rows; shared frames hit in cache)"}
+        log(f"[bench] ungrouped: step {ums * 1e3:.1f} us")
     part_start = 3 if append_args is not None else 0
-    append_ms = np.array([e[0].elapsed_time(e[3]) for e in evs]) if append_args else np.zeros(1)
-    part_ms = np.array([e[part_start].elapsed_time(e[1]) for e in evs])
+    append_ms = np.array([e[0].elapsed_time(e[3]) for e in pevs]) if append_args else np.zeros(1)
+    part_ms = np.array([e[part_start].elapsed_time(e[1]) for e in pevs])
     kern_ms = np.array([e[4].elapsed_time(e[5]) for e in kevs])  # kernel alone, no dispatch gap
-    merge_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    merge_ms = np.array([e[1].elapsed_time(e[2]) for e in pevs])
     step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
     ms = float(step_ms.mean())
     log(f"[bench] {args.steps} steps: step {ms * 1e3:.1f} us (median {np.median(step_ms) * 1e3:.1f}), "
-        f"partition kernel {part_ms.mean() * 1e3:.1f} us (kernel alone {kern_ms.mean() * 1e3:.1f}), "
-        f"merge {merge_ms.mean() * 1e3:.1f} us"
+        + (f"grouped call {part_ms.mean() * 1e3:.1f} us (grouped partition kernel alone "
+           f"{kern_ms.mean() * 1e3:.1f})" if grouped else
+           f"partition kernel {part_ms.mean() * 1e3:.1f} us (kernel alone {kern_ms.mean() * 1e3:.1f}), "
+           f"merge {merge_ms.mean() * 1e3:.1f} us")
         + (f", kv_append {append_ms.mean() * 1e3:.1f} us" if append_args else ""))
 
     # Streaming-read ceiling: the same non-temporal 16-byte loads over a
@@ -652,12 +716,22 @@ def main():
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "warm_us_per_step": round(warm_ms * 1e3, 2),
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "launch": ("paged_attn_decode_grouped (grouped partition pass + merge pass)" if grouped
+                   else "paged_attn_decode_partitions + paged_attn_merge"),
+        "groups": ({"count": int(len(group_shared)), "sequences_in_shared_groups":
+                    int(sum(b - a for a, b, sh in zip(group_start[:-1], group_start[1:], group_shared)
+                            if sh > 0)),
+                    "shared_tokens": sorted({int(x) for x in group_shared})[-4:]} if grouped else None),
+        "ungrouped": ungrouped_ctx,
         "kernels_us": {"partition": round(float(part_ms.mean()) * 1e3, 2),
                        "partition_kernel_alone": round(float(kern_ms.mean()) * 1e3, 2),
-                       "merge": round(float(merge_ms.mean()) * 1e3, 2),
-                       "kv_append": round(float(append_ms.mean()) * 1e3, 2) if append_args else None},
+                       "merge": None if grouped else round(float(merge_ms.mean()) * 1e3, 2),
+                       "kv_append": round(float(append_ms.mean()) * 1e3, 2) if append_args else None,
+                       "what": ("partition = the grouped call (both passes) between stream events; "
+                                "partition_kernel_alone = the grouped partition kernel's own stamps"
+                                if grouped else "between stream events; kernel alone = its own stamps")},
         "roofline": {
-            "kernel": "decode_partition_kernel", "bound": "hbm",
+            "kernel": "decode_group_kernel" if grouped else "decode_partition_kernel", "bound": "hbm",
             "achieved": round(part_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(part_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": kv_bytes_unique,

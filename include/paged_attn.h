@@ -198,6 +198,43 @@ pa_status paged_attn_decode_partitions(const void* q, const void* k_cache, const
 pa_status paged_attn_merge(const int32_t* context_lens, void* out, const pa_decode_shape* shape,
                            const void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Grouped decode: paged_attn_decode for batches in which groups of
+ * sequences share the first frames of their block tables (the branches of
+ * one prompt after forks: "PagedAttention: Virtual Memory Guide for LLM
+ * Inference", "2. Zero-Copy Branching via Copy-on-Write"). One workgroup
+ * serves a whole group: each shared K/V row is read from memory once and
+ * folded into every member's softmax; the members' own rows are read as
+ * usual. Same shape rules, partition size and workspace as
+ * paged_attn_decode, and the same outputs, bit for bit.
+ *
+ *   group_start   device int32 [num_groups + 1]: group g is the batch's
+ *                 sequences group_start[g] .. group_start[g + 1] - 1, at most
+ *                 4 of them (PA_MAX_GROUP). Groups should cover every
+ *                 sequence once: a sequence in no group gets no output, one
+ *                 in two groups is written twice, members past the 4th are
+ *                 ignored. Values are clamped into [0, S].
+ *   group_shared  device int32 [num_groups]: tokens the members share. The
+ *                 first ceil(group_shared[g] / B) entries of the members'
+ *                 block-table rows must be equal; the shared length is cut
+ *                 to the shortest member's context. If the rows differ
+ *                 there, the shared tokens are read through the first
+ *                 member's row (never outside the cache).
+ *   num_groups    0 .. 65535
+ *
+ * The call queues the grouped partition pass and the merge pass on
+ * `stream`. Errors: as paged_attn_decode;
+ * PA_EINVAL for a negative or too large num_groups or missing group arrays,
+ * PA_EALIGN for misaligned ones.
+ */
+#define PA_MAX_GROUP 4
+pa_status paged_attn_decode_grouped(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    int32_t block_size, float scale, void* out,
+                                    const pa_decode_shape* shape, const int32_t* group_start,
+                                    const int32_t* group_shared, int32_t num_groups,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Shapes and types of one prefill call. */
 typedef struct pa_prefill_shape {
   int32_t num_seqs;            /* S */
@@ -268,10 +305,10 @@ pa_status pa_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* s
 /*
  * pa_set_launch_events: kernel-accurate timing, for benchmarks and
  * profilers. While set on a thread, every launch that thread makes of the
- * decode partition kernel (paged_attn_decode, paged_attn_decode_partitions),
- * of the prefill kernel (paged_attn_prefill) or of pa_stream_read's kernel
- * stamps `start` with the
- * kernel's own start time and `stop` with its end time (hipEvent_t handles
+ * decode partition kernel (paged_attn_decode, paged_attn_decode_partitions;
+ * the grouped partition kernel of paged_attn_decode_grouped), of the prefill
+ * kernel (paged_attn_prefill) or of pa_stream_read's kernel stamps `start`
+ * with the kernel's own start time and `stop` with its end time (hipEvent_t handles
  * owned by the caller, created with timing enabled; either may be NULL).
  * An event plainly recorded on the stream around a launch also counts the
  * dispatch gap before the kernel starts; these do not. Other kernels are

@@ -28,6 +28,7 @@ constexpr int32_t kMinDefaultPartition = 512;
 constexpr int64_t kTargetWorkgroups = 8192;
 constexpr int64_t kMaxGridYZ = 65535;
 constexpr size_t kWorkspaceAlign = 256;
+static_assert(pa::kMaxGroup == PA_MAX_GROUP, "group size limit of the kernels and the header");
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -243,6 +244,30 @@ pa_status paged_attn_merge(const int32_t* context_lens, void* out, const pa_deco
   a.out_f32 = shape->out_dtype == PA_F32 ? 1 : 0;
   return from_hip(pa::launch_decode_merge(a, to_internal(shape->kv_dtype), shape->head_dim,
                                           static_cast<hipStream_t>(stream)));
+}
+
+pa_status paged_attn_decode_grouped(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    int32_t block_size, float scale, void* out,
+                                    const pa_decode_shape* shape, const int32_t* group_start,
+                                    const int32_t* group_shared, int32_t num_groups,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_groups < 0 || num_groups > kMaxGridYZ) return PA_EINVAL;
+  pa::DecodeArgs a;
+  pa_status st = prepare_decode(q, k_cache, v_cache, block_tables, context_lens, block_size,
+                                scale, out, shape, workspace, workspace_bytes, &a);
+  if (st != PA_OK) return st;
+  if (shape->num_seqs == 0 || num_groups == 0) return PA_OK;
+  if (!group_start || !group_shared) return PA_EINVAL;
+  if (!aligned(group_start, 4) || !aligned(group_shared, 4)) return PA_EALIGN;
+  pa::GroupArgs g;
+  g.group_start = group_start;
+  g.group_shared = group_shared;
+  g.num_groups = num_groups;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = from_hip(pa::launch_decode_groups(a, &g, to_internal(shape->kv_dtype), shape->head_dim, s));
+  if (st != PA_OK) return st;
+  return paged_attn_merge(context_lens, out, shape, workspace, workspace_bytes, stream);
 }
 
 pa_status paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,

@@ -51,6 +51,17 @@ struct DecodeArgs {
   int32_t stream_loads;  // 1: non-temporal K/V loads; 0: ordinary cached loads
 };
 
+// Groups of consecutive sequences whose block tables agree on a leading
+// run of tokens (forks of one prompt): group g is sequences
+// group_start[g] .. group_start[g + 1] - 1 (at most kMaxGroup of them), and
+// their tables agree on the first group_shared[g] tokens.
+constexpr int kMaxGroup = 4;
+struct GroupArgs {
+  const int32_t* group_start;   // [num_groups + 1]
+  const int32_t* group_shared;  // [num_groups], tokens
+  int32_t num_groups;
+};
+
 enum class Dtype : int { F32 = 0, F16 = 1, BF16 = 2 };
 
 // Arguments of the causal multi-query (prefill) kernel.
@@ -85,6 +96,10 @@ int chunk_tokens(Dtype dt, int head_dim);
 hipError_t launch_decode_partitions(const DecodeArgs& a, Dtype dt, int head_dim,
                                     hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, Dtype dt, int head_dim, hipStream_t stream);
+// The partition pass over groups of sequences (g != nullptr), or the
+// ungrouped pass (g == nullptr).
+hipError_t launch_decode_groups(const DecodeArgs& a, const GroupArgs* g, Dtype dt, int head_dim,
+                                hipStream_t stream);
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, const int64_t* slots,
                             void* k_cache, void* v_cache, int64_t num_tokens, int64_t row_bytes,

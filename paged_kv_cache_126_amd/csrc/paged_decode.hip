@@ -32,6 +32,11 @@
 #include "pa_device.h"
 #include "pa_launch.h"
 
+// No multiply-add contraction beyond the fmaf calls written out: the
+// grouped and ungrouped passes inline the same helpers into different code,
+// and their results must agree bit for bit.
+#pragma clang fp contract(off)
+
 namespace pa {
 namespace {
 
@@ -56,67 +61,54 @@ struct Tiling {
   static_assert(kLPR >= 1 && kLPR <= 64 && (64 % kLPR) == 0, "row must tile a wavefront");
 };
 
-// kStream selects non-temporal K/V loads (frames read once) or ordinary
-// cached loads (frames shared by several sequences of the call).
+// Per-lane constants of the chunk loads of one (sequence, head).
 template <typename T, int D, int BT, bool kStream>
-__global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(DecodeArgs a) {
+struct ChunkLoader {
   using Tl = Tiling<T, D>;
-  constexpr int VEC = Tl::kVEC, LPR = Tl::kLPR, RPL = Tl::kRPL, CH = Tl::kCH;
+  static constexpr int VEC = Tl::kVEC, LPR = Tl::kLPR, RPL = Tl::kRPL, CH = Tl::kCH;
   // Uniform translation: with a compile-time block size that is a multiple
   // of the rows per load, the kRPL rows of one load share a frame, so the
   // frame is read once per load as a scalar.
-  constexpr bool kUniformFrame = BT > 0 && (BT % RPL) == 0;
+  static constexpr bool kUniformFrame = BT > 0 && (BT % RPL) == 0;
 
-  const int h = blockIdx.x;
-  const int part = blockIdx.y;
-  const int s = blockIdx.z;
-  int ctx = a.context_lens[s];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-  const int n_parts = ctx <= a.part_tokens ? 1 : (ctx + a.part_tokens - 1) / a.part_tokens;
-  if (part >= n_parts) return;  // uniform over the workgroup
-  const int tok_begin = part * a.part_tokens;
-  const int tok_end = min(ctx, tok_begin + a.part_tokens);
-
-  // readfirstlane tells the compiler the wavefront index is uniform, so the
-  // chunk loop, block-table reads and frame arithmetic stay scalar.
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int grp = lane / LPR;  // which of the kRPL rows of a load this lane holds
-  const int col = lane % LPR;  // which 16-byte piece of that row
-
-  const int32_t* table_row = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
+  const char* kbase;
+  const char* vbase;
   // Byte strides of the [NB, B, H, D] caches: one token row (all heads) and
   // one frame. The host guarantees frame_bytes < 2^31, so offsets inside a
   // frame fit 32 bits; frame bases are 64-bit scalars.
-  const uint32_t row_bytes = static_cast<uint32_t>(a.num_heads) * D * T::kBytes;
-  const int64_t frame_bytes = static_cast<int64_t>(row_bytes) * a.block_size;
-  const uint32_t lane_bytes = (static_cast<uint32_t>(h) * D + col * VEC) * T::kBytes;
-  const char* kbase = static_cast<const char*>(a.k_cache);
-  const char* vbase = static_cast<const char*>(a.v_cache);
-  const uint32_t max_frame = static_cast<uint32_t>(a.num_blocks - 1);  // num_blocks <= 2^31
+  uint32_t row_bytes;
+  int64_t frame_bytes;
+  uint32_t lane_bytes;  // this lane's 16 bytes inside a token row
+  uint32_t max_frame;   // num_blocks - 1 (num_blocks <= 2^31)
+  int32_t block_size;
+  int64_t num_blocks;
+  int grp;              // which of the kRPL rows of a load this lane holds
 
-  const u32x4 qv = load16(static_cast<const char*>(a.q) +
-                          ((static_cast<int64_t>(s) * a.num_heads + h) * D + col * VEC) * T::kBytes);
+  __device__ __forceinline__ ChunkLoader(const DecodeArgs& a, const int h, const int lane) {
+    kbase = static_cast<const char*>(a.k_cache);
+    vbase = static_cast<const char*>(a.v_cache);
+    row_bytes = static_cast<uint32_t>(a.num_heads) * D * T::kBytes;
+    frame_bytes = static_cast<int64_t>(row_bytes) * a.block_size;
+    grp = lane / LPR;
+    lane_bytes = (static_cast<uint32_t>(h) * D + (lane % LPR) * VEC) * T::kBytes;
+    max_frame = static_cast<uint32_t>(a.num_blocks - 1);
+    block_size = a.block_size;
+    num_blocks = a.num_blocks;
+  }
 
-  float m = kNegBig;
-  float l = 0.f;
-  float acc[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) acc[j] = 0.f;
-
-  // One chunk: kU row loads of K and of V per lane, then the online-softmax
-  // update. kMasked is false for chunks wholly inside the context, which
-  // then load without any per-lane condition.
-  auto attend_chunk = [&](const int t0, auto masked) {
-    constexpr bool kMasked = decltype(masked)::value;
-    u32x4 kv[kU], vv[kU];
-    bool valid[kU];
+  // The chunk of CH tokens starting at t0 (tokens of a sequence whose block
+  // table row is table_row): kU row loads of K and of V per lane. kMasked is
+  // false for chunks wholly inside [t0, tok_end), which then load without
+  // any per-lane condition; masked rows load nothing and are marked invalid.
+  template <bool kMasked>
+  __device__ __forceinline__ void load(const int32_t* table_row, const int t0, const int tok_end,
+                                       u32x4 (&kv)[kU], u32x4 (&vv)[kU], bool (&valid)[kU]) const {
 #pragma unroll
     for (int u = 0; u < kU; ++u) valid[u] = !kMasked || (t0 + u * RPL + grp < tok_end);
     if constexpr (kUniformFrame) {
       // All block-table reads of the chunk first (scalar loads). A load
-      // wholly past ctx reads the last valid table entry instead (its rows
-      // are masked), so table columns past ceil(ctx / B) are never read.
+      // wholly past tok_end reads the last valid table entry instead (its
+      // rows are masked), so table columns past ceil(ctx / B) are never read.
       uint32_t frame[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -149,7 +141,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(DecodeArgs a
         u32x4 kz = {0u, 0u, 0u, 0u}, vz = {0u, 0u, 0u, 0u};
         if (valid[u]) {
           const int64_t off =
-              token_row(table_row, t0 + u * RPL + grp, a.block_size, a.num_blocks) * row_bytes +
+              token_row(table_row, t0 + u * RPL + grp, block_size, num_blocks) * row_bytes +
               lane_bytes;
           kz = load_row<kStream>(kbase + off);
           vz = load_row<kStream>(vbase + off);
@@ -158,13 +150,36 @@ __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(DecodeArgs a
         vv[u] = vz;
       }
     }
+  }
+};
 
+// Online-softmax state of one query in one lane group: running maximum m
+// (log2 units), running sum l and the lane's kVEC accumulator elements.
+template <typename T, int D>
+struct SoftmaxState {
+  static constexpr int VEC = Tiling<T, D>::kVEC;
+  float m, l;
+  float acc[VEC];
+
+  __device__ __forceinline__ void reset() {
+    m = kNegBig;
+    l = 0.f;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) acc[j] = 0.f;
+  }
+
+  // Fold one loaded chunk into the state: scores q . k (DPP sums inside each
+  // lane group), scaled into log2 units; rows marked invalid weigh exactly 0.
+  __device__ __forceinline__ void update(const u32x4 qv, const float scale_log2,
+                                         const u32x4 (&kv)[kU], const u32x4 (&vv)[kU],
+                                         const bool (&valid)[kU]) {
+    constexpr int LPR = Tiling<T, D>::kLPR;
     float sc[kU];
     float cmax = kNegBig;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const float d = group_sum<LPR>(dot16(T{}, qv, kv[u]));
-      sc[u] = valid[u] ? d * a.scale_log2 : -__builtin_inff();
+      sc[u] = valid[u] ? d * scale_log2 : -__builtin_inff();
       cmax = fmaxf(cmax, sc[u]);
     }
     const float m_new = fmaxf(m, cmax);
@@ -182,17 +197,34 @@ __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(DecodeArgs a
       for (int j = 0; j < VEC; ++j) acc[j] = __builtin_fmaf(p, vf[j], acc[j]);
     }
     m = m_new;
-  };
-
-  const int n_chunks = (tok_end - tok_begin + CH - 1) / CH;
-  for (int chunk = wave; chunk < n_chunks; chunk += kNW) {
-    const int t0 = tok_begin + chunk * CH;
-    if (t0 + CH <= tok_end)
-      attend_chunk(t0, std::false_type{});
-    else
-      attend_chunk(t0, std::true_type{});
   }
+};
 
+// LDS of the wavefront combine.
+template <int D>
+struct CombineLds {
+  float m[kNW];
+  float l[kNW];
+  float acc[kNW][D];
+};
+
+// Combine a (sequence, head, partition)'s states of all lane groups and
+// wavefronts (log-sum-exp rule) and store the result: the normalised output
+// when the sequence has one partition, else the partition's partial (max,
+// sum, unnormalised output) in the workspace. Every thread of the workgroup
+// calls it; it synchronises the workgroup and leaves `lds` free for reuse
+// after a further barrier.
+template <typename T, int D>
+__device__ __forceinline__ void finish_partition(const DecodeArgs& a, const int s, const int h,
+                                                 const int part, const int n_parts,
+                                                 SoftmaxState<T, D> st, CombineLds<D>& lds) {
+  using Tl = Tiling<T, D>;
+  constexpr int VEC = Tl::kVEC, LPR = Tl::kLPR;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int grp = lane / LPR;
+  const int col = lane % LPR;
+  float m = st.m, l = st.l;
   // Combine the kRPL lane groups of the wavefront (lanes col, col + LPR, ...).
 #pragma unroll
   for (int x = LPR; x < 64; x <<= 1) {
@@ -201,41 +233,39 @@ __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(DecodeArgs a
     const float m_n = fmaxf(m, m_o);
     const float fa = fast_exp2(m - m_n);
     const float fb = fast_exp2(m_o - m_n);
-    l = l * fa + l_o * fb;
+    l = __builtin_fmaf(l, fa, l_o * fb);
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) acc[j] = acc[j] * fa + __shfl_xor(acc[j], x) * fb;
+    for (int j = 0; j < VEC; ++j)
+      st.acc[j] = __builtin_fmaf(st.acc[j], fa, __shfl_xor(st.acc[j], x) * fb);
     m = m_n;
   }
 
   // Combine the wavefronts through LDS.
-  __shared__ float s_m[kNW];
-  __shared__ float s_l[kNW];
-  __shared__ float s_acc[kNW][D];
   if (grp == 0) {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) s_acc[wave][col * VEC + j] = acc[j];
+    for (int j = 0; j < VEC; ++j) lds.acc[wave][col * VEC + j] = st.acc[j];
     if (col == 0) {
-      s_m[wave] = m;
-      s_l[wave] = l;
+      lds.m[wave] = m;
+      lds.l[wave] = l;
     }
   }
   __syncthreads();
 
   float M = kNegBig;
 #pragma unroll
-  for (int w = 0; w < kNW; ++w) M = fmaxf(M, s_m[w]);
+  for (int w = 0; w < kNW; ++w) M = fmaxf(M, lds.m[w]);
   float fw[kNW];
   float L = 0.f;
 #pragma unroll
   for (int w = 0; w < kNW; ++w) {
-    fw[w] = fast_exp2(s_m[w] - M);
-    L += s_l[w] * fw[w];
+    fw[w] = fast_exp2(lds.m[w] - M);
+    L = __builtin_fmaf(lds.l[w], fw[w], L);
   }
   const int64_t sh = static_cast<int64_t>(s) * a.num_heads + h;
   for (int e = threadIdx.x; e < D; e += kNW * 64) {
     float O = 0.f;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) O += s_acc[w][e] * fw[w];
+    for (int w = 0; w < kNW; ++w) O = __builtin_fmaf(lds.acc[w][e], fw[w], O);
     if (n_parts == 1) {
       const float r = L > 0.f ? O / L : 0.f;
       const int64_t o = sh * D + e;
@@ -254,6 +284,164 @@ __global__ __launch_bounds__(kNW * 64) void decode_partition_kernel(DecodeArgs a
         a.ws_ml[2 * p] = M;
         a.ws_ml[2 * p + 1] = L;
       }
+    }
+  }
+}
+
+__device__ __forceinline__ int clamp_ctx(const DecodeArgs& a, const int s) {
+  const int ctx = a.context_lens[s];
+  return ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
+}
+
+__device__ __forceinline__ int parts_of(const DecodeArgs& a, const int ctx) {
+  return ctx <= a.part_tokens ? 1 : (ctx + a.part_tokens - 1) / a.part_tokens;
+}
+
+// kStream selects non-temporal K/V loads (frames read once) or ordinary
+// cached loads (frames shared by several sequences of the call).
+// Eight wavefronts per SIMD (at most 64 registers per lane): the kernel is
+// bound by memory latency, so it keeps the most loads in flight.
+template <typename T, int D, int BT, bool kStream>
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(8)))
+void decode_partition_kernel(DecodeArgs a) {
+  using Ld = ChunkLoader<T, D, BT, kStream>;
+  constexpr int VEC = Ld::VEC, LPR = Ld::LPR, CH = Ld::CH;
+
+  const int h = blockIdx.x;
+  const int part = blockIdx.y;
+  const int s = blockIdx.z;
+  const int ctx = clamp_ctx(a, s);
+  const int n_parts = parts_of(a, ctx);
+  if (part >= n_parts) return;  // uniform over the workgroup
+  const int tok_begin = part * a.part_tokens;
+  const int tok_end = min(ctx, tok_begin + a.part_tokens);
+
+  // readfirstlane tells the compiler the wavefront index is uniform, so the
+  // chunk loop, block-table reads and frame arithmetic stay scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const Ld ld(a, h, lane);
+  const int32_t* table_row = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
+  const u32x4 qv = load16(static_cast<const char*>(a.q) +
+                          ((static_cast<int64_t>(s) * a.num_heads + h) * D + (lane % LPR) * VEC) *
+                              T::kBytes);
+
+  SoftmaxState<T, D> st;
+  st.reset();
+  const int n_chunks = (tok_end - tok_begin + CH - 1) / CH;
+  for (int chunk = wave; chunk < n_chunks; chunk += kNW) {
+    const int t0 = tok_begin + chunk * CH;
+    u32x4 kv[kU], vv[kU];
+    bool valid[kU];
+    if (t0 + CH <= tok_end) {
+      ld.template load<false>(table_row, t0, tok_end, kv, vv, valid);
+    } else {
+      ld.template load<true>(table_row, t0, tok_end, kv, vv, valid);
+    }
+    st.update(qv, a.scale_log2, kv, vv, valid);
+  }
+
+  __shared__ CombineLds<D> lds;
+  finish_partition<T, D>(a, s, h, part, n_parts, st, lds);
+}
+
+// Grouped partition pass: a workgroup serves a group of up to G sequences
+// (batch indices group_start[g] .. group_start[g + 1] - 1) whose block
+// tables agree on the first group_shared[g] tokens. Partition p covers the
+// same tokens [p * P, (p + 1) * P) as in the ungrouped pass. Chunks below
+// the shared length are loaded once and folded into every member's state;
+// the remaining chunks are each member's own. Chunk boundaries and the
+// chunk-to-wavefront assignment are those of the ungrouped pass (the shared
+// length is rounded down to a whole chunk), so every member's result equals
+// the ungrouped pass's bit for bit.
+template <typename T, int D, int BT, bool kStream, int G>
+__global__ __launch_bounds__(kNW * 64) void decode_group_kernel(DecodeArgs a, GroupArgs g) {
+  using Ld = ChunkLoader<T, D, BT, kStream>;
+  constexpr int VEC = Ld::VEC, LPR = Ld::LPR, CH = Ld::CH;
+
+  const int h = blockIdx.x;
+  const int part = blockIdx.y;
+  const int gi = blockIdx.z;
+  const int s0 = min(max(g.group_start[gi], 0), a.num_seqs);
+  const int ns = min(max(g.group_start[gi + 1], s0), a.num_seqs) - s0;  // members (<= G)
+  const int members = min(ns, G);
+  int ctx[G];
+  int max_ctx = 0, min_ctx = a.max_ctx;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    ctx[i] = i < members ? clamp_ctx(a, s0 + i) : 0;
+    if (i < members) {
+      max_ctx = max(max_ctx, ctx[i]);
+      min_ctx = min(min_ctx, ctx[i]);
+    }
+  }
+  if (members == 0 || part >= parts_of(a, max_ctx)) return;  // uniform over the workgroup
+  const int tok_begin = part * a.part_tokens;
+  // shared tokens: at most every member's context, whole chunks only
+  int shared = min(g.group_shared[gi], min_ctx);
+  shared = shared < 0 ? 0 : shared / CH * CH;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const Ld ld(a, h, lane);
+
+  u32x4 qv[G];
+  SoftmaxState<T, D> st[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    st[i].reset();
+    qv[i] = u32x4{0u, 0u, 0u, 0u};
+    if (i < members)
+      qv[i] = load16(static_cast<const char*>(a.q) +
+                     ((static_cast<int64_t>(s0 + i) * a.num_heads + h) * D + (lane % LPR) * VEC) *
+                         T::kBytes);
+  }
+
+  // Shared chunks: [tok_begin, sh_end), every one whole and inside every
+  // member's context; the first member's table row addresses them.
+  const int sh_end = min(shared, tok_begin + a.part_tokens);
+  const int n_shared = sh_end > tok_begin ? (sh_end - tok_begin) / CH : 0;
+  const int32_t* row0 = a.block_tables + static_cast<int64_t>(s0) * a.max_blocks;
+  for (int chunk = wave; chunk < n_shared; chunk += kNW) {
+    const int t0 = tok_begin + chunk * CH;
+    u32x4 kv[kU], vv[kU];
+    bool valid[kU];
+    ld.template load<false>(row0, t0, sh_end, kv, vv, valid);
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (i < members) st[i].update(qv[i], a.scale_log2, kv, vv, valid);
+  }
+
+  // Each member's own chunks, numbered on from the shared ones so that
+  // wavefront w keeps every chunk c with c % kNW == w.
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    if (i >= members) break;
+    const int tok_end = min(ctx[i], tok_begin + a.part_tokens);
+    const int n_chunks = tok_end > tok_begin ? (tok_end - tok_begin + CH - 1) / CH : 0;
+    const int32_t* row = a.block_tables + static_cast<int64_t>(s0 + i) * a.max_blocks;
+    int chunk = n_shared + ((wave - n_shared) % kNW + kNW) % kNW;
+    for (; chunk < n_chunks; chunk += kNW) {
+      const int t0 = tok_begin + chunk * CH;
+      u32x4 kv[kU], vv[kU];
+      bool valid[kU];
+      if (t0 + CH <= tok_end) {
+        ld.template load<false>(row, t0, tok_end, kv, vv, valid);
+      } else {
+        ld.template load<true>(row, t0, tok_end, kv, vv, valid);
+      }
+      st[i].update(qv[i], a.scale_log2, kv, vv, valid);
+    }
+  }
+
+  __shared__ CombineLds<D> lds;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    if (i >= members) break;
+    const int n_parts = parts_of(a, ctx[i]);
+    if (part < n_parts) {  // uniform: the member has tokens in this partition
+      finish_partition<T, D>(a, s0 + i, h, part, n_parts, st[i], lds);
+      __syncthreads();  // lds is reused by the next member
     }
   }
 }
@@ -294,46 +482,55 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   }
 }
 
+// Ungrouped (g == nullptr) or grouped partition pass.
 template <typename T, int D, int BT>
-hipError_t launch_part(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.num_heads, a.max_parts, a.num_seqs);
+hipError_t launch_part(const DecodeArgs& a, const GroupArgs* g, hipStream_t stream) {
+  const dim3 block(kNW * 64);
+  if (g != nullptr) {
+    const dim3 grid(a.num_heads, a.max_parts, g->num_groups);
+    if (a.stream_loads)
+      return launch_timed(decode_group_kernel<T, D, BT, true, kMaxGroup>, grid, block, stream, a, *g);
+    return launch_timed(decode_group_kernel<T, D, BT, false, kMaxGroup>, grid, block, stream, a, *g);
+  }
+  const dim3 grid(a.num_heads, a.max_parts, a.num_seqs);
   if (a.stream_loads)
-    return launch_timed(decode_partition_kernel<T, D, BT, true>, grid, dim3(kNW * 64), stream, a);
-  return launch_timed(decode_partition_kernel<T, D, BT, false>, grid, dim3(kNW * 64), stream, a);
+    return launch_timed(decode_partition_kernel<T, D, BT, true>, grid, block, stream, a);
+  return launch_timed(decode_partition_kernel<T, D, BT, false>, grid, block, stream, a);
 }
 
 // Block sizes with a uniform-frame specialisation; other sizes take the
 // per-lane translation path (BT = 0).
 template <typename T, int D>
-hipError_t dispatch_block(const DecodeArgs& a, hipStream_t stream) {
+hipError_t dispatch_block(const DecodeArgs& a, const GroupArgs* g, hipStream_t stream) {
   constexpr int RPL = Tiling<T, D>::kRPL;
   switch (a.block_size) {
     case 8:
-      if constexpr (8 % RPL == 0) return launch_part<T, D, 8>(a, stream);
+      if constexpr (8 % RPL == 0) return launch_part<T, D, 8>(a, g, stream);
       break;
     case 16:
-      if constexpr (16 % RPL == 0) return launch_part<T, D, 16>(a, stream);
+      if constexpr (16 % RPL == 0) return launch_part<T, D, 16>(a, g, stream);
       break;
     case 32:
-      if constexpr (32 % RPL == 0) return launch_part<T, D, 32>(a, stream);
+      if constexpr (32 % RPL == 0) return launch_part<T, D, 32>(a, g, stream);
       break;
     case 64:
-      if constexpr (64 % RPL == 0) return launch_part<T, D, 64>(a, stream);
+      if constexpr (64 % RPL == 0) return launch_part<T, D, 64>(a, g, stream);
       break;
     default:
       break;
   }
-  return launch_part<T, D, 0>(a, stream);
+  return launch_part<T, D, 0>(a, g, stream);
 }
 
 template <typename T>
-hipError_t dispatch_dim(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+hipError_t dispatch_dim(const DecodeArgs& a, const GroupArgs* g, int head_dim,
+                        hipStream_t stream) {
   switch (head_dim) {
-    case 16: return dispatch_block<T, 16>(a, stream);
-    case 32: return dispatch_block<T, 32>(a, stream);
-    case 64: return dispatch_block<T, 64>(a, stream);
-    case 128: return dispatch_block<T, 128>(a, stream);
-    case 256: return dispatch_block<T, 256>(a, stream);
+    case 16: return dispatch_block<T, 16>(a, g, stream);
+    case 32: return dispatch_block<T, 32>(a, g, stream);
+    case 64: return dispatch_block<T, 64>(a, g, stream);
+    case 128: return dispatch_block<T, 128>(a, g, stream);
+    case 256: return dispatch_block<T, 256>(a, g, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -370,10 +567,15 @@ int chunk_tokens(Dtype dt, int head_dim) {
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, Dtype dt, int head_dim,
                                     hipStream_t stream) {
+  return launch_decode_groups(a, nullptr, dt, head_dim, stream);
+}
+
+hipError_t launch_decode_groups(const DecodeArgs& a, const GroupArgs* g, Dtype dt, int head_dim,
+                                hipStream_t stream) {
   switch (dt) {
-    case Dtype::F32: return dispatch_dim<F32>(a, head_dim, stream);
-    case Dtype::F16: return dispatch_dim<F16>(a, head_dim, stream);
-    case Dtype::BF16: return dispatch_dim<BF16>(a, head_dim, stream);
+    case Dtype::F32: return dispatch_dim<F32>(a, g, head_dim, stream);
+    case Dtype::F16: return dispatch_dim<F16>(a, g, head_dim, stream);
+    case Dtype::BF16: return dispatch_dim<BF16>(a, g, head_dim, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -125,6 +125,46 @@ def plan(schedule, pad: int = -1, max_blocks: int | None = None, native: bool = 
     return events, mgr
 
 
+def share_groups(tables: np.ndarray, context_lens: np.ndarray, block_size: int,
+                 max_group: int = 4, min_shared: int = 1):
+    """Groups of consecutive sequences whose block-table rows start with the
+    same frames (forks of one prompt), for ``paged_attn_decode_grouped``.
+
+    Greedy over the batch order: a group starts at sequence i and takes the
+    following sequences while they share at least ``min_shared`` leading
+    frames with sequence i, up to ``max_group`` members. A group's shared
+    length is the run of leading frames common to all its members, in
+    tokens, cut to its shortest member's context. Sequences sharing nothing
+    with their neighbours form groups of one with no shared tokens. Returns
+    int32 ``group_start`` [G + 1] and ``group_shared`` [G].
+    """
+    tables = np.asarray(tables)
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    S = len(ctx)
+    nblk = -(-ctx // block_size)  # table entries in use
+
+    def common(i, j):
+        n = int(min(nblk[i], nblk[j]))
+        neq = np.flatnonzero(tables[i, :n] != tables[j, :n])
+        return n if len(neq) == 0 else int(neq[0])
+
+    starts, shared = [0], []
+    i = 0
+    while i < S:
+        j, run = i + 1, int(nblk[i])
+        while j < S and j - i < max_group:
+            c = common(i, j)
+            if c < min_shared:
+                break
+            run = min(run, c)
+            j += 1
+        members = ctx[i:j]
+        shared.append(0 if j - i == 1 else int(min(run * block_size, members.min())))
+        starts.append(j)
+        i = j
+    return np.asarray(starts, dtype=np.int32), np.asarray(shared, dtype=np.int32)
+
+
 class DeviceCache:
     """K and V caches [NB, B, H, D] in device memory, optionally NaN-filled."""
 

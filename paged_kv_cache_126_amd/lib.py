@@ -21,8 +21,9 @@ EXPORTS = (
     "pa_status_string", "pa_abi_version", "kv_append", "kv_copy_blocks", "paged_attn_workspace_size",
     "paged_attn_partition_tokens", "paged_attn_decode", "paged_attn_decode_partitions",
     "paged_attn_merge", "paged_attn_prefill", "paged_gather", "pa_set_launch_events",
-    "pa_stream_read",
+    "pa_stream_read", "paged_attn_decode_grouped",
 )
+PA_MAX_GROUP = 4
 
 
 class PagedAttnError(RuntimeError):
@@ -92,6 +93,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("paged_attn_decode", "paged_attn_decode_partitions"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = ctypes.c_int
+    lib.paged_attn_decode_grouped.argtypes = [P, P, P, P, P, I32, F, P, SH, P, P, I32, P, SZ, P]
+    lib.paged_attn_decode_grouped.restype = ctypes.c_int
     lib.paged_attn_merge.argtypes = [P, P, SH, P, SZ, P]
     lib.paged_attn_merge.restype = ctypes.c_int
     lib.paged_attn_prefill.argtypes = [P, P, P, P, P, P, I32, F, P, ctypes.POINTER(PrefillShape), P]
@@ -231,6 +234,30 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_siz
     _check(fn, getattr(lib, fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                 _ptr(context_lens), int(block_size), float(scale), _ptr(out),
                                 ctypes.byref(shape), _ptr(workspace), ws_bytes, st))
+
+
+def paged_attn_decode_grouped(q, k_cache, v_cache, block_tables, context_lens, block_size: int,
+                              scale: float, out, max_context_len: int, group_start, group_shared,
+                              workspace=None, partition_tokens: int = 0, stream=None,
+                              cache_policy: int = PA_CACHE_STREAM) -> None:
+    """Decode attention with groups of sequences that share leading frames
+    (int32 device ``group_start`` [G + 1], ``group_shared`` [G] tokens); see
+    include/paged_attn.h. ``workspace`` is sized as for ``paged_attn_decode``."""
+    _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out)
+    _dense(group_start, group_shared)
+    G = group_shared.numel()
+    if group_start.numel() != G + 1:
+        raise ValueError("group_start must have one more entry than group_shared")
+    if str(group_start.dtype) != "torch.int32" or str(group_shared.dtype) != "torch.int32":
+        raise TypeError("group arrays must be int32")
+    shape = make_shape(q, k_cache, block_tables, max_context_len, dtype_code(out), partition_tokens,
+                       cache_policy)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("paged_attn_decode_grouped",
+           load().paged_attn_decode_grouped(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                            _ptr(context_lens), int(block_size), float(scale), _ptr(out),
+                                            ctypes.byref(shape), _ptr(group_start), _ptr(group_shared),
+                                            G, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size: int,

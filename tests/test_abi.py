@@ -117,6 +117,21 @@ def test_decode_argument_errors():
     assert lib.paged_attn_decode(None, p, p, p, p, 16, 0.1, p, None, p, 0, None) == -1
 
 
+def test_grouped_argument_errors():
+    lib = pkv.load()
+    sh = shape()
+    p = ctypes.c_void_p(1 << 20)
+    args = lambda **o: [p, p, p, p, p, 16, 0.088, p, ctypes.byref(sh), o.get("gs", p), o.get("gh", p),
+                        o.get("G", 16), o.get("ws", p), o.get("wsb", 1 << 30), None]
+    assert lib.paged_attn_decode_grouped(*args(G=-1)) == -1
+    assert lib.paged_attn_decode_grouped(*args(G=70000)) == -1
+    assert lib.paged_attn_decode_grouped(*args(gs=None)) == -1
+    assert lib.paged_attn_decode_grouped(*args(gh=None)) == -1
+    assert lib.paged_attn_decode_grouped(*args(gs=ctypes.c_void_p((1 << 20) + 2))) == -2
+    assert lib.paged_attn_decode_grouped(*args(ws=None)) == -3
+    assert lib.paged_attn_decode_grouped(*args(G=0)) == 0  # no group: nothing queued
+
+
 def test_append_and_gather_argument_errors():
     lib = pkv.load()
     p = ctypes.c_void_p(1 << 20)

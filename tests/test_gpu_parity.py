@@ -84,6 +84,102 @@ def test_full_size_sampled_parity(cfg):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("pt", [0, 16, 64])
+def test_grouped_decode_equals_ungrouped(cfg, pt):
+    """paged_attn_decode_grouped over the groups the host finds (forks of one
+    prompt; singletons elsewhere) equals paged_attn_decode at the same
+    partition size bit for bit (checked inside run_gpu at every attention
+    point), and the oracle within tolerance. Forced 16/64-token partitions
+    put the shared/own boundary inside, at and past partition edges."""
+    w = configs.small(cfg)
+    say(f"[gpu] {w.name}: grouped decode, partition_tokens={pt}")
+    _check_against_oracle(w, run_gpu(w, partition_tokens=pt, grouped=True), f"{w.name}/grouped/P{pt}")
+
+
+def test_grouped_decode_full_size_shared_prefix():
+    """The shared-prefix workload at full size, grouped as the benchmark
+    runs it: bit-equal to the ungrouped pass (inside run_gpu) and sampled
+    outputs against the contiguous definition."""
+    import torch
+
+    w = configs.FULL[4]()
+    say(f"[gpu] full workload {w.name}, grouped: {w.description}")
+    results = run_gpu(w, grouped=True)
+    for pt, out in results:
+        pairs = sample_pairs(w, pt.context_lens)
+        ref = oracle_sampled(w, pt.step, pt.context_lens, pairs)
+        err = max(max_err(out.numpy()[s, h], r) for (s, h), r in ref.items())
+        say(f"  {w.name} grouped: {len(pairs)} sampled outputs, max-abs err {err:.3e}")
+        assert err <= TOL[w.dtype]
+    del results
+    torch.cuda.empty_cache()
+
+
+def test_grouped_decode_edge_groups():
+    """Hand-built groups: members whose context is all shared but for a few
+    tokens past the last whole chunk, a member with an empty context, a
+    claimed shared length longer than the shortest member, a shared length
+    that is not a whole chunk, groups of 1 to 4. Checked against the
+    oracle's paged decode and, bit for bit, against paged_attn_decode."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+    from tests.gpu_support import oracle_default
+
+    dev = torch.device("cuda:0")
+    H, D, B, NB = 3, 64, 16, 64
+    dtype = "bf16"
+    rng = np.random.default_rng(77)
+    ids = np.arange(NB * B, dtype=np.int64)
+    k = V.draw_np(5, V.STREAM_K, ids, H, D, dtype).reshape(NB, B, H, D)
+    v = V.draw_np(5, V.STREAM_V, ids, H, D, dtype).reshape(NB, B, H, D)
+    base = rng.permutation(NB)[:12].astype(np.int32)
+    rows, ctx = [], []
+    # group A: 3 members, identical tables, identical contexts (all shared)
+    for _ in range(3):
+        rows.append(base.copy()); ctx.append(100)
+    # group B: 4 members sharing 5 frames, own tails of different lengths
+    for i in range(4):
+        r = base.copy(); r[5:] = rng.permutation(NB)[:7]; rows.append(r); ctx.append([90, 81, 150, 80][i])
+    # group C: 2 members, one with an empty context
+    rows.append(base.copy()); ctx.append(37)
+    rows.append(base.copy()); ctx.append(0)
+    # group D: a single sequence
+    rows.append(rng.permutation(NB)[:12].astype(np.int32)); ctx.append(191)
+    tables = np.stack(rows).astype(np.int32)
+    ctx = np.asarray(ctx, dtype=np.int32)
+    S = len(ctx)
+    group_start = np.array([0, 3, 7, 9, 10], dtype=np.int32)
+    # claimed shared tokens: A all (more than the context: cut to it), B 5
+    # frames minus 3 tokens (not a whole chunk), C 40 (cut to 0), D 0
+    group_shared = np.array([1000, 5 * B - 3, 40, 0], dtype=np.int32)
+    q = V.draw_np(6, V.STREAM_Q, np.arange(S, dtype=np.int64), H, D, dtype)
+    scale = D ** -0.5
+    ref = oracle_default().paged_decode(q, k, v, tables, ctx, B, scale, dtype)
+    # bf16 values travel as their 16-bit patterns
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+                  for x in (q, k, v))
+    bt = torch.from_numpy(tables).to(dev)
+    cl = torch.from_numpy(ctx).to(dev)
+    for pt in (0, 16, 48):
+        out = torch.full((S, H, D), float("nan"), dtype=torch.float32, device=dev)
+        shape = pkv.lib.make_shape(tq, tk, bt, int(ctx.max()), pkv.lib.PA_F32, pt)
+        ws = pkv.alloc_workspace(shape, dev)
+        P = pkv.partition_tokens(shape)
+        pkv.paged_attn_decode_grouped(tq, tk, tv, bt, cl, B, scale, out, int(ctx.max()),
+                                      torch.from_numpy(group_start).to(dev),
+                                      torch.from_numpy(group_shared).to(dev), ws, pt)
+        two = torch.full_like(out, float("nan"))
+        pkv.paged_attn_decode(tq, tk, tv, bt, cl, B, scale, two, int(ctx.max()), ws, pt)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        assert np.array_equal(o, two.cpu().numpy()), pt
+        err = max_err(o, ref)
+        say(f"  edge groups P{P}: max-abs err {err:.3e}")
+        assert err <= TOL[dtype]
+
+
 def test_kv_append_bit_exact_with_cow():
     """The whole device cache (written by kv_append, copy-on-write copies
     included, NaN poison elsewhere) equals the oracle's host scatter, bit for bit."""
