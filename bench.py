@@ -83,7 +83,18 @@ def _compact_caches(w, tables, ctx, slot_ident):
     return k, v, tab
 
 
-def _time_bounded(fn, budget_s: float, max_runs: int = 50):
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _time_bounded(fn, budget_s: float, max_runs: int = 500):
     times = []
     t_start = time.perf_counter()
     while True:
@@ -121,6 +132,7 @@ def cpu_baseline_prefill(w, budget_s: float = 12.0):
     flops = 4 * w.D * w.H * int(pairs[sample].sum())
     return {
         "value": flops / t / 1e12, "unit": "TFLOP/s", "cores": orc.num_threads(), "kind": "oracle",
+        "cpu_model": _cpu_model(),
         "sample": f"{len(sample)} of {w.num_seqs} sequences (all {w.H} heads, "
                   f"{int(sub_n.sum())} queries, {int(pairs[sample].sum())} visible pairs), "
                   f"fp64 C oracle, median of {runs} runs",
@@ -147,6 +159,7 @@ def cpu_baseline(w, tables, ctx, budget_s: float = 12.0):
     kv_bytes = 2 * w.H * w.D * w.elem_bytes * int(sub_ctx.sum())
     return {
         "value": kv_bytes / t / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
+        "cpu_model": _cpu_model(),
         "sample": f"{len(sample)} of {w.num_seqs} sequences (all {w.H} heads, "
                   f"{int(sub_ctx.sum())} tokens, {kv_bytes / 1e6:.1f} MB of KV), fp64 C oracle, "
                   f"median of {runs} runs",
