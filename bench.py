@@ -185,6 +185,10 @@ def bench_prefill(args, w, pt, cache, dev):
     cl = torch.from_numpy(pt.context_lens).to(dev)
     qsd = torch.from_numpy(qs.astype(np.int32)).to(dev)
     max_ctx, max_q = int(pt.context_lens.max()), int(np.diff(qs).max())
+    from paged_kv_cache_126_amd.driver import prefill_order
+
+    order = None if args.prefill_batch_order else torch.from_numpy(
+        prefill_order(pt.context_lens, qs)).to(dev)
     # algorithmic work: 4 D flops per (query, visible key) per head
     n = np.asarray(w.query_lens, dtype=np.int64)
     ctx = pt.context_lens.astype(np.int64)
@@ -196,8 +200,9 @@ def bench_prefill(args, w, pt, cache, dev):
     flush_buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
 
-    def step():
-        pkv.paged_attn_prefill(q, cache.k, cache.v, bt, cl, qsd, w.B, w.scale, out, max_ctx, max_q)
+    def step(seq_order=order):
+        pkv.paged_attn_prefill(q, cache.k, cache.v, bt, cl, qsd, w.B, w.scale, out, max_ctx, max_q,
+                               seq_order=seq_order)
 
     for _ in range(args.warmup):
         step()
@@ -217,6 +222,19 @@ def bench_prefill(args, w, pt, cache, dev):
         with pkv.kernel_timing(k0, k1):
             step()
     torch.cuda.synchronize()
+    # context: the same launches in batch order
+    batch_order_ms = None
+    if order is not None:
+        bevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+        for b0, b1 in bevs:
+            if not args.no_flush:
+                torch.sum(flush_buf, dim=0, out=flush_sink)
+            b0.record()
+            step(None)
+            b1.record()
+        torch.cuda.synchronize()
+        batch_order_ms = float(np.mean([b0.elapsed_time(b1) for b0, b1 in bevs]))
     ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     kms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     tflops = flops / (kms * 1e-3) / 1e12
@@ -232,6 +250,8 @@ def bench_prefill(args, w, pt, cache, dev):
                    "sum_ctx": int(ctx.sum()), "visible_pairs": pairs, "flops": flops,
                    "cache_flush_between_steps": not args.no_flush},
         "us_per_step": round(ms * 1e3, 2),
+        "dispatch_order": "batch order" if order is None else "costliest sequence first (driver.prefill_order)",
+        "batch_order_us_per_step": None if batch_order_ms is None else round(batch_order_ms * 1e3, 2),
         "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
@@ -254,7 +274,7 @@ def bench_prefix(args, w, dev):
     import torch
 
     import paged_kv_cache_126_amd as pkv
-    from paged_kv_cache_126_amd.driver import DeviceCache, plan_prefix_rounds
+    from paged_kv_cache_126_amd.driver import DeviceCache, plan_prefix_rounds, prefill_order
     from workloads import values as V
 
     def prepare(caching):
@@ -283,7 +303,9 @@ def bench_prefix(args, w, dev):
                 out=torch.empty((T, w.H, w.D), dtype=torch.float32, device=dev),
                 bt=torch.from_numpy(rd.tables).to(dev), cl=torch.from_numpy(rd.context_lens).to(dev),
                 qs=torch.from_numpy(rd.query_start).to(dev), max_ctx=int(ctx.max()),
-                max_q=int(n.max()), rows=len(wb.slots), flops=4 * w.D * w.H * pairs))
+                max_q=int(n.max()), rows=len(wb.slots), flops=4 * w.D * w.H * pairs,
+                order=None if args.prefill_batch_order else
+                torch.from_numpy(prefill_order(rd.context_lens, rd.query_start)).to(dev)))
         return rounds, mgr, cache, launches, (host_s, host_py_s)
 
     flush_buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
@@ -301,10 +323,12 @@ def bench_prefix(args, w, dev):
                 if stamp:
                     with pkv.kernel_timing(evs[i][3], evs[i][4]):  # the kernel's own start and end
                         pkv.paged_attn_prefill(L["q"], cache.k, cache.v, L["bt"], L["cl"], L["qs"],
-                                               w.B, w.scale, L["out"], L["max_ctx"], L["max_q"])
+                                               w.B, w.scale, L["out"], L["max_ctx"], L["max_q"],
+                                               seq_order=L["order"])
                 else:
                     pkv.paged_attn_prefill(L["q"], cache.k, cache.v, L["bt"], L["cl"], L["qs"], w.B,
-                                           w.scale, L["out"], L["max_ctx"], L["max_q"])
+                                           w.scale, L["out"], L["max_ctx"], L["max_q"],
+                                           seq_order=L["order"])
                 if evs:
                     evs[i][2].record()
 
@@ -408,6 +432,9 @@ def main():
                     help="workload 5: a seeded permuted frame pool instead of first in, first out "
                          "in id order (the sensitivity variant)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--prefill-batch-order", action="store_true",
+                    help="dispatch prefill sequences in batch order (by default costliest first, "
+                         "driver.prefill_order)")
     ap.add_argument("--ungrouped", action="store_true",
                     help="time paged_attn_decode even where sequences share frames (by default "
                          "forked sequences go through paged_attn_decode_grouped)")

@@ -259,6 +259,13 @@ typedef struct pa_prefill_shape {
  *   block_tables, context_lens, k_cache, v_cache, block_size, scale: as for
  *                 paged_attn_decode
  *   out           [T, H, D] in out_dtype
+ *   seq_order     NULL, or device int32 [S]: the order in which the
+ *                 sequences' workgroups are dispatched, a permutation of
+ *                 0 .. S-1 (values are clamped into that range; a sequence
+ *                 missing from it gets no output). Sequences whose
+ *                 workgroups see the most (query, key) pairs first make the
+ *                 launch's tail shorter; prefill_order in the Python binding
+ *                 computes that order. Outputs do not depend on it.
  *
  * The n_s = query_start[s+1] - query_start[s] queries of sequence s are its
  * last n_s tokens, whose K and V are already in the cache: query r sits at
@@ -273,7 +280,8 @@ typedef struct pa_prefill_shape {
 pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, const int32_t* context_lens,
                              const int32_t* query_start, int32_t block_size, float scale,
-                             void* out, const pa_prefill_shape* shape, void* stream);
+                             void* out, const pa_prefill_shape* shape,
+                             const int32_t* seq_order, void* stream);
 
 /*
  * paged_gather: block translation made visible, for checking it bit for bit.

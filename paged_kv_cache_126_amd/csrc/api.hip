@@ -285,7 +285,8 @@ pa_status paged_attn_decode(const void* q, const void* k_cache, const void* v_ca
 pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, const int32_t* context_lens,
                              const int32_t* query_start, int32_t block_size, float scale,
-                             void* out, const pa_prefill_shape* sh, void* stream) {
+                             void* out, const pa_prefill_shape* sh, const int32_t* seq_order,
+                             void* stream) {
   if (!sh) return PA_EINVAL;
   if (sh->num_seqs < 0 || sh->num_heads <= 0 || sh->block_size <= 0 || sh->num_blocks <= 0 ||
       sh->num_blocks > 0x7FFFFFFFLL || sh->max_blocks_per_seq <= 0 || sh->max_context_len < 0 ||
@@ -306,7 +307,8 @@ pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_c
     return PA_EINVAL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(out, static_cast<uintptr_t>(elem_bytes(sh->out_dtype))) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4) ||
+      !aligned(seq_order, 4))
     return PA_EALIGN;
   pa::PrefillArgs a;
   a.q = q;
@@ -326,6 +328,7 @@ pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_c
   a.max_query_len = sh->max_query_len;
   a.total_queries = sh->total_queries;
   a.out_f32 = sh->out_dtype == PA_F32 ? 1 : 0;
+  a.seq_order = seq_order;
   return from_hip(pa::launch_prefill(a, to_internal(sh->kv_dtype), sh->head_dim,
                                      static_cast<hipStream_t>(stream)));
 }

@@ -83,6 +83,7 @@ struct PrefillArgs {
   int32_t max_query_len;
   int32_t total_queries;
   int32_t out_f32;
+  const int32_t* seq_order;    // [S] dispatch order of the sequences, or null
 };
 
 bool prefill_supported(Dtype dt, int head_dim);

@@ -141,7 +141,10 @@ void prefill_kernel(PrefillArgs a) {
   }
   const int qt = ntiles - 1 - tile;
   const int h = group % static_cast<int>(gridDim.y);
-  const int s = group / static_cast<int>(gridDim.y);
+  // Sequences are dispatched in seq_order (costliest first shortens the
+  // tail of the launch), else in batch order.
+  int s = group / static_cast<int>(gridDim.y);
+  if (a.seq_order != nullptr) s = min(max(a.seq_order[s], 0), a.num_seqs - 1);
   int ctx = a.context_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
   int q0 = a.query_start[s];

@@ -165,6 +165,17 @@ def share_groups(tables: np.ndarray, context_lens: np.ndarray, block_size: int,
     return np.asarray(starts, dtype=np.int32), np.asarray(shared, dtype=np.int32)
 
 
+def prefill_order(context_lens, query_start) -> np.ndarray:
+    """Dispatch order for ``paged_attn_prefill``: sequences by the number of
+    (query, key) pairs their queries see, most first (a longest-first
+    schedule leaves the shortest work for the launch's tail). int32 [S]."""
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    n = np.diff(np.asarray(query_start, dtype=np.int64))
+    n = np.clip(n, 0, ctx)
+    pairs = n * (ctx - n) + n * (n + 1) // 2
+    return np.argsort(-pairs, kind="stable").astype(np.int32)
+
+
 class DeviceCache:
     """K and V caches [NB, B, H, D] in device memory, optionally NaN-filled."""
 

@@ -97,7 +97,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.paged_attn_decode_grouped.restype = ctypes.c_int
     lib.paged_attn_merge.argtypes = [P, P, SH, P, SZ, P]
     lib.paged_attn_merge.restype = ctypes.c_int
-    lib.paged_attn_prefill.argtypes = [P, P, P, P, P, P, I32, F, P, ctypes.POINTER(PrefillShape), P]
+    lib.paged_attn_prefill.argtypes = [P, P, P, P, P, P, I32, F, P, ctypes.POINTER(PrefillShape), P, P]
     lib.paged_attn_prefill.restype = ctypes.c_int
     lib.paged_gather.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I64, I32, I32, ctypes.c_int, P]
     lib.paged_gather.restype = ctypes.c_int
@@ -262,10 +262,11 @@ def paged_attn_decode_grouped(q, k_cache, v_cache, block_tables, context_lens, b
 
 def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size: int,
                        scale: float, out, max_context_len: int, max_query_len: int,
-                       stream=None) -> None:
+                       stream=None, seq_order=None) -> None:
     """Causal attention of each sequence's last tokens into ``out`` [T, H, D];
-    see include/paged_attn.h."""
-    _dense(q, k_cache, v_cache, block_tables, context_lens, query_start, out)
+    see include/paged_attn.h. ``seq_order`` (int32 device [S], optional) is
+    the dispatch order of the sequences (``driver.prefill_order``)."""
+    _dense(q, k_cache, v_cache, block_tables, context_lens, query_start, out, seq_order)
     T, H, D = q.shape
     NB, B = k_cache.shape[0], k_cache.shape[1]
     S = context_lens.shape[0]
@@ -277,12 +278,14 @@ def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_st
         raise TypeError("query_start must be int32 [S + 1]")
     if str(block_tables.dtype) != "torch.int32" or str(context_lens.dtype) != "torch.int32":
         raise TypeError("block_tables and context_lens must be int32")
+    if seq_order is not None and (seq_order.shape != (S,) or str(seq_order.dtype) != "torch.int32"):
+        raise TypeError("seq_order must be int32 [S]")
     shape = PrefillShape(S, H, D, B, NB, block_tables.shape[1], int(max_context_len),
                          int(max_query_len), T, dtype_code(k_cache), dtype_code(out))
     _check("paged_attn_prefill", load().paged_attn_prefill(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         _ptr(query_start), int(block_size), float(scale), _ptr(out), ctypes.byref(shape),
-        _stream(stream)))
+        _ptr(seq_order), _stream(stream)))
 
 
 def paged_gather(cache, block_tables, context_lens, out_row_start, out, max_context_len: int,

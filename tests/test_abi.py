@@ -173,21 +173,21 @@ def test_prefill_argument_errors(bad, code):
     lib = pkv.load()
     p = ctypes.c_void_p(1 << 20)
     sh = prefill_shape(**bad)
-    assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, ctypes.byref(sh), None) == code
+    assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, ctypes.byref(sh), None, None) == code
 
 
 def test_prefill_pointer_errors():
     lib = pkv.load()
     p = ctypes.c_void_p(1 << 20)
     sh = prefill_shape()
-    assert lib.paged_attn_prefill(None, p, p, p, p, p, 16, 0.088, p, ctypes.byref(sh), None) == -1
-    assert lib.paged_attn_prefill(p, p, p, p, p, None, 16, 0.088, p, ctypes.byref(sh), None) == -1
-    assert lib.paged_attn_prefill(p, p, p, p, p, p, 32, 0.088, p, ctypes.byref(sh), None) == -1
+    assert lib.paged_attn_prefill(None, p, p, p, p, p, 16, 0.088, p, ctypes.byref(sh), None, None) == -1
+    assert lib.paged_attn_prefill(p, p, p, p, p, None, 16, 0.088, p, ctypes.byref(sh), None, None) == -1
+    assert lib.paged_attn_prefill(p, p, p, p, p, p, 32, 0.088, p, ctypes.byref(sh), None, None) == -1
     assert lib.paged_attn_prefill(p, p, p, p, p, ctypes.c_void_p((1 << 20) + 2), 16, 0.088, p,
-                                  ctypes.byref(sh), None) == -2
-    assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, None, None) == -1
+                                  ctypes.byref(sh), None, None) == -2
+    assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, None, None, None) == -1
     empty = prefill_shape(total_queries=0)
-    assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, ctypes.byref(empty), None) == 0
+    assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, ctypes.byref(empty), None, None) == 0
 
 
 def test_stream_read_argument_errors():

@@ -91,3 +91,18 @@ def test_hand_example():
     assert gs.tolist() == [0, 3, 5] and gsh.tolist() == [4, 6]
     gs, gsh = share_groups(tables, ctx, B, max_group=2)
     assert gs.tolist() == [0, 2, 3, 5] and gsh.tolist() == [8, 0, 6]
+
+
+def test_prefill_order_is_costliest_first():
+    """driver.prefill_order: a permutation of the batch, sequences by visible
+    (query, key) pairs, most first, ties in batch order."""
+    from paged_kv_cache_126_amd.driver import prefill_order
+
+    ctx = np.array([10, 300, 300, 0, 40, 1000], dtype=np.int32)
+    qs = np.array([0, 10, 12, 312, 312, 352, 356], dtype=np.int32)  # n = 10, 2, 300, 0, 40, 4
+    order = prefill_order(ctx, qs)
+    n = np.diff(qs).astype(np.int64)
+    pairs = n * (ctx - n) + n * (n + 1) // 2   # 55, 599, 45150, 0, 820, 4006
+    assert sorted(order.tolist()) == list(range(6)) and order.dtype == np.int32
+    assert order.tolist() == [2, 5, 4, 1, 0, 3]
+    assert np.all(np.diff(pairs[order]) <= 0)
