@@ -140,6 +140,42 @@ def cpu_baseline_prefill(w, budget_s: float = 12.0):
     }
 
 
+def cpu_baseline_prefix(w, budget_s: float = 12.0):
+    """The fp64 oracle on a bounded sample of the prefix-cached rounds: the
+    oracle side's own replay of the rounds (its prefix cache), then its paged
+    prefill over the positions one request of the last round must compute,
+    the request with the fewest visible (query, key) pairs. The rate counts
+    that request's prompt tokens (reused + computed), as the GPU figure does."""
+    from oracle.oracle import default
+    from oracle.prefixcache import replay_rounds
+    from workloads import values as V
+
+    orc = default()
+    rounds, _ = replay_rounds(w)
+    rd = rounds[-1]
+    ctx = rd.context_lens.astype(np.int64)
+    n = ctx - rd.reused.astype(np.int64)
+    pairs = n * (ctx - n) + n * (n + 1) // 2
+    cand = np.flatnonzero(n > 0)
+    i = int(cand[np.argmin(pairs[cand])])
+    k, v, tab = _compact_caches(w, rd.tables[[i]], rd.context_lens[[i]], rd.slot_ident)
+    c = rd.seqs[i]
+    ids = w.idents(c, np.arange(int(rd.reused[i]), int(ctx[i])))
+    q = V.draw_np(w.seed, V.STREAM_Q, ids, w.H, w.D, w.dtype)
+    qs = np.array([0, int(n[i])], dtype=np.int64)
+    sub_ctx = rd.context_lens[[i]]
+    t, runs = _time_bounded(
+        lambda: orc.paged_prefill(q, k, v, tab, sub_ctx, qs, w.B, w.scale, w.dtype), budget_s, 50)
+    return {
+        "value": float(ctx[i]) / t, "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
+        "cpu_model": _cpu_model(),
+        "sample": f"1 request of the last round ({int(ctx[i])} prompt tokens, {int(rd.reused[i])} "
+                  f"reused, {int(n[i])} computed, all {w.H} heads), after the oracle's own replay of "
+                  f"all {len(rounds)} rounds; fp64 C oracle, median of {runs} runs",
+        "seconds_per_sample": t,
+    }
+
+
 def cpu_baseline(w, tables, ctx, budget_s: float = 12.0):
     """The fp64 oracle on a bounded sample of the same workload (host cores)."""
     from oracle import blockmgr as obm
@@ -415,6 +451,9 @@ def bench_prefix(args, w, dev):
                      "launch_us_per_step": round(on["kernel_ms"] * 1e3, 2)},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline_prefix(w)
     print(json.dumps(out), flush=True)
 
 
