@@ -483,8 +483,8 @@ def main():
                          "reference for hardware traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
-              "has no cross-GPU step in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has "
+              "no cross-GPU step; each GPU would serve its own sequences", file=sys.stderr)
         sys.exit(2)
 
     import torch
