@@ -612,3 +612,68 @@ def test_stream_read_probe_runs_and_leaves_sink():
         pkv.lib.stream_read(buf, sink)
         torch.cuda.synchronize()
         assert int(sink.item()) == 7
+
+
+@pytest.mark.parametrize("cfg", [2, 4, 5])
+def test_graph_capture_replays_equal_eager(cfg):
+    """A decode step (kv_append + partition + merge; grouped on the
+    shared-prefix workload) captured in a HIP graph: every replay, with
+    eager launches and synchronisations in between, equals the eager
+    result bit for bit. The library's launches allocate nothing and set no
+    memory, so capture needs nothing special."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+    from paged_kv_cache_126_amd.driver import share_groups
+
+    w = configs.small(cfg)
+    say(f"[gpu] graph capture, {w.name}")
+    res, cache = run_gpu(w, keep_cache=True)
+    pt, _ = res[-1]
+    dev = torch.device("cuda:0")
+    q = V.draw_torch(w.seed, V.STREAM_Q, w.q_idents(pt.step), w.H, w.D, w.dtype, dev).contiguous()
+    bt = torch.from_numpy(pt.tables).to(dev)
+    cl = torch.from_numpy(pt.context_lens).to(dev)
+    mc = int(pt.context_lens.max())
+    out = torch.zeros((w.num_seqs, w.H, w.D), dtype=torch.float32, device=dev)
+    shape = pkv.lib.make_shape(q, cache.k, bt, mc, pkv.lib.PA_F32, 16)  # forced splits: merge runs
+    ws = pkv.alloc_workspace(shape, dev)
+    gs, gsh = share_groups(pt.tables, pt.context_lens, w.B)
+    gsd, gshd = torch.from_numpy(gs).to(dev), torch.from_numpy(gsh).to(dev)
+    # rewrite the last rows of every sequence (idempotent) as the step's append
+    last = np.array([int(pt.tables[s, (c - 1) // w.B]) * w.B + (c - 1) % w.B
+                     for s, c in enumerate(pt.context_lens.tolist()) if c > 0], dtype=np.int64)
+    k_new = cache.k.reshape(-1, w.H, w.D)[torch.from_numpy(last).to(dev)].contiguous()
+    v_new = cache.v.reshape(-1, w.H, w.D)[torch.from_numpy(last).to(dev)].contiguous()
+    slots = torch.from_numpy(last).to(dev)
+
+    def step():
+        pkv.kv_append(k_new, v_new, slots, cache.k, cache.v)
+        if (gsh > 0).any():
+            pkv.paged_attn_decode_grouped(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, mc, gsd,
+                                          gshd, ws, 16)
+        else:
+            pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, out, mc, ws, 16)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+        other = torch.zeros_like(out)
+        pkv.paged_attn_decode(q, cache.k, cache.v, bt, cl, w.B, w.scale, other, mc, ws, 16)
+        torch.cuda.synchronize()
+        assert torch.equal(other, ref)
+    del g
