@@ -594,6 +594,11 @@ def main():
         pt.tables[s_, np.arange(c) // w.B].astype(np.int64) * w.B + np.arange(c) % w.B
         for s_, c in enumerate(pt.context_lens.tolist()) if c > 0]))
     kv_bytes_unique = 2 * w.H * w.D * w.elem_bytes * len(uniq_slots)
+    # block-manager memory use at this point: distinct cached tokens over the
+    # slots of the frames holding them (waste is the unfilled tail slots)
+    frames_used = len(np.unique(uniq_slots // w.B))
+    memory = {"frames_used": int(frames_used), "tokens_stored": int(len(uniq_slots)),
+              "utilisation": round(len(uniq_slots) / (frames_used * w.B), 5)}
     # Cache flush between steps: read a 2 GiB buffer (8x the 256 MB last-level
     # cache). A read leaves clean lines; a write would leave dirty lines whose
     # write-back competes with the timed step.
@@ -790,6 +795,7 @@ def main():
             "partition_tokens": part_tokens,
             "out_dtype": "f32", "cache_flush_between_steps": not args.no_flush,
             "cache_policy": "reuse" if policy else "stream",
+            "memory": memory,
         },
         "us_per_step": round(ms * 1e3, 2),
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),

@@ -267,6 +267,30 @@ def pin_paged_equals_dense(orc):
         assert np.max(np.abs(paged - dense)) <= 1e-12
 
 
+def pin_gather_then_dense_torch(orc):
+    """A structurally different second opinion ("Solving the LLM Memory Wall",
+    "Implementation": the forward pass gathers each sequence's blocks
+    through its table, flattens them, trims to the sequence length and runs
+    ordinary scaled dot-product attention): the same computation in torch
+    fp64 on the CPU, with its own widening, equals the oracle within 1e-12."""
+    import torch
+
+    for dt, seed in (("bf16", 81), ("f16", 82), ("f32", 83)):
+        c = Case(seed, 5, 3, 16, 7, dt, 60)
+        k_all = torch.from_numpy(np_widen(c.k, dt))
+        v_all = torch.from_numpy(np_widen(c.v, dt))
+        q_all = torch.from_numpy(np_widen(c.q, dt))
+        want = c.decode(orc)
+        for s in range(c.S):
+            n = int(c.ctx[s])
+            blocks = torch.from_numpy(c.tables[s, :-(-n // c.B)].astype(np.int64))
+            k = k_all[blocks].reshape(-1, c.H, c.D)[:n]          # [n, H, D]
+            v = v_all[blocks].reshape(-1, c.H, c.D)[:n]
+            scores = torch.einsum("hd,nhd->hn", q_all[s], k) * c.scale
+            o = torch.einsum("hn,nhd->hd", torch.softmax(scores, dim=-1), v)
+            assert np.max(np.abs(o.numpy() - want[s])) <= 1e-12, (dt, s)
+
+
 def pin_split_merge_identity(orc):
     """Partitioned attention merged by log-sum-exp equals the single pass."""
     c = Case(71, 4, 2, 8, 5, "f32", 90, min_ctx=2)
