@@ -210,10 +210,11 @@ pa_status paged_attn_merge(const int32_t* context_lens, void* out, const pa_deco
  *
  *   group_start   device int32 [num_groups + 1]: group g is the batch's
  *                 sequences group_start[g] .. group_start[g + 1] - 1, at most
- *                 4 of them (PA_MAX_GROUP). Groups should cover every
- *                 sequence once: a sequence in no group gets no output, one
- *                 in two groups is written twice, members past the 4th are
- *                 ignored. Values are clamped into [0, S].
+ *                 4 of them (PA_MAX_GROUP). Groups must cover every
+ *                 sequence exactly once: the output of a sequence in no
+ *                 group (or past a group's 4th member) is undefined, and
+ *                 one in two groups is written twice. Values are clamped
+ *                 into [0, S], so no access leaves the buffers.
  *   group_shared  device int32 [num_groups]: tokens the members share. The
  *                 first ceil(group_shared[g] / B) entries of the members'
  *                 block-table rows must be equal; the shared length is cut
