@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum pa_dtype {
   PA_F32 = 0,
@@ -99,6 +99,17 @@ typedef struct pa_decode_shape {
                                   library from the shape. Rounded up to what the
                                   kernel's tiling needs. */
   int32_t cache_policy;        /* a pa_cache_policy value */
+  const int32_t* dispatch_order; /* NULL, or a device int32 array: the order in
+                                  which the launch's units are dispatched, a
+                                  permutation of their indices (sequences 0 .. S-1;
+                                  groups 0 .. num_groups-1 for
+                                  paged_attn_decode_grouped). Values are clamped
+                                  into range; a unit missing from it gets no output.
+                                  Longest work first shortens the launch's tail;
+                                  with an order the default partition size also
+                                  grows (see paged_attn_partition_tokens).
+                                  Outputs equal the unordered call's at the same
+                                  partition size, bit for bit. */
 } pa_decode_shape;
 
 /* Human-readable name of a status code. Never NULL. */
@@ -152,7 +163,13 @@ pa_status kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
  */
 size_t paged_attn_workspace_size(const pa_decode_shape* shape);
 
-/* Partition size (tokens) the library uses for `shape`; 0 if invalid. */
+/*
+ * Partition size (tokens) the library uses for `shape`; 0 if invalid. The
+ * default is the largest of 2048, 1024 and 512 tokens that still gives about
+ * 8,192 workgroups (S * H * partitions of the longest context), or, with a
+ * dispatch_order, about 1,024: longest-first dispatch balances long
+ * partitions, which write fewer partial results and often need no merge.
+ */
 int32_t paged_attn_partition_tokens(const pa_decode_shape* shape);
 
 /*

@@ -26,6 +26,9 @@ namespace {
 constexpr int32_t kMaxDefaultPartition = 2048;
 constexpr int32_t kMinDefaultPartition = 512;
 constexpr int64_t kTargetWorkgroups = 8192;
+// With a dispatch order (longest work first) the tail is balanced by the
+// order, and four workgroups per compute unit suffice.
+constexpr int64_t kTargetWorkgroupsOrdered = 1024;
 constexpr int64_t kMaxGridYZ = 65535;
 constexpr size_t kWorkspaceAlign = 256;
 static_assert(pa::kMaxGroup == PA_MAX_GROUP, "group size limit of the kernels and the header");
@@ -69,8 +72,8 @@ pa_status check_shape(const pa_decode_shape* sh, int32_t* part_tokens, int32_t* 
   if (pt == 0) {
     pt = kMaxDefaultPartition;
     const int64_t pairs = static_cast<int64_t>(sh->num_seqs) * sh->num_heads;
-    while (pt > kMinDefaultPartition &&
-           pairs * ((sh->max_context_len + pt - 1) / pt) < kTargetWorkgroups)
+    const int64_t target = sh->dispatch_order ? kTargetWorkgroupsOrdered : kTargetWorkgroups;
+    while (pt > kMinDefaultPartition && pairs * ((sh->max_context_len + pt - 1) / pt) < target)
       pt /= 2;
   }
   pt = (pt + chunk - 1) / chunk * chunk;
@@ -109,7 +112,7 @@ pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PA_EINVAL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(out, static_cast<uintptr_t>(elem_bytes(sh->out_dtype))) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(sh->dispatch_order, 4))
     return PA_EALIGN;
   const size_t need = workspace_bytes_for(sh, parts);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kWorkspaceAlign)))
@@ -134,6 +137,7 @@ pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache
   a->max_parts = parts;
   a->out_f32 = sh->out_dtype == PA_F32 ? 1 : 0;
   a->stream_loads = sh->cache_policy == PA_CACHE_STREAM ? 1 : 0;
+  a->seq_order = sh->dispatch_order;
   return PA_OK;
 }
 

@@ -309,7 +309,8 @@ void decode_partition_kernel(DecodeArgs a) {
 
   const int h = blockIdx.x;
   const int part = blockIdx.y;
-  const int s = blockIdx.z;
+  const int s = a.seq_order ? min(max(a.seq_order[blockIdx.z], 0), a.num_seqs - 1)
+                            : static_cast<int>(blockIdx.z);
   const int ctx = clamp_ctx(a, s);
   const int n_parts = parts_of(a, ctx);
   if (part >= n_parts) return;  // uniform over the workgroup
@@ -361,7 +362,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_group_kernel(DecodeArgs a, Gr
 
   const int h = blockIdx.x;
   const int part = blockIdx.y;
-  const int gi = blockIdx.z;
+  const int gi = a.seq_order ? min(max(a.seq_order[blockIdx.z], 0), g.num_groups - 1)
+                             : static_cast<int>(blockIdx.z);
   const int s0 = min(max(g.group_start[gi], 0), a.num_seqs);
   const int ns = min(max(g.group_start[gi + 1], s0), a.num_seqs) - s0;  // members (<= G)
   const int members = min(ns, G);

@@ -165,6 +165,25 @@ def share_groups(tables: np.ndarray, context_lens: np.ndarray, block_size: int,
     return np.asarray(starts, dtype=np.int32), np.asarray(shared, dtype=np.int32)
 
 
+def decode_order(context_lens) -> np.ndarray:
+    """Dispatch order for decode (``pa_decode_shape.dispatch_order``): the
+    sequences by context length, longest first, ties in batch order. int32 [S]."""
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    return np.argsort(-ctx, kind="stable").astype(np.int32)
+
+
+def group_order(group_start, group_shared, context_lens) -> np.ndarray:
+    """Dispatch order for ``paged_attn_decode_grouped``: groups by the rows
+    their workgroups read (the shared tokens once, then each member's own),
+    most first. int32 [G]."""
+    gs = np.asarray(group_start, dtype=np.int64)
+    sh = np.asarray(group_shared, dtype=np.int64)
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    work = np.array([sh[g] + np.sum(np.maximum(ctx[gs[g]:gs[g + 1]] - sh[g], 0))
+                     for g in range(len(sh))], dtype=np.int64)
+    return np.argsort(-work, kind="stable").astype(np.int32)
+
+
 def prefill_order(context_lens, query_start) -> np.ndarray:
     """Dispatch order for ``paged_attn_prefill``: sequences by the number of
     (query, key) pairs their queries see, most first (a longest-first

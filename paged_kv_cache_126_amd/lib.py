@@ -45,6 +45,7 @@ class DecodeShape(ctypes.Structure):
         ("out_dtype", ctypes.c_int),
         ("partition_tokens", ctypes.c_int32),
         ("cache_policy", ctypes.c_int32),
+        ("dispatch_order", ctypes.c_void_p),
     ]
 
 
@@ -141,13 +142,19 @@ def _dense(*tensors) -> None:
 
 
 def make_shape(q, k_cache, block_tables, max_context_len: int, out_dtype_code: int | None = None,
-               partition_tokens: int = 0, cache_policy: int = PA_CACHE_STREAM) -> DecodeShape:
+               partition_tokens: int = 0, cache_policy: int = PA_CACHE_STREAM,
+               dispatch_order=None) -> DecodeShape:
+    """``dispatch_order``: None, or an int32 device tensor (see pa_decode_shape)."""
     S, H, D = q.shape
     NB, B = k_cache.shape[0], k_cache.shape[1]
     kv = dtype_code(k_cache)
+    if dispatch_order is not None:
+        _dense(dispatch_order)
+        if str(dispatch_order.dtype) != "torch.int32" or dispatch_order.dim() != 1:
+            raise TypeError("dispatch_order must be a 1-D int32 tensor")
     return DecodeShape(S, H, D, B, NB, block_tables.shape[1], int(max_context_len), kv,
                        kv if out_dtype_code is None else out_dtype_code, int(partition_tokens),
-                       int(cache_policy))
+                       int(cache_policy), _ptr(dispatch_order) or None)
 
 
 def workspace_size(shape: DecodeShape) -> int:
@@ -212,16 +219,19 @@ def _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out):
 
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_size: int, scale: float,
                       out, max_context_len: int, workspace=None, partition_tokens: int = 0,
-                      stream=None, phase: str = "both", cache_policy: int = PA_CACHE_STREAM) -> None:
+                      stream=None, phase: str = "both", cache_policy: int = PA_CACHE_STREAM,
+                      dispatch_order=None) -> None:
     """Decode attention into ``out``; see include/paged_attn.h.
 
     ``phase`` selects "both" (paged_attn_decode), "partitions" or "merge"
     (the two launches it is made of). ``cache_policy`` is PA_CACHE_REUSE when
     sequences of the batch share frames, else PA_CACHE_STREAM.
+    ``dispatch_order`` (int32 [S], e.g. ``driver.decode_order``) sets the order
+    the sequences are dispatched in; give the merge phase the same one.
     """
     _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out)
     shape = make_shape(q, k_cache, block_tables, max_context_len, dtype_code(out), partition_tokens,
-                       cache_policy)
+                       cache_policy, dispatch_order)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load()
     st = _stream(stream)
@@ -239,7 +249,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_siz
 def paged_attn_decode_grouped(q, k_cache, v_cache, block_tables, context_lens, block_size: int,
                               scale: float, out, max_context_len: int, group_start, group_shared,
                               workspace=None, partition_tokens: int = 0, stream=None,
-                              cache_policy: int = PA_CACHE_STREAM) -> None:
+                              cache_policy: int = PA_CACHE_STREAM, dispatch_order=None) -> None:
     """Decode attention with groups of sequences that share leading frames
     (int32 device ``group_start`` [G + 1], ``group_shared`` [G] tokens); see
     include/paged_attn.h. ``workspace`` is sized as for ``paged_attn_decode``."""
@@ -251,7 +261,7 @@ def paged_attn_decode_grouped(q, k_cache, v_cache, block_tables, context_lens, b
     if str(group_start.dtype) != "torch.int32" or str(group_shared.dtype) != "torch.int32":
         raise TypeError("group arrays must be int32")
     shape = make_shape(q, k_cache, block_tables, max_context_len, dtype_code(out), partition_tokens,
-                       cache_policy)
+                       cache_policy, dispatch_order)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("paged_attn_decode_grouped",
            load().paged_attn_decode_grouped(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     for header in (HEADER, BLOCKS_HEADER):
         for name in declared_functions(header):
             assert hasattr(lib, name), name
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
 
 
 def test_status_strings():
@@ -115,6 +115,22 @@ def test_decode_argument_errors():
     assert lib.paged_attn_decode(*args(wsb=16)) == -3
     assert lib.paged_attn_decode(*args(ws=ctypes.c_void_p((1 << 20) + 16))) == -3
     assert lib.paged_attn_decode(None, p, p, p, p, 16, 0.1, p, None, p, 0, None) == -1
+
+
+def test_partition_size_with_a_dispatch_order():
+    """With a dispatch order the default partition targets about 1,024
+    workgroups instead of 8,192."""
+    p = ctypes.c_void_p(1 << 20)
+    assert pkv.partition_tokens(shape()) == 512
+    assert pkv.partition_tokens(shape(dispatch_order=p)) == 2048          # 64 x 32 pairs
+    assert pkv.partition_tokens(shape(num_seqs=8, num_heads=40, max_context_len=32768,
+                                      max_blocks_per_seq=2048, dispatch_order=p)) == 2048
+    assert pkv.partition_tokens(shape(num_seqs=1, num_heads=32, max_context_len=32768,
+                                      max_blocks_per_seq=2048, dispatch_order=p)) == 1024
+    lib = pkv.load()
+    sh = shape(dispatch_order=ctypes.c_void_p((1 << 20) + 2))
+    rc = lib.paged_attn_decode(p, p, p, p, p, 16, 0.088, p, ctypes.byref(sh), p, 1 << 30, None)
+    assert rc == -2
 
 
 def test_grouped_argument_errors():

@@ -71,7 +71,7 @@ def test_full_size_sampled_parity(cfg):
 
     w = configs.FULL[cfg]()
     say(f"[gpu] full workload {w.name}: {w.description}")
-    results = run_gpu(w)
+    results = run_gpu(w, order="longest")  # as the benchmark dispatches
     for pt, out in results:
         o = out.numpy()
         assert np.all(np.isfinite(o)), "non-finite output"
@@ -97,6 +97,21 @@ def test_grouped_decode_equals_ungrouped(cfg, pt):
     _check_against_oracle(w, run_gpu(w, partition_tokens=pt, grouped=True), f"{w.name}/grouped/P{pt}")
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 4, 5])
+def test_dispatch_order_leaves_outputs_unchanged(cfg):
+    """A random dispatch order (sequences, or groups in the grouped pass)
+    gives the batch-order outputs bit for bit at the same partition size;
+    longest-first with its own default partition size matches the oracle."""
+    w = configs.small(cfg)
+    say(f"[gpu] {w.name}: dispatch orders")
+    grouped = cfg == 4
+    base = run_gpu(w, partition_tokens=16, grouped=grouped)
+    shuffled = run_gpu(w, partition_tokens=16, grouped=grouped, order="random")
+    for (_, x), (_, y) in zip(base, shuffled):
+        assert np.array_equal(x.numpy(), y.numpy())
+    _check_against_oracle(w, run_gpu(w, grouped=grouped, order="longest"), f"{w.name}/longest")
+
+
 def test_grouped_decode_full_size_shared_prefix():
     """The shared-prefix workload at full size, grouped as the benchmark
     runs it: bit-equal to the ungrouped pass (inside run_gpu) and sampled
@@ -105,7 +120,7 @@ def test_grouped_decode_full_size_shared_prefix():
 
     w = configs.FULL[4]()
     say(f"[gpu] full workload {w.name}, grouped: {w.description}")
-    results = run_gpu(w, grouped=True)
+    results = run_gpu(w, grouped=True, order="longest")
     for pt, out in results:
         pairs = sample_pairs(w, pt.context_lens)
         ref = oracle_sampled(w, pt.step, pt.context_lens, pairs)
