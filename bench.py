@@ -705,14 +705,16 @@ def main():
         for i in range(args.steps):
             if not args.no_flush:
                 flush()
-            step(uevs[i], use_groups=False)
+            # batch order: sorting by length would split the fork families whose
+            # shared frames this pass relies on reading close together in time
+            step(uevs[i], use_groups=False, ordered=False)
         torch.cuda.synchronize()
         ums = float(np.mean([e[0].elapsed_time(e[2]) for e in uevs]))
         ungrouped_ctx = {"us_per_step": round(ums * 1e3, 2),
                          "GB/s": round(kv_bytes / (ums * 1e-3) / 1e9, 1),
                          "cache_policy": "reuse" if ungrouped_policy else "stream",
-                         "what": "the same steps through paged_attn_decode (every sequence "
-                                 "reads its own rows; shared frames hit in cache)"}
+                         "what": "the same steps through paged_attn_decode in batch order (every "
+                                 "sequence reads its own rows; shared frames hit in cache)"}
         log(f"[bench] ungrouped: step {ums * 1e3:.1f} us")
     # Context: the same steps dispatched in batch order.
     batch_order_ctx = None
