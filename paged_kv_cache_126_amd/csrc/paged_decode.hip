@@ -23,6 +23,14 @@
 // LDS, both with the log-sum-exp rule. The context partitions of one
 // sequence are combined the same way by the merge kernel.
 //
+// An optional dispatch order maps the launch's last grid index to the
+// sequence (or group) it serves, so that the longest work starts first.
+// The grouped pass serves up to four sequences per workgroup whose block
+// tables start with the same frames (forks of one prompt): each shared row
+// is loaded once and folded into every member's softmax ("PagedAttention:
+// Virtual Memory Guide for LLM Inference", "2. Zero-Copy Branching via
+// Copy-on-Write", shares the frames; here the reads are shared too).
+//
 // Masking: tokens at or past ctx are never loaded; their score is -inf and
 // their weight exactly 0, so NaN-filled unused slots cannot leak in. The
 // running maximum starts at a large finite negative value so that no
