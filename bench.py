@@ -39,11 +39,23 @@ KERNEL_SOURCES = {"paged_decode": ("paged_decode.hip", "pa_device.h", "pa_launch
                   "paged_prefill": ("paged_prefill.hip", "pa_device.h", "pa_launch.h")}
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines: what the compiler sees
+    (string literals in these files hold no comment markers)."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_digest(kind: str = "paged_decode") -> str:
+    """Digest of the code (comments excluded) a kernel is built from: hardware
+    counters taken on one digest are reported only while it still holds."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "paged_kv_cache_126_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_126_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
