@@ -123,6 +123,7 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int kPieces = D / 8;   // 16-byte pieces per cache row
   constexpr int kPadK = 8;         // LDS row padding (elements) against bank conflicts
   constexpr int kPadV = 16;
+  constexpr bool kSplitP = std::is_same<T, BF16>::value;  // weights as hi + lo (see below)
 
   // Work item of this workgroup. Workgroups go to the 8 XCDs round-robin by
   // linear id, and each XCD has its own L2; the query tiles of one (head,
@@ -221,7 +222,29 @@ void prefill_kernel(PrefillArgs a) {
   // position into (block, offset) with a shift and a mask.
   const bool pow2_block = (a.block_size & (a.block_size - 1)) == 0;
   const int block_shift = __builtin_ctz(static_cast<unsigned>(a.block_size));
+  // Piece i of a wavefront covers kWaveKeys consecutive keys; with
+  // power-of-two frames of at least that many tokens they sit in one frame,
+  // whose number is then the same for the whole wavefront. Rows past the
+  // workgroup's last key are loaded from the last key's row (finite data,
+  // weight 0), which keeps that property and needs no per-lane branch.
+  constexpr int kWaveKeys = 64 / kPieces;
+  const bool uniform_frames = pow2_block && a.block_size >= kWaveKeys && tbl_in_lds;
+  const uint32_t lane_col = 16u * (threadIdx.x % kPieces) + static_cast<uint32_t>(head_bytes);
   auto fetch = [&](const int k0) {
+    if (uniform_frames) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int key0 = (wave * 64 + i * kWaves * 64) / kPieces;  // the wavefront's first key
+        const int tok0 = min(k0 + key0, wg_last);
+        const int tok = min(k0 + key0 + lane / kPieces, wg_last);
+        const uint32_t f = __builtin_amdgcn_readfirstlane(lds_tbl[tok0 >> block_shift]);
+        const int64_t base = static_cast<int64_t>(f) * frame_bytes;
+        const uint32_t off = static_cast<uint32_t>(tok & (a.block_size - 1)) * row_bytes + lane_col;
+        pk[i] = load16(static_cast<const char*>(a.k_cache) + base + off);
+        pv[i] = load16(static_cast<const char*>(a.v_cache) + base + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int piece = threadIdx.x + i * kWaves * 64;
@@ -319,14 +342,8 @@ void prefill_kernel(PrefillArgs a) {
           for (int t = 0; t < 16; ++t) o[b][t] *= alpha;
         m = m_new;
       }
-      float psum = 0.f;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        x[t] = fast_exp2(__builtin_fmaf(x[t], a.scale_log2, -m));
-        psum += x[t];
-      }
-      psum = sum_halves(psum);
-      l += psum;
+      for (int t = 0; t < 16; ++t) x[t] = fast_exp2(__builtin_fmaf(x[t], a.scale_log2, -m));
 
       // P^T into the B-operand layout: for keys 16j .. 16j+15 the lower half
       // of the wavefront needs keys 16j + [0,8), the upper half 16j + [8,16);
@@ -336,22 +353,33 @@ void prefill_kernel(PrefillArgs a) {
       for (int g = 0; g < 16; g += 8)
 #pragma unroll
         for (int i = 0; i < 4; ++i) swap_halves(x[g + i], x[g + i + 4]);
-      // P = hi + lo per pair of weights: hi rounded to the element type, lo
-      // the rounded residual (x - hi is exact in fp32)
+      // bf16 keeps 8 significant bits: P = hi + lo per pair of weights, hi
+      // rounded to bf16 and lo the rounded residual (x - hi is exact in
+      // fp32), two MFMAs. fp16 keeps 11: one rounding, one MFMA, and l sums
+      // the rounded weights, so that O / l is a convex combination of the
+      // values with exactly the weights the matrix cores applied.
       vec p_hi[2], p_lo[2];
+      float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const f32x2 xv = {x[8 * j + e], x[8 * j + e + 1]};
           const auto hp = __builtin_convertvector(xv, typename M::pair);
-          const f32x2 hw = __builtin_convertvector(hp, f32x2);
-          const auto lp = __builtin_convertvector(f32x2{xv.x - hw.x, xv.y - hw.y}, typename M::pair);
           p_hi[j][e] = hp.x;
           p_hi[j][e + 1] = hp.y;
-          p_lo[j][e] = lp.x;
-          p_lo[j][e + 1] = lp.y;
+          if constexpr (kSplitP) {
+            const f32x2 hw = __builtin_convertvector(hp, f32x2);
+            const auto lp =
+                __builtin_convertvector(f32x2{xv.x - hw.x, xv.y - hw.y}, typename M::pair);
+            p_lo[j][e] = lp.x;
+            p_lo[j][e + 1] = lp.y;
+            psum += xv.x + xv.y;
+          } else {
+            psum = __builtin_amdgcn_fdot2(hp, typename M::pair{1, 1}, psum, false);
+          }
         }
+      l += sum_halves(psum);
       // O^T += V^T P^T. The V^T operand (8 consecutive keys per lane at one
       // head-dim element) comes from the row-major V tile through transposing
       // LDS reads: in each group of 16 lanes, a 64-bit transpose read hands
@@ -375,7 +403,7 @@ void prefill_kernel(PrefillArgs a) {
         const vec va = va_next;
         if (n + 1 < 2 * kDBlk) va_next = v_operand((n + 1) / 2, (n + 1) % 2);
         o[b] = M::run(va, p_hi[j], o[b]);
-        o[b] = M::run(va, p_lo[j], o[b]);
+        if constexpr (kSplitP) o[b] = M::run(va, p_lo[j], o[b]);
       }
     }
     if (kt + 1 < n_tiles) stage((kt + 1) & 1);

@@ -464,6 +464,51 @@ def test_prefill_narrow_output_within_one_ulp():
     assert _narrow_ok(out, ref, w.dtype)
 
 
+@pytest.mark.parametrize("dtype,D,B", [("f16", 128, 16), ("bf16", 128, 16), ("f16", 64, 8),
+                                       ("bf16", 64, 32)])
+def test_prefill_constant_values_reproduced(dtype, D, B):
+    """Every value row of head h equal to one vector c_h: each output is a
+    convex combination of identical rows, so it equals c_h whatever the
+    softmax weights are (a property of the definition, no oracle needed).
+    The bound (5e-5, fp32 accumulation over up to 700 keys) fails if l sums
+    other weights than the ones applied to the rows: a query that sees a
+    few keys would then be off by a rounding of its weights, up to 2^-11
+    (fp16) or 2^-9 (bf16) relative."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+
+    dev = torch.device("cuda:0")
+    tdt = V.torch_dtype(dtype)
+    gen = torch.Generator().manual_seed(1234 + D + B)
+    H = 4
+    ctx = np.array([1, 2, 3, 33, 300, 700], dtype=np.int32)
+    nblk = (ctx + B - 1) // B
+    mb = int(nblk.max())
+    NB = int(nblk.sum()) + 3
+    frames = torch.randperm(NB, generator=gen).numpy().astype(np.int32)
+    tables = np.full((len(ctx), mb), NB - 1, dtype=np.int32)
+    used = 0
+    for s, n in enumerate(nblk):
+        tables[s, :n] = frames[used:used + n]
+        used += n
+    k = torch.randn(NB, B, H, D, generator=gen).to(tdt).to(dev)
+    c = torch.randn(H, D, generator=gen).to(tdt)
+    v = c.reshape(1, 1, H, D).expand(NB, B, H, D).contiguous().to(dev)
+    qs = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    T = int(qs[-1])
+    q = torch.randn(T, H, D, generator=gen).to(tdt).to(dev)
+    out = torch.full((T, H, D), float("nan"), dtype=torch.float32, device=dev)
+    say(f"[gpu] prefill constant values: {dtype}, D {D}, block {B}, contexts {ctx.tolist()}")
+    pkv.paged_attn_prefill(q, k, v, torch.from_numpy(tables).to(dev), torch.from_numpy(ctx).to(dev),
+                           torch.from_numpy(qs).to(dev), B, D ** -0.5, out, int(ctx.max()),
+                           int(ctx.max()))
+    torch.cuda.synchronize()
+    err = float((out.cpu() - c.float().reshape(1, H, D)).abs().max())
+    say(f"  {T} queries, max-abs deviation from the value row {err:.3e}")
+    assert err <= 5e-5
+
+
 def test_prefix_cache_small_parity():
     """Prefix caching across rounds of requests: each round writes only the
     positions its requests do not reuse, prefills them through tables that
