@@ -236,7 +236,7 @@ def bench_prefill(args, w, pt, cache, dev):
     from paged_kv_cache_126_amd.driver import prefill_order
 
     order = None if args.prefill_batch_order else torch.from_numpy(
-        prefill_order(pt.context_lens, qs)).to(dev)
+        prefill_order(pt.context_lens, qs, max_q)).to(dev)
     # algorithmic work: 4 D flops per (query, visible key) per head
     n = np.asarray(w.query_lens, dtype=np.int64)
     ctx = pt.context_lens.astype(np.int64)
@@ -248,9 +248,9 @@ def bench_prefill(args, w, pt, cache, dev):
     flush_buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
 
-    def step(seq_order=order):
+    def step(work_order=order):
         pkv.paged_attn_prefill(q, cache.k, cache.v, bt, cl, qsd, w.B, w.scale, out, max_ctx, max_q,
-                               seq_order=seq_order)
+                               work_order=work_order)
 
     for _ in range(args.warmup):
         step()
@@ -270,7 +270,7 @@ def bench_prefill(args, w, pt, cache, dev):
         with pkv.kernel_timing(k0, k1):
             step()
     torch.cuda.synchronize()
-    # context: the same launches in batch order
+    # context: the same launches in the default order (sequence by sequence)
     batch_order_ms = None
     if order is not None:
         bevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -298,8 +298,10 @@ def bench_prefill(args, w, pt, cache, dev):
                    "sum_ctx": int(ctx.sum()), "visible_pairs": pairs, "flops": flops,
                    "cache_flush_between_steps": not args.no_flush},
         "us_per_step": round(ms * 1e3, 2),
-        "dispatch_order": "batch order" if order is None else "costliest sequence first (driver.prefill_order)",
-        "batch_order_us_per_step": None if batch_order_ms is None else round(batch_order_ms * 1e3, 2),
+        "dispatch_order": ("default (sequence by sequence)" if order is None else
+                           "costliest sequence first, its later query tiles first "
+                           "(driver.prefill_order)"),
+        "default_order_us_per_step": None if batch_order_ms is None else round(batch_order_ms * 1e3, 2),
         "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
@@ -353,7 +355,7 @@ def bench_prefix(args, w, dev):
                 qs=torch.from_numpy(rd.query_start).to(dev), max_ctx=int(ctx.max()),
                 max_q=int(n.max()), rows=len(wb.slots), flops=4 * w.D * w.H * pairs,
                 order=None if args.prefill_batch_order else
-                torch.from_numpy(prefill_order(rd.context_lens, rd.query_start)).to(dev)))
+                torch.from_numpy(prefill_order(rd.context_lens, rd.query_start, int(n.max()))).to(dev)))
         return rounds, mgr, cache, launches, (host_s, host_py_s)
 
     flush_buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
@@ -372,11 +374,11 @@ def bench_prefix(args, w, dev):
                     with pkv.kernel_timing(evs[i][3], evs[i][4]):  # the kernel's own start and end
                         pkv.paged_attn_prefill(L["q"], cache.k, cache.v, L["bt"], L["cl"], L["qs"],
                                                w.B, w.scale, L["out"], L["max_ctx"], L["max_q"],
-                                               seq_order=L["order"])
+                                               work_order=L["order"])
                 else:
                     pkv.paged_attn_prefill(L["q"], cache.k, cache.v, L["bt"], L["cl"], L["qs"], w.B,
                                            w.scale, L["out"], L["max_ctx"], L["max_q"],
-                                           seq_order=L["order"])
+                                           work_order=L["order"])
                 if evs:
                     evs[i][2].record()
 
@@ -484,7 +486,8 @@ def main():
                          "in id order (the sensitivity variant)")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--prefill-batch-order", action="store_true",
-                    help="dispatch prefill sequences in batch order (by default costliest first, "
+                    help="dispatch prefill work in the default order, sequence by sequence in "
+                         "batch order (by default the costliest sequences go first, "
                          "driver.prefill_order)")
     ap.add_argument("--decode-batch-order", action="store_true",
                     help="dispatch decode work in batch order (by default longest first: "

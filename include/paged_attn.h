@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum pa_dtype {
   PA_F32 = 0,
@@ -268,6 +268,9 @@ typedef struct pa_prefill_shape {
   pa_dtype out_dtype;          /* PA_F32 or kv_dtype */
 } pa_prefill_shape;
 
+/* Queries per prefill work item (one query tile of one sequence). */
+#define PA_PREFILL_TILE 128
+
 /*
  * paged_attn_prefill: causal multi-query attention over the paged cache.
  *
@@ -277,13 +280,19 @@ typedef struct pa_prefill_shape {
  *   block_tables, context_lens, k_cache, v_cache, block_size, scale: as for
  *                 paged_attn_decode
  *   out           [T, H, D] in out_dtype
- *   seq_order     NULL, or device int32 [S]: the order in which the
- *                 sequences' workgroups are dispatched, a permutation of
- *                 0 .. S-1 (values are clamped into that range; a sequence
- *                 missing from it gets no output). Sequences whose
- *                 workgroups see the most (query, key) pairs first make the
- *                 launch's tail shorter; prefill_order in the Python binding
- *                 computes that order. Outputs do not depend on it.
+ *   work_order    NULL, or device int32 [S * Tq] with
+ *                 Tq = ceil(max_query_len / PA_PREFILL_TILE): the order in
+ *                 which the launch's work items are dispatched, a
+ *                 permutation of 0 .. S*Tq-1. Item s * Tq + t is query tile t
+ *                 of sequence s: its queries t * PA_PREFILL_TILE ..
+ *                 (t+1) * PA_PREFILL_TILE - 1, counted from the sequence's
+ *                 first query (items past its last query do nothing). Values
+ *                 are clamped into range; an item missing from the order
+ *                 gets no output. NULL dispatches sequence by sequence, each
+ *                 sequence's later tiles first. Items that see the most keys
+ *                 first make the launch's tail shorter; prefill_order in the
+ *                 Python binding computes that order. Outputs do not depend
+ *                 on it.
  *
  * The n_s = query_start[s+1] - query_start[s] queries of sequence s are its
  * last n_s tokens, whose K and V are already in the cache: query r sits at
@@ -292,14 +301,16 @@ typedef struct pa_prefill_shape {
  * softmax_j(a_ij) v_j). n_s = ctx_s is a whole prompt, n_s < ctx_s a chunk of
  * one, n_s = 1 a decode step. Device-side preconditions: 0 <= n_s <= ctx_s and
  * n_s <= max_query_len (larger values are clamped). Scores and the output
- * accumulate in fp32 on the matrix cores; the softmax weights enter the
- * weighted sum of V as a 16-bit value plus its 16-bit residual.
+ * accumulate in fp32 on the matrix cores. The softmax weights enter the
+ * weighted sum of V as a bf16 value plus its bf16 residual (bf16 caches), or
+ * as one fp16 rounding that the normaliser also sums (fp16 caches).
+ * S * Tq * H must not exceed 2^31 - 1 (else PA_EINVAL).
  */
 pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, const int32_t* context_lens,
                              const int32_t* query_start, int32_t block_size, float scale,
                              void* out, const pa_prefill_shape* shape,
-                             const int32_t* seq_order, void* stream);
+                             const int32_t* work_order, void* stream);
 
 /*
  * paged_gather: block translation made visible, for checking it bit for bit.

@@ -5,12 +5,13 @@ frame pool and block tables that feed it.
 """
 from .block_manager import AppendResult, BlockPool, SeqManager
 from .block_manager import PrefixCachingSeqManager
-from .lib import (PagedAttnError, alloc_workspace, kernel_timing, kv_append,
+from .lib import (PA_MAX_GROUP, PA_PREFILL_TILE, PagedAttnError, alloc_workspace, kernel_timing,
+                  kv_append,
                   kv_copy_blocks, load, paged_attn_decode, paged_attn_decode_grouped,
                   paged_attn_prefill, paged_gather, partition_tokens, workspace_size)
 
 __all__ = [
-    "AppendResult", "BlockPool", "SeqManager", "PrefixCachingSeqManager", "PagedAttnError",
+    "PA_MAX_GROUP", "PA_PREFILL_TILE", "AppendResult", "BlockPool", "SeqManager", "PrefixCachingSeqManager", "PagedAttnError",
     "alloc_workspace", "kernel_timing", "kv_append", "kv_copy_blocks",
     "load", "paged_attn_decode", "paged_attn_decode_grouped", "paged_attn_prefill", "paged_gather",
     "partition_tokens", "workspace_size",

@@ -32,6 +32,7 @@ constexpr int64_t kTargetWorkgroupsOrdered = 1024;
 constexpr int64_t kMaxGridYZ = 65535;
 constexpr size_t kWorkspaceAlign = 256;
 static_assert(pa::kMaxGroup == PA_MAX_GROUP, "group size limit of the kernels and the header");
+static_assert(pa::kPrefillTile == PA_PREFILL_TILE, "prefill work items are query tiles");
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -289,7 +290,7 @@ pa_status paged_attn_decode(const void* q, const void* k_cache, const void* v_ca
 pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, const int32_t* context_lens,
                              const int32_t* query_start, int32_t block_size, float scale,
-                             void* out, const pa_prefill_shape* sh, const int32_t* seq_order,
+                             void* out, const pa_prefill_shape* sh, const int32_t* work_order,
                              void* stream) {
   if (!sh) return PA_EINVAL;
   if (sh->num_seqs < 0 || sh->num_heads <= 0 || sh->block_size <= 0 || sh->num_blocks <= 0 ||
@@ -305,14 +306,16 @@ pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_c
   if (static_cast<int64_t>(sh->block_size) * sh->num_heads * sh->head_dim * elem_bytes(sh->kv_dtype) >
       0x7FFFFFFFLL)
     return PA_EINVAL;
-  if (sh->num_seqs > kMaxGridYZ || sh->num_heads > kMaxGridYZ) return PA_EINVAL;
+  const int64_t query_tiles = (static_cast<int64_t>(sh->max_query_len) + PA_PREFILL_TILE - 1) /
+                              PA_PREFILL_TILE;
+  if (sh->num_seqs * query_tiles * sh->num_heads > 0x7FFFFFFFLL) return PA_EINVAL;
   if (sh->num_seqs == 0 || sh->max_query_len == 0 || sh->total_queries == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out)
     return PA_EINVAL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(out, static_cast<uintptr_t>(elem_bytes(sh->out_dtype))) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4) ||
-      !aligned(seq_order, 4))
+      !aligned(work_order, 4))
     return PA_EALIGN;
   pa::PrefillArgs a;
   a.q = q;
@@ -332,7 +335,7 @@ pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_c
   a.max_query_len = sh->max_query_len;
   a.total_queries = sh->total_queries;
   a.out_f32 = sh->out_dtype == PA_F32 ? 1 : 0;
-  a.seq_order = seq_order;
+  a.work_order = work_order;
   return from_hip(pa::launch_prefill(a, to_internal(sh->kv_dtype), sh->head_dim,
                                      static_cast<hipStream_t>(stream)));
 }

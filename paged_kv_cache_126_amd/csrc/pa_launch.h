@@ -84,8 +84,11 @@ struct PrefillArgs {
   int32_t max_query_len;
   int32_t total_queries;
   int32_t out_f32;
-  const int32_t* seq_order;    // [S] dispatch order of the sequences, or null
+  const int32_t* work_order;   // [S * query tiles] dispatch order of the work items, or null
 };
+
+// Queries per prefill work item (the prefill kernel's query tile).
+constexpr int kPrefillTile = 128;
 
 bool prefill_supported(Dtype dt, int head_dim);
 hipError_t launch_prefill(const PrefillArgs& a, Dtype dt, int head_dim, hipStream_t stream);

@@ -38,6 +38,7 @@ namespace {
 constexpr int kWaves = 4;                 // wavefronts per workgroup
 constexpr int kQW = 32;                   // queries per wavefront
 constexpr int kBM = kWaves * kQW;         // queries per workgroup
+static_assert(kBM == kPrefillTile, "a work item is one workgroup's query tile");
 constexpr int kBN = 32;                   // keys per tile
 constexpr float kNegBig = -1.0e30f;
 constexpr float kLazy = 8.0f;             // reference-maximum slack, log2 units
@@ -125,27 +126,33 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int kPadV = 16;
   constexpr bool kSplitP = std::is_same<T, BF16>::value;  // weights as hi + lo (see below)
 
-  // Work item of this workgroup. Workgroups go to the 8 XCDs round-robin by
-  // linear id, and each XCD has its own L2; the query tiles of one (head,
-  // sequence) read the same keys, so they are kept on one XCD, back to back.
-  // Within a (head, sequence), later query tiles see more keys (causal) and
-  // are dispatched first.
-  const int ntiles = static_cast<int>(gridDim.x);
-  const int ngroups = static_cast<int>(gridDim.y * gridDim.z);
-  int tile = blockIdx.x;
-  int group = blockIdx.y + gridDim.y * blockIdx.z;
-  if (ngroups % kXcds == 0) {
-    const int lin = tile + ntiles * group;
+  // Work item and head of this workgroup. Workgroups go to the 8 XCDs
+  // round-robin by linear id, and each XCD has its own L2. With H a
+  // multiple of 8, head h runs on XCD h % 8 for every item, so the query
+  // tiles of one (head, sequence), which read the same keys, share an L2;
+  // each XCD takes the items in dispatch order, its H / 8 heads of an item
+  // back to back.
+  const int ntiles = (a.max_query_len + kBM - 1) / kBM;
+  const int nitems = a.num_seqs * ntiles;
+  const int lin = static_cast<int>(blockIdx.x);
+  int item, h;
+  if (a.num_heads % kXcds == 0) {
+    const int per = a.num_heads / kXcds;
     const int idx = lin / kXcds;
-    group = (idx / ntiles) * kXcds + lin % kXcds;
-    tile = idx % ntiles;
+    item = idx / per;
+    h = lin % kXcds + kXcds * (idx % per);
+  } else {
+    item = lin / a.num_heads;
+    h = lin % a.num_heads;
   }
-  const int qt = ntiles - 1 - tile;
-  const int h = group % static_cast<int>(gridDim.y);
-  // Sequences are dispatched in seq_order (costliest first shortens the
-  // tail of the launch), else in batch order.
-  int s = group / static_cast<int>(gridDim.y);
-  if (a.seq_order != nullptr) s = min(max(a.seq_order[s], 0), a.num_seqs - 1);
+  // Items in work_order (longest first shortens the launch's tail), else
+  // sequence by sequence with a sequence's later query tiles, which see
+  // more keys, first.
+  const int code = a.work_order != nullptr
+                       ? min(max(a.work_order[item], 0), nitems - 1)
+                       : item + (ntiles - 1) - 2 * (item % ntiles);
+  const int s = code / ntiles;
+  const int qt = code % ntiles;
   int ctx = a.context_lens[s];
   ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
   int q0 = a.query_start[s];
@@ -428,7 +435,8 @@ void prefill_kernel(PrefillArgs a) {
 
 template <typename T, int D>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
-  dim3 grid((a.max_query_len + kBM - 1) / kBM, a.num_heads, a.num_seqs);
+  const int ntiles = (a.max_query_len + kBM - 1) / kBM;
+  dim3 grid(a.num_seqs * ntiles * a.num_heads);
   return launch_timed(prefill_kernel<T, D>, grid, dim3(kWaves * 64), stream, a);
 }
 

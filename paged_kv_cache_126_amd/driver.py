@@ -184,15 +184,27 @@ def group_order(group_start, group_shared, context_lens) -> np.ndarray:
     return np.argsort(-work, kind="stable").astype(np.int32)
 
 
-def prefill_order(context_lens, query_start) -> np.ndarray:
-    """Dispatch order for ``paged_attn_prefill``: sequences by the number of
-    (query, key) pairs their queries see, most first (a longest-first
-    schedule leaves the shortest work for the launch's tail). int32 [S]."""
+def prefill_order(context_lens, query_start, max_query_len=None) -> np.ndarray:
+    """Dispatch order for ``paged_attn_prefill``'s work items (query tile t
+    of sequence s is item s * Tq + t, Tq = ceil(max_query_len /
+    PA_PREFILL_TILE)): sequences by the number of (query, key) pairs their
+    queries see, most first, ties in batch order; within a sequence its
+    later tiles, which see more keys, first. A longest-first schedule leaves
+    the shortest work for the launch's tail, and a sequence's tiles stay
+    together, so the keys they share are still in cache when the next tile
+    reads them (measured: sorting all tiles by cost instead, across
+    sequences, was slower). ``max_query_len`` must be the value the call is
+    made with (default: the largest query count). int32 [S * Tq]."""
+    from .lib import PA_PREFILL_TILE
+
     ctx = np.asarray(context_lens, dtype=np.int64)
-    n = np.diff(np.asarray(query_start, dtype=np.int64))
-    n = np.clip(n, 0, ctx)
+    n = np.clip(np.diff(np.asarray(query_start, dtype=np.int64)), 0, ctx)
+    mq = int(n.max(initial=0)) if max_query_len is None else int(max_query_len)
+    n = np.minimum(n, mq)
+    tq = max(1, -(-mq // PA_PREFILL_TILE))
     pairs = n * (ctx - n) + n * (n + 1) // 2
-    return np.argsort(-pairs, kind="stable").astype(np.int32)
+    seqs = np.argsort(-pairs, kind="stable")
+    return (seqs[:, None] * tq + np.arange(tq - 1, -1, -1)[None, :]).reshape(-1).astype(np.int32)
 
 
 class DeviceCache:

@@ -24,6 +24,7 @@ EXPORTS = (
     "pa_stream_read", "paged_attn_decode_grouped",
 )
 PA_MAX_GROUP = 4
+PA_PREFILL_TILE = 128
 
 
 class PagedAttnError(RuntimeError):
@@ -272,11 +273,13 @@ def paged_attn_decode_grouped(q, k_cache, v_cache, block_tables, context_lens, b
 
 def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size: int,
                        scale: float, out, max_context_len: int, max_query_len: int,
-                       stream=None, seq_order=None) -> None:
+                       stream=None, work_order=None) -> None:
     """Causal attention of each sequence's last tokens into ``out`` [T, H, D];
-    see include/paged_attn.h. ``seq_order`` (int32 device [S], optional) is
-    the dispatch order of the sequences (``driver.prefill_order``)."""
-    _dense(q, k_cache, v_cache, block_tables, context_lens, query_start, out, seq_order)
+    see include/paged_attn.h. ``work_order`` (int32 device
+    [S * ceil(max_query_len / PA_PREFILL_TILE)], optional) is the dispatch
+    order of the work items, one per query tile of a sequence
+    (``driver.prefill_order``)."""
+    _dense(q, k_cache, v_cache, block_tables, context_lens, query_start, out, work_order)
     T, H, D = q.shape
     NB, B = k_cache.shape[0], k_cache.shape[1]
     S = context_lens.shape[0]
@@ -288,14 +291,16 @@ def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_st
         raise TypeError("query_start must be int32 [S + 1]")
     if str(block_tables.dtype) != "torch.int32" or str(context_lens.dtype) != "torch.int32":
         raise TypeError("block_tables and context_lens must be int32")
-    if seq_order is not None and (seq_order.shape != (S,) or str(seq_order.dtype) != "torch.int32"):
-        raise TypeError("seq_order must be int32 [S]")
+    items = S * ((int(max_query_len) + PA_PREFILL_TILE - 1) // PA_PREFILL_TILE)
+    if work_order is not None and (work_order.shape != (items,) or
+                                   str(work_order.dtype) != "torch.int32"):
+        raise TypeError(f"work_order must be int32 [{items}]")
     shape = PrefillShape(S, H, D, B, NB, block_tables.shape[1], int(max_context_len),
                          int(max_query_len), T, dtype_code(k_cache), dtype_code(out))
     _check("paged_attn_prefill", load().paged_attn_prefill(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         _ptr(query_start), int(block_size), float(scale), _ptr(out), ctypes.byref(shape),
-        _ptr(seq_order), _stream(stream)))
+        _ptr(work_order), _stream(stream)))
 
 
 def paged_gather(cache, block_tables, context_lens, out_row_start, out, max_context_len: int,

@@ -135,9 +135,9 @@ def run_gpu(w, partition_tokens: int = 0, out_dtype=None, phases: bool = False, 
 def run_gpu_prefill(w, out_dtype=None, order=None):
     """Play prefill workload ``w`` on cuda:0: write every token with kv_append,
     then one paged_attn_prefill over each sequence's last query_lens tokens.
-    ``order`` ("cost": driver.prefill_order; "random": a seeded permutation)
-    dispatches the sequences in that order, and checks that the output equals
-    the batch-order launch's bit for bit. Returns (AttendPoint, query_start,
+    ``order`` ("cost": driver.prefill_order; "random": a seeded permutation
+    of the work items) dispatches the query tiles in that order, and checks
+    that the output equals the default-order launch's bit for bit. Returns (AttendPoint, query_start,
     out cpu tensor [T, H, D])."""
     import torch
 
@@ -160,11 +160,13 @@ def run_gpu_prefill(w, out_dtype=None, order=None):
                 w.B, w.scale, out, int(pt.context_lens.max()), int(np.diff(qs).max()))
         pkv.paged_attn_prefill(*args)
         if order is not None:
-            seq_order = (prefill_order(pt.context_lens, qs) if order == "cost" else
-                         np.random.default_rng(w.seed).permutation(len(pt.context_lens)).astype(np.int32))
+            mq = int(np.diff(qs).max())
+            items = len(pt.context_lens) * -(-mq // pkv.PA_PREFILL_TILE)
+            work = (prefill_order(pt.context_lens, qs, mq) if order == "cost" else
+                    np.random.default_rng(w.seed).permutation(items).astype(np.int32))
             first = out.clone()
             out.fill_(float("nan"))
-            pkv.paged_attn_prefill(*args, seq_order=torch.from_numpy(seq_order).to(dev))
+            pkv.paged_attn_prefill(*args, work_order=torch.from_numpy(work).to(dev))
             torch.cuda.synchronize()
             assert torch.equal(out, first), f"dispatch order {order} changed the output"
         torch.cuda.synchronize()

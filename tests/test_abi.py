@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     for header in (HEADER, BLOCKS_HEADER):
         for name in declared_functions(header):
             assert hasattr(lib, name), name
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
 
 
 def test_status_strings():
@@ -204,6 +204,19 @@ def test_prefill_pointer_errors():
     assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, None, None, None) == -1
     empty = prefill_shape(total_queries=0)
     assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, ctypes.byref(empty), None, None) == 0
+    # a misaligned work order
+    assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, ctypes.byref(sh),
+                                  ctypes.c_void_p((1 << 20) + 2), None) == -2
+
+
+def test_prefill_launch_size_limit():
+    """S * ceil(max_query_len / PA_PREFILL_TILE) * H workgroups must fit a
+    one-dimensional grid (2^31 - 1)."""
+    lib = pkv.load()
+    p = ctypes.c_void_p(1 << 20)
+    big = prefill_shape(num_seqs=100000, num_heads=128, max_query_len=200 * L.PA_PREFILL_TILE,
+                        max_context_len=2048)
+    assert lib.paged_attn_prefill(p, p, p, p, p, p, 16, 0.088, p, ctypes.byref(big), None, None) == -1
 
 
 def test_stream_read_argument_errors():

@@ -94,8 +94,10 @@ def test_hand_example():
 
 
 def test_prefill_order_is_costliest_first():
-    """driver.prefill_order: a permutation of the batch, sequences by visible
-    (query, key) pairs, most first, ties in batch order."""
+    """driver.prefill_order: a permutation of the launch's work items (query
+    tile t of sequence s is item 3s + t here: the longest query count is 300,
+    three tiles of 128); sequences by visible (query, key) pairs, most first,
+    ties in batch order, and each sequence's tiles last to first."""
     from paged_kv_cache_126_amd.driver import prefill_order
 
     ctx = np.array([10, 300, 300, 0, 40, 1000], dtype=np.int32)
@@ -103,6 +105,9 @@ def test_prefill_order_is_costliest_first():
     order = prefill_order(ctx, qs)
     n = np.diff(qs).astype(np.int64)
     pairs = n * (ctx - n) + n * (n + 1) // 2   # 55, 599, 45150, 0, 820, 4006
-    assert sorted(order.tolist()) == list(range(6)) and order.dtype == np.int32
-    assert order.tolist() == [2, 5, 4, 1, 0, 3]
-    assert np.all(np.diff(pairs[order]) <= 0)
+    assert sorted(order.tolist()) == list(range(18)) and order.dtype == np.int32
+    # sequences 2, 5, 4, 1, 0, 3, each as tiles 2, 1, 0
+    assert order.tolist() == [8, 7, 6, 17, 16, 15, 14, 13, 12, 5, 4, 3, 2, 1, 0, 11, 10, 9]
+    assert np.all(np.diff(pairs[order // 3]) <= 0)
+    # the tile count follows the call's max_query_len
+    assert len(prefill_order(ctx, qs, max_query_len=512)) == 6 * 4
