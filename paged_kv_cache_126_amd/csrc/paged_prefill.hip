@@ -10,10 +10,12 @@
 // Memory Guide for LLM Inference", "The Mathematics of Block Translation").
 //
 // Work decomposition. One workgroup per (query tile of 128, head, sequence);
-// each of its 4 wavefronts owns 32 consecutive queries. The workgroup walks
-// the keys in tiles of 32: the tile's K and V rows are staged in LDS
-// row-major, double-buffered (the next tile is fetched into registers
-// meanwhile), then every wavefront
+// a (sequence, query tile) pair is a work item, dispatched in the caller's
+// order, and head h of every item runs on XCD h % 8. Each of the 4
+// wavefronts owns 32 consecutive queries. The workgroup walks the keys in
+// tiles of 32: the tile's K and V rows are staged in LDS row-major,
+// double-buffered (the next tile is fetched into registers meanwhile), then
+// every wavefront
 //   1. forms S^T = K Q^T (32 keys x 32 queries) with D/16 MFMA 32x32x16
 //      steps; Q^T stays in registers as the B operand, so each lane owns one
 //      query column and 16 of the tile's keys,
@@ -21,8 +23,10 @@
 //      lanes sharing a query exchange one value),
 //   3. accumulates O^T += V^T P^T with P^T moved from the accumulator layout
 //      into the B-operand layout by one exchange between the wavefront's
-//      halves. P is split into a bf16/fp16 high part and the residual (two
-//      MFMAs), which keeps ~16 significant bits of every softmax weight.
+//      halves. In bf16, P is split into a high part and the residual (two
+//      MFMAs), which keeps ~16 significant bits of every softmax weight; in
+//      fp16 one rounding keeps 11, and the normaliser sums the rounded
+//      weights.
 // Matrix layouts (verified on the device): for v_mfma_f32_32x32x16, A[i][k]
 // sits in lane i + 32 * (k / 8), element k % 8; B[k][j] in lane
 // j + 32 * (k / 8), element k % 8; D[i][j] in lane j + 32 * ((i / 4) % 2),
