@@ -1,8 +1,9 @@
 """GPU parity over the shapes the kernels accept beyond the named workloads:
 every decode head dimension, block sizes on the compiled fast paths and off
 them, each storage dtype, and prefill at both head dimensions with block
-sizes from 1 to 64, sequences with no queries, and a context whose block
-table is too long to stage in LDS (the direct table-read path).
+sizes from 1 to 64, sequences with no queries, a context whose block table
+is too long to stage in LDS (the direct table-read path), and head counts
+that take the head-per-XCD launch mapping.
 
 Each case is a small seeded workload (random context lengths, a permuted
 frame pool) written through the product block manager and kv_append, and
@@ -85,3 +86,20 @@ def test_prefill_shapes(dtype, D, B, ctx, qlens):
     err = max_err(out.numpy(), ref)
     say(f"  {int(qs[-1])} queries, max-abs err {err:.3e} (tol {TOL[dtype]})")
     assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,H,order", [("bf16", 8, "cost"), ("f16", 16, "random")])
+def test_prefill_heads_on_xcds(dtype, H, order):
+    """Head counts that are multiples of 8 take the launch mapping that pins
+    head h to XCD h mod 8; every output is compared with the oracle, in the
+    default order and in another dispatch order (bit for bit)."""
+    ctx, qlens = [700, 129, 400, 5], [512, 129, 1, 5]
+    w = shape_workload(dtype, 128, 16, ctx, H=H, query_lens=qlens, seed=12)
+    say(f"[gpu] prefill {w.description}, queries {qlens}, order {order}")
+    pt, qs, out = run_gpu_prefill(w, order=order)
+    snap, ref = oracle_prefill(w, pad_frame_for(w))
+    assert np.array_equal(pt.tables, snap.tables)
+    err = max_err(out.numpy(), ref)
+    say(f"  {int(qs[-1])} queries, max-abs err {err:.3e} (tol {TOL[dtype]})")
+    assert err <= TOL[dtype]
+
