@@ -1,8 +1,8 @@
 """Seeded random sweeps on the GPU against the fp64 oracle: decode over
 random dtypes, head dims, block sizes (on and off the compiled fast paths),
 head counts, batch sizes, context mixes (empty, single-token, block-aligned,
-long) and forced partition sizes; prefill over random chunk shapes and
-dispatch orders; grouped decode over random fork families. Every case is
+long) and forced partition sizes; prefill over random chunk shapes, head
+counts and dispatch orders; grouped decode over random fork families. Every case is
 compared element by element; grouped decode is also compared bit for bit
 with the ungrouped pass."""
 from __future__ import annotations
@@ -65,16 +65,18 @@ def test_decode_random_shapes(seed):
         assert err <= TOL[dtype]
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_prefill_random_shapes(seed):
     rng = np.random.default_rng(6000 + seed)
     dtype = ("bf16", "f16")[seed % 2]
     D = (64, 128)[(seed // 2) % 2]
     B = int(rng.choice(BLOCKS))
     S = int(rng.integers(1, 7))
+    # head counts on both launch mappings (multiples of 8: head h on XCD h mod 8)
+    H = (2, 8, 3, 16, 1, 8)[seed % 6]
     ctx = [int(c) for c in rng.integers(1, 700, size=S)]
     qlens = [int(rng.integers(0, c + 1)) if rng.random() < 0.7 else c for c in ctx]
-    w = shape_workload(dtype, D, B, ctx, H=2, query_lens=qlens, seed=80 + seed)
+    w = shape_workload(dtype, D, B, ctx, H=H, query_lens=qlens, seed=80 + seed)
     order = ("cost", "random", None)[seed % 3]
     say(f"[gpu] fuzz prefill seed {seed}: {w.description}, queries {qlens}, order {order}")
     pt, qs, out = run_gpu_prefill(w, order=order)
