@@ -11,7 +11,8 @@
 //
 // Work decomposition. One workgroup per (query tile of 128, head, sequence);
 // a (sequence, query tile) pair is a work item, dispatched in the caller's
-// order, and head h of every item runs on XCD h % 8. Each of the 4
+// order, and with H a multiple of 8 head h of every item runs on XCD h % 8.
+// Each of the 4
 // wavefronts owns 32 consecutive queries. The workgroup walks the keys in
 // tiles of 32: the tile's K and V rows are staged in LDS row-major,
 // double-buffered (the next tile is fetched into registers meanwhile), then
