@@ -256,10 +256,11 @@ def bench_prefill(args, w, pt, cache, dev):
         step()
     torch.cuda.synchronize()
     # Plain launches between stream events (the step time) alternate with
-    # launches that stamp the kernel's own start and end (its duration), so
-    # that both see the same clock and cache conditions.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for e0, e1, k0, k1 in evs:
+    # launches that stamp the kernel's own start and end (its duration) and,
+    # for context, plain launches in the default order, so that all three see
+    # the same clock and cache conditions.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for e0, e1, k0, k1, b0, b1 in evs:
         if not args.no_flush:
             torch.sum(flush_buf, dim=0, out=flush_sink)
         e0.record()
@@ -269,20 +270,16 @@ def bench_prefill(args, w, pt, cache, dev):
             torch.sum(flush_buf, dim=0, out=flush_sink)
         with pkv.kernel_timing(k0, k1):
             step()
-    torch.cuda.synchronize()
-    # context: the same launches in the default order (sequence by sequence)
-    batch_order_ms = None
-    if order is not None:
-        bevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(args.steps)]
-        for b0, b1 in bevs:
+        if order is not None:
             if not args.no_flush:
                 torch.sum(flush_buf, dim=0, out=flush_sink)
             b0.record()
             step(None)
             b1.record()
-        torch.cuda.synchronize()
-        batch_order_ms = float(np.mean([b0.elapsed_time(b1) for b0, b1 in bevs]))
+    torch.cuda.synchronize()
+    batch_order_ms = None
+    if order is not None:
+        batch_order_ms = float(np.mean([e[4].elapsed_time(e[5]) for e in evs]))
     ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     kms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     tflops = flops / (kms * 1e-3) / 1e12          # the kernel alone (roofline)

@@ -407,13 +407,14 @@ void prefill_kernel(PrefillArgs a) {
         const v4i16 hi4 = tr_read(&lds_v[kb + 4 + (c16 >> 2)][d0 + 4 * (c16 & 3)]);
         return M::from_bits(join(lo4, hi4));
       };
-      // the next V operand is read while the current one's two MFMAs run
+      // the next V operand is read while the current one's two MFMAs run;
+      // keys 0-15 of the tile for every output block first, then keys 16-31
       vec va_next = v_operand(0, 0);
 #pragma unroll
       for (int n = 0; n < 2 * kDBlk; ++n) {
-        const int b = n / 2, j = n % 2;
+        const int j = n / kDBlk, b = n % kDBlk;
         const vec va = va_next;
-        if (n + 1 < 2 * kDBlk) va_next = v_operand((n + 1) / 2, (n + 1) % 2);
+        if (n + 1 < 2 * kDBlk) va_next = v_operand((n + 1) % kDBlk, (n + 1) / kDBlk);
         o[b] = M::run(va, p_hi[j], o[b]);
         if constexpr (kSplitP) o[b] = M::run(va, p_lo[j], o[b]);
       }
