@@ -453,6 +453,36 @@ def test_prefill_full_size_sampled(cfg):
     assert err <= TOL[w.dtype]
 
 
+def test_binding_rejects_malformed_orders():
+    """The binding checks an order's dtype and length before anything is
+    launched: a prefill work order must be int32 [S * ceil(max_query_len /
+    PA_PREFILL_TILE)], a decode dispatch order a 1-D int32 tensor."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+
+    dev = torch.device("cuda:0")
+    S, H, D, B, NB, mq = 3, 2, 128, 16, 8, 200
+    q = torch.zeros((S * mq, H, D), dtype=torch.bfloat16, device=dev)
+    k = torch.zeros((NB, B, H, D), dtype=torch.bfloat16, device=dev)
+    bt = torch.zeros((S, 16), dtype=torch.int32, device=dev)
+    cl = torch.full((S,), mq, dtype=torch.int32, device=dev)
+    qs = torch.arange(0, (S + 1) * mq, mq, dtype=torch.int32, device=dev)
+    out = torch.zeros((S * mq, H, D), dtype=torch.float32, device=dev)
+    items = S * -(-mq // pkv.PA_PREFILL_TILE)
+    args = (q, k, k, bt, cl, qs, B, 0.088, out, mq, mq)
+    with pytest.raises(TypeError):
+        pkv.paged_attn_prefill(*args, work_order=torch.arange(S, dtype=torch.int32, device=dev))
+    with pytest.raises(TypeError):
+        pkv.paged_attn_prefill(*args, work_order=torch.arange(items, dtype=torch.int64, device=dev))
+    qd = torch.zeros((S, H, D), dtype=torch.bfloat16, device=dev)
+    od = torch.zeros((S, H, D), dtype=torch.float32, device=dev)
+    with pytest.raises(TypeError):
+        pkv.paged_attn_decode(qd, k, k, bt, cl, B, 0.088, od, mq,
+                              dispatch_order=torch.arange(S, dtype=torch.int64, device=dev))
+    torch.cuda.synchronize()
+
+
 def test_prefill_narrow_output_within_one_ulp():
     """Prefill with a bf16 output: the fp32 result rounded to nearest even."""
     import torch
