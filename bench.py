@@ -11,6 +11,15 @@ with HIP events on the stream the kernels run on. Prints one JSON line.
 Inputs are synthetic and seeded (see workloads/): context lengths uniform in
 [1, 2048], frames drawn from a randomly permuted pool of 20,000, q/k/v
 standard-normal values rounded to bf16.
+
+Other workloads (--workload N): 1 the worked example, 3 eight 32k-token
+sequences, 4 forks of shared prompts (through paged_attn_decode_grouped
+unless --ungrouped), 5 batch 256 with the step's kv_append (--permuted-pool
+for its pool-order variant); 6 and 7 paged prefill (a 512-token chunk after
+a cached prefix, whole prompts); 8 prefix-cached prefill rounds, with and
+without caching. Decode and prefill dispatch their longest work first unless
+--decode-batch-order / --prefill-batch-order. --gpus N > 1 exits: the
+library runs on one GPU.
 """
 from __future__ import annotations
 
