@@ -213,6 +213,47 @@ def test_kv_append_bit_exact_with_cow():
         assert np.array_equal(cache.v.view(tview).cpu().numpy(), v.view(view))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_kv_append_skips_padding_and_out_of_range_slots(dtype):
+    """Tokens whose slot is negative (padding) or past the pool's last slot
+    write nothing; the rest land bit for bit where the oracle's scatter puts
+    them, and every other slot keeps its previous bytes (the oracle is given
+    the out-of-range slots as padding, the rule the library documents)."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+    from oracle.oracle import default
+
+    rng = np.random.default_rng(90)
+    NB, B, H, D, N = 9, 4, 2, 64, 24
+    slots = np.empty(N, dtype=np.int64)
+    slots[:20] = rng.permutation(NB * B)[:20]
+    slots[20:] = [-1, -7, NB * B, NB * B + 1000]
+    slots = slots[rng.permutation(N)]
+    kn = V.draw_np(90, V.STREAM_K, np.arange(N), H, D, dtype)
+    vn = V.draw_np(90, V.STREAM_V, np.arange(N), H, D, dtype)
+    base_k = V.draw_np(91, V.STREAM_K, np.arange(NB * B), H, D, dtype).reshape(NB, B, H, D)
+    base_v = V.draw_np(91, V.STREAM_V, np.arange(NB * B), H, D, dtype).reshape(NB, B, H, D)
+    ref_k, ref_v = base_k.copy(), base_v.copy()
+    default().kv_append(kn, vn, np.where(slots < NB * B, slots, -1), ref_k, ref_v, B, dtype)
+
+    view = np.int32 if dtype == "f32" else np.int16
+    tview = torch.int32 if dtype == "f32" else torch.int16
+    tdt = V.torch_dtype(dtype)
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(view)).to(dev).view(tdt)
+
+    k, v = to_dev(base_k), to_dev(base_v)
+    say(f"[gpu] kv_append with padding and out-of-range slots, {dtype}: {slots.tolist()}")
+    pkv.kv_append(to_dev(kn), to_dev(vn), torch.from_numpy(slots).to(dev), k, v)
+    torch.cuda.synchronize()
+    assert np.array_equal(k.view(tview).cpu().numpy(), ref_k.view(view))
+    assert np.array_equal(v.view(tview).cpu().numpy(), ref_v.view(view))
+    assert not np.array_equal(ref_k.view(view), base_k.view(view))  # something was written
+
+
 def test_gather_bit_exact():
     """Block translation: the device gather of every sequence's rows in logical
     order equals the oracle's gather, bit for bit."""
