@@ -457,9 +457,31 @@ __global__ __launch_bounds__(kNW * 64) void decode_group_kernel(DecodeArgs a, Gr
 }
 
 // Log-sum-exp merge of a sequence's partitions: with M = max_p m_p,
-// out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p. The workgroup
+// reduces the partitions' maxima and normalisers in parallel; for the
+// weighted sum its wavefronts take every kMergeWaves-th partition and add
+// their parts in LDS. The order of every sum is fixed by the launch shape,
+// so results repeat bit for bit.
+constexpr int kMergeWaves = 2;
+constexpr int kMergeChunk = 1024;  // partitions whose weights sit in LDS at a time
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int kEPL = (D + 63) / 64;  // output elements per lane
+  __shared__ float red_max[kMergeWaves], red_sum[kMergeWaves];
+  __shared__ float weights[kMergeChunk];
+  __shared__ float parts[kMergeWaves][D];
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   int ctx = a.context_lens[s];
@@ -467,27 +489,69 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   int n_parts = ctx <= a.part_tokens ? 1 : (ctx + a.part_tokens - 1) / a.part_tokens;
   if (n_parts <= 1) return;  // written by the partition pass
   n_parts = min(n_parts, a.max_parts);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int64_t sh = static_cast<int64_t>(s) * a.num_heads + h;
   const float* ml = a.ws_ml + 2 * sh * a.max_parts;
   const float* pacc = a.ws_acc + sh * a.max_parts * D;
-  float M = kNegBig;
-  for (int p = 0; p < n_parts; ++p) M = fmaxf(M, ml[2 * p]);
-  for (int e = threadIdx.x; e < D; e += blockDim.x) {
-    float L = 0.f, O = 0.f;
-    for (int p = 0; p < n_parts; ++p) {
-      const float f = fast_exp2(ml[2 * p] - M);
-      L += ml[2 * p + 1] * f;
-      O += pacc[static_cast<int64_t>(p) * D + e] * f;
+
+  float mx = kNegBig;
+  for (int p = tid; p < n_parts; p += kMergeWaves * 64) mx = fmaxf(mx, ml[2 * p]);
+  mx = wave_max(mx);
+  if (lane == 0) red_max[wave] = mx;
+  __syncthreads();
+  float M = red_max[0];
+#pragma unroll
+  for (int w = 1; w < kMergeWaves; ++w) M = fmaxf(M, red_max[w]);
+
+  float L = 0.f;
+  float O[kEPL];
+#pragma unroll
+  for (int k = 0; k < kEPL; ++k) O[k] = 0.f;
+  for (int c0 = 0; c0 < n_parts; c0 += kMergeChunk) {
+    const int cn = min(kMergeChunk, n_parts - c0);
+    __syncthreads();  // the previous chunk's weights are no longer read
+    for (int p = tid; p < cn; p += kMergeWaves * 64) {
+      const float f = fast_exp2(ml[2 * (c0 + p)] - M);
+      weights[p] = f;
+      L += ml[2 * (c0 + p) + 1] * f;
     }
-    const float r = L > 0.f ? O / L : 0.f;
-    const int64_t o = sh * D + e;
+    __syncthreads();
+    for (int p = wave; p < cn; p += kMergeWaves) {
+      const float f = weights[p];
+      const float* row = pacc + static_cast<int64_t>(c0 + p) * D;
+#pragma unroll
+      for (int k = 0; k < kEPL; ++k) {
+        const int e = lane + 64 * k;
+        if (e < D) O[k] = __builtin_fmaf(row[e], f, O[k]);
+      }
+    }
+  }
+  L = wave_sum(L);
+  if (lane == 0) red_sum[wave] = L;
+#pragma unroll
+  for (int k = 0; k < kEPL; ++k) {
+    const int e = lane + 64 * k;
+    if (e < D) parts[wave][e] = O[k];
+  }
+  __syncthreads();
+  float Lt = red_sum[0];
+#pragma unroll
+  for (int w = 1; w < kMergeWaves; ++w) Lt += red_sum[w];
+  for (int e = tid; e < D; e += kMergeWaves * 64) {
+    float o = parts[0][e];
+#pragma unroll
+    for (int w = 1; w < kMergeWaves; ++w) o += parts[w][e];
+    const float r = Lt > 0.f ? o / Lt : 0.f;
+    const int64_t oi = sh * D + e;
     if constexpr (T::kBytes == 4) {
-      static_cast<float*>(a.out)[o] = r;
+      static_cast<float*>(a.out)[oi] = r;
     } else {
       if (a.out_f32)
-        static_cast<float*>(a.out)[o] = r;
+        static_cast<float*>(a.out)[oi] = r;
       else
-        static_cast<uint16_t*>(a.out)[o] = static_cast<uint16_t>(narrow_bits(T{}, r));
+        static_cast<uint16_t*>(a.out)[oi] = static_cast<uint16_t>(narrow_bits(T{}, r));
     }
   }
 }
@@ -548,8 +612,7 @@ hipError_t dispatch_dim(const DecodeArgs& a, const GroupArgs* g, int head_dim,
 template <typename T, int D>
 hipError_t launch_merge_t(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.num_heads, a.num_seqs);
-  const int threads = D < 64 ? 64 : (D > 256 ? 256 : D);
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), grid, dim3(threads), 0, stream, a);
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), grid, dim3(kMergeWaves * 64), 0, stream, a);
   return hipGetLastError();
 }
 
