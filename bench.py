@@ -757,13 +757,17 @@ def main():
     part_ms = np.array([e[part_start].elapsed_time(e[1]) for e in pevs])
     kern_ms = np.array([e[4].elapsed_time(e[5]) for e in kevs])  # kernel alone, no dispatch gap
     merge_ms = np.array([e[1].elapsed_time(e[2]) for e in pevs])
+    # the library queues no merge when no sequence spans two partitions (no
+    # workspace); the events around that call then time only themselves
+    merge_launched = ws is not None
     step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
     ms = float(step_ms.mean())
     log(f"[bench] {args.steps} steps: step {ms * 1e3:.1f} us (median {np.median(step_ms) * 1e3:.1f}), "
         + (f"grouped call {part_ms.mean() * 1e3:.1f} us (grouped partition kernel alone "
            f"{kern_ms.mean() * 1e3:.1f})" if grouped else
            f"partition kernel {part_ms.mean() * 1e3:.1f} us (kernel alone {kern_ms.mean() * 1e3:.1f}), "
-           f"merge {merge_ms.mean() * 1e3:.1f} us")
+           + (f"merge {merge_ms.mean() * 1e3:.1f} us" if merge_launched else
+              "no merge launch (no sequence spans two partitions)"))
         + (f", kv_append {append_ms.mean() * 1e3:.1f} us" if append_args else ""))
 
     # Streaming-read ceiling: the same non-temporal 16-byte loads over a
@@ -872,7 +876,9 @@ def main():
         "batch_order": batch_order_ctx,
         "kernels_us": {"partition": round(float(part_ms.mean()) * 1e3, 2),
                        "partition_kernel_alone": round(float(kern_ms.mean()) * 1e3, 2),
-                       "merge": None if grouped else round(float(merge_ms.mean()) * 1e3, 2),
+                       "merge": (None if grouped or not merge_launched
+                                 else round(float(merge_ms.mean()) * 1e3, 2)),
+                       "merge_launched": (not grouped) and merge_launched,
                        "kv_append": round(float(append_ms.mean()) * 1e3, 2) if append_args else None,
                        "what": ("partition = the grouped call (both passes) between stream events; "
                                 "partition_kernel_alone = the grouped partition kernel's own stamps"
