@@ -179,6 +179,10 @@ void prefill_kernel(PrefillArgs a) {
   const int wg_last = first + min(n, (qt + 1) * kBM) - 1;   // last position in the workgroup
   const int wave_first = first + qt * kBM + wave * kQW;     // first position of the wavefront
   const int wave_last = first + min(n, qt * kBM + (wave + 1) * kQW) - 1;
+  // A wavefront past the tile's last query (short query runs) still loads
+  // and stages its share of every K/V tile, but computes nothing, leaving
+  // its SIMD to the wavefronts of other workgroups.
+  const bool wave_live = qt * kBM + wave * kQW < n;
 
   const int64_t head_bytes = static_cast<int64_t>(h) * D * T::kBytes;
   const uint32_t row_bytes = static_cast<uint32_t>(a.num_heads) * D * T::kBytes;
@@ -306,7 +310,7 @@ void prefill_kernel(PrefillArgs a) {
     auto& lds_k = lds_kb[kt & 1];
     auto& lds_v = lds_vb[kt & 1];
 
-    if (k0 <= wave_last) {  // the tile holds keys some query of this wavefront sees
+    if (wave_live && k0 <= wave_last) {  // the tile holds keys some query of this wavefront sees
       // S^T = K Q^T: rows = keys of the tile, columns = this wavefront's queries
       f32x16 st;
 #pragma unroll
