@@ -103,3 +103,22 @@ def test_prefill_heads_on_xcds(dtype, H, order):
     say(f"  {int(qs[-1])} queries, max-abs err {err:.3e} (tol {TOL[dtype]})")
     assert err <= TOL[dtype]
 
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_prefill_idle_wavefronts(dtype):
+    """Query counts on each side of the 32-query wavefront and 128-query tile
+    boundaries: in the last tile of such a sequence the wavefronts past its
+    last query compute nothing, yet still stage K/V for the others; every
+    output is compared with the oracle, also in a random dispatch order."""
+    qlens = [1, 31, 32, 33, 64, 95, 96, 97, 127, 128, 129, 161]
+    ctx = [q + e for q, e in zip(qlens, [0, 300, 17, 0, 129, 64, 1, 250, 0, 33, 400, 2])]
+    w = shape_workload(dtype, 128, 16, ctx, H=8, query_lens=qlens, seed=14)
+    say(f"[gpu] prefill {w.description}, queries {qlens}")
+    pt, qs, out = run_gpu_prefill(w, order="random")
+    snap, ref = oracle_prefill(w, pad_frame_for(w))
+    assert np.array_equal(pt.tables, snap.tables)
+    assert int(qs[-1]) == sum(qlens)
+    err = max_err(out.numpy(), ref)
+    say(f"  {int(qs[-1])} queries, max-abs err {err:.3e} (tol {TOL[dtype]})")
+    assert err <= TOL[dtype]
