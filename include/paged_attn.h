@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 typedef enum pa_dtype {
   PA_F32 = 0,
@@ -198,6 +198,35 @@ pa_status paged_attn_decode(const void* q, const void* k_cache, const void* v_ca
                             int32_t block_size, float scale, void* out,
                             const pa_decode_shape* shape, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_decode_noalloc: paged_attn_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments and results as
+ * paged_attn_decode (bit for bit, at the same shape), without the
+ * workspace: the partition partials go to a fixed scratch array of
+ * PA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on,
+ * from the first call on that GPU (which looks up the array's device
+ * address) until the process ends. The call allocates nothing.
+ *
+ *   The scratch of the device current on the calling thread is used;
+ *   `stream` must belong to that device.
+ *   Errors: as paged_attn_decode, plus PA_EWORKSPACE when the shape needs more
+ *   partial results than the scratch holds (paged_attn_workspace_size(shape)
+ *   > PA_NOALLOC_SCRATCH_BYTES; a larger partition_tokens needs fewer), and
+ *   PA_EHIP when the scratch's device address cannot be obtained. Both are
+ *   detected before anything is queued.
+ *   Every call on one GPU shares that GPU's scratch, which keeps the last
+ *   call's contents: calls whose work overlaps in time on one GPU (other
+ *   streams, other threads) race and give undefined results; calls queued
+ *   in order on one stream are safe. Nothing in the scratch needs clearing:
+ *   the partition pass writes every partial the merge pass reads.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+pa_status paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    int32_t block_size, float scale, void* out,
+                                    const pa_decode_shape* shape, void* stream);
 
 /*
  * The two launches of paged_attn_decode, exposed separately (same arguments

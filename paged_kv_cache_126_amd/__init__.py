@@ -8,11 +8,12 @@ from .block_manager import PrefixCachingSeqManager
 from .lib import (PA_MAX_GROUP, PA_PREFILL_TILE, PagedAttnError, alloc_workspace, kernel_timing,
                   kv_append,
                   kv_copy_blocks, load, paged_attn_decode, paged_attn_decode_grouped,
+                  paged_attn_decode_noalloc,
                   paged_attn_prefill, paged_gather, partition_tokens, workspace_size)
 
 __all__ = [
     "PA_MAX_GROUP", "PA_PREFILL_TILE", "AppendResult", "BlockPool", "SeqManager", "PrefixCachingSeqManager", "PagedAttnError",
     "alloc_workspace", "kernel_timing", "kv_append", "kv_copy_blocks",
-    "load", "paged_attn_decode", "paged_attn_decode_grouped", "paged_attn_prefill", "paged_gather",
+    "load", "paged_attn_decode", "paged_attn_decode_grouped", "paged_attn_decode_noalloc", "paged_attn_prefill", "paged_gather",
     "partition_tokens", "workspace_size",
 ]

@@ -3,6 +3,7 @@
 // happens before anything is queued; nothing here synchronises the device.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "paged_attn.h"
 #include "pa_launch.h"
@@ -101,11 +102,25 @@ size_t workspace_bytes_for(const pa_decode_shape* sh, int32_t max_parts) {
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_EHIP; }
 
-// Shared validation and argument packing of the decode entry points.
+// Points the partial-result arrays of `a` into `workspace` (a buffer of at
+// least workspace_bytes_for(sh, a->max_parts) bytes), or at nothing when no
+// sequence is split.
+void set_workspace(const pa_decode_shape* sh, void* workspace, pa::DecodeArgs* a) {
+  const bool split = workspace_bytes_for(sh, a->max_parts) > 0;
+  a->ws_ml = split ? static_cast<float*>(workspace) : nullptr;
+  a->ws_acc = split ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                               ml_bytes(sh, a->max_parts))
+                    : nullptr;
+}
+
+// Shared validation and argument packing of the decode entry points. With
+// check_workspace false the workspace arguments are ignored and the
+// partial-result pointers are left for the caller to set.
 pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* context_lens,
                          int32_t block_size, float scale, void* out, const pa_decode_shape* sh,
-                         void* workspace, size_t workspace_bytes, pa::DecodeArgs* a) {
+                         void* workspace, size_t workspace_bytes, pa::DecodeArgs* a,
+                         bool check_workspace = true) {
   int32_t pt = 0, parts = 0;
   pa_status st = check_shape(sh, &pt, &parts);
   if (st != PA_OK) return st;
@@ -116,7 +131,8 @@ pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache
       !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(sh->dispatch_order, 4))
     return PA_EALIGN;
   const size_t need = workspace_bytes_for(sh, parts);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, kWorkspaceAlign)))
+  if (check_workspace && need > 0 &&
+      (!workspace || workspace_bytes < need || !aligned(workspace, kWorkspaceAlign)))
     return PA_EWORKSPACE;
   a->q = q;
   a->k_cache = k_cache;
@@ -124,9 +140,6 @@ pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache
   a->block_tables = block_tables;
   a->context_lens = context_lens;
   a->out = out;
-  a->ws_ml = need ? static_cast<float*>(workspace) : nullptr;
-  a->ws_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ml_bytes(sh, parts))
-                   : nullptr;
   a->num_blocks = sh->num_blocks;
   a->scale_log2 = scale * 1.4426950408889634f;  // log2(e)
   a->num_seqs = sh->num_seqs;
@@ -139,6 +152,34 @@ pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache
   a->out_f32 = sh->out_dtype == PA_F32 ? 1 : 0;
   a->stream_loads = sh->cache_policy == PA_CACHE_STREAM ? 1 : 0;
   a->seq_order = sh->dispatch_order;
+  set_workspace(sh, check_workspace ? workspace : nullptr, a);
+  return PA_OK;
+}
+
+// Scratch of paged_attn_decode_noalloc: the partition partials of one call,
+// in a fixed device array instead of a caller's workspace. Each GPU the
+// library runs on holds its own copy of the array, at its own address, until
+// the process ends. In host code `scratch` names a host-side stand-in, not
+// device memory: host code uses only the device address obtained below.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the calling thread's current device, looked
+// up once per device (with that device current) and kept.
+pa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PA_EHIP;
+    if (!aligned(p, kWorkspaceAlign)) return PA_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return PA_OK;
 }
 
@@ -151,7 +192,9 @@ const char* pa_status_string(pa_status status) {
     case PA_OK: return "PA_OK";
     case PA_EINVAL: return "PA_EINVAL: invalid argument or unsupported shape/dtype";
     case PA_EALIGN: return "PA_EALIGN: misaligned pointer";
-    case PA_EWORKSPACE: return "PA_EWORKSPACE: workspace missing or too small";
+    case PA_EWORKSPACE:
+      return "PA_EWORKSPACE: workspace missing or too small (paged_attn_decode_noalloc: the "
+             "shape needs more than PA_NOALLOC_SCRATCH_BYTES of partial results)";
     case PA_EHIP: return "PA_EHIP: HIP launch error";
   }
   return "unknown pa_status";
@@ -285,6 +328,30 @@ pa_status paged_attn_decode(const void* q, const void* k_cache, const void* v_ca
                                               workspace_bytes, stream);
   if (st != PA_OK) return st;
   return paged_attn_merge(context_lens, out, shape, workspace, workspace_bytes, stream);
+}
+
+pa_status paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    int32_t block_size, float scale, void* out,
+                                    const pa_decode_shape* shape, void* stream) {
+  pa::DecodeArgs a;
+  pa_status st = prepare_decode(q, k_cache, v_cache, block_tables, context_lens, block_size,
+                                scale, out, shape, nullptr, 0, &a, /*check_workspace=*/false);
+  if (st != PA_OK) return st;
+  const size_t need = workspace_bytes_for(shape, a.max_parts);
+  if (need > PA_NOALLOC_SCRATCH_BYTES) return PA_EWORKSPACE;
+  if (shape->num_seqs == 0) return PA_OK;
+  if (need > 0) {
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != PA_OK) return st;
+    set_workspace(shape, ws, &a);
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const pa::Dtype dt = to_internal(shape->kv_dtype);
+  st = from_hip(pa::launch_decode_partitions(a, dt, shape->head_dim, s));
+  if (st != PA_OK || need == 0) return st;
+  return from_hip(pa::launch_decode_merge(a, dt, shape->head_dim, s));
 }
 
 pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,

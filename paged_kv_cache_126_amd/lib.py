@@ -21,8 +21,9 @@ EXPORTS = (
     "pa_status_string", "pa_abi_version", "kv_append", "kv_copy_blocks", "paged_attn_workspace_size",
     "paged_attn_partition_tokens", "paged_attn_decode", "paged_attn_decode_partitions",
     "paged_attn_merge", "paged_attn_prefill", "paged_gather", "pa_set_launch_events",
-    "pa_stream_read", "paged_attn_decode_grouped",
+    "pa_stream_read", "paged_attn_decode_grouped", "paged_attn_decode_noalloc",
 )
+PA_NOALLOC_SCRATCH_BYTES = 64 << 20
 PA_MAX_GROUP = 4
 PA_PREFILL_TILE = 128
 
@@ -95,6 +96,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("paged_attn_decode", "paged_attn_decode_partitions"):
         getattr(lib, name).argtypes = dec
         getattr(lib, name).restype = ctypes.c_int
+    lib.paged_attn_decode_noalloc.argtypes = [P, P, P, P, P, I32, F, P, SH, P]
+    lib.paged_attn_decode_noalloc.restype = ctypes.c_int
     lib.paged_attn_decode_grouped.argtypes = [P, P, P, P, P, I32, F, P, SH, P, P, I32, P, SZ, P]
     lib.paged_attn_decode_grouped.restype = ctypes.c_int
     lib.paged_attn_merge.argtypes = [P, P, SH, P, SZ, P]
@@ -245,6 +248,22 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_siz
     _check(fn, getattr(lib, fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                 _ptr(context_lens), int(block_size), float(scale), _ptr(out),
                                 ctypes.byref(shape), _ptr(workspace), ws_bytes, st))
+
+
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, block_size: int,
+                              scale: float, out, max_context_len: int, partition_tokens: int = 0,
+                              stream=None, cache_policy: int = PA_CACHE_STREAM,
+                              dispatch_order=None) -> None:
+    """``paged_attn_decode`` without a workspace: partial results go to the
+    library's fixed per-GPU scratch (see include/paged_attn.h). Calls that
+    overlap in time on one GPU race."""
+    _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out)
+    shape = make_shape(q, k_cache, block_tables, max_context_len, dtype_code(out), partition_tokens,
+                       cache_policy, dispatch_order)
+    _check("paged_attn_decode_noalloc",
+           load().paged_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                            _ptr(context_lens), int(block_size), float(scale),
+                                            _ptr(out), ctypes.byref(shape), _stream(stream)))
 
 
 def paged_attn_decode_grouped(q, k_cache, v_cache, block_tables, context_lens, block_size: int,

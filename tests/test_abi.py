@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     for header in (HEADER, BLOCKS_HEADER):
         for name in declared_functions(header):
             assert hasattr(lib, name), name
-    assert lib.pa_abi_version() == 3
+    assert lib.pa_abi_version() == 4
 
 
 def test_status_strings():
@@ -115,6 +115,36 @@ def test_decode_argument_errors():
     assert lib.paged_attn_decode(*args(wsb=16)) == -3
     assert lib.paged_attn_decode(*args(ws=ctypes.c_void_p((1 << 20) + 16))) == -3
     assert lib.paged_attn_decode(None, p, p, p, p, 16, 0.1, p, None, p, 0, None) == -1
+
+
+def test_noalloc_argument_errors():
+    """paged_attn_decode_noalloc validates like paged_attn_decode and rejects
+    shapes whose partial results exceed its fixed scratch, all before any
+    device call."""
+    lib = pkv.load()
+    p = ctypes.c_void_p(1 << 20)
+
+    def call(sh, **o):
+        return lib.paged_attn_decode_noalloc(o.get("q", p), p, p, p, p, o.get("B", sh.block_size),
+                                             o.get("scale", 0.088), p, ctypes.byref(sh), None)
+
+    sh = shape()
+    assert call(sh, q=None) == -1
+    assert call(sh, B=32) == -1
+    assert call(sh, scale=float("inf")) == -1
+    assert call(sh, q=ctypes.c_void_p((1 << 20) + 8)) == -2
+    assert call(shape(head_dim=96)) == -1
+    assert lib.paged_attn_decode_noalloc(p, p, p, p, p, 16, 0.1, p, None, None) == -1
+    # 256 x 64 pairs x 64 partitions of (128 + 2) floats: about 545 MB of partials
+    big = shape(num_seqs=256, num_heads=64, max_context_len=32768, max_blocks_per_seq=2048,
+                partition_tokens=512)
+    assert pkv.workspace_size(big) > L.PA_NOALLOC_SCRATCH_BYTES
+    assert call(big) == -3
+    msg = lib.pa_status_string(-3).decode()
+    assert "PA_NOALLOC_SCRATCH_BYTES" in msg
+    # the same batch with one partition per sequence needs no scratch; an
+    # empty batch queues nothing
+    assert call(shape(num_seqs=0)) == 0
 
 
 def test_partition_size_with_a_dispatch_order():
