@@ -206,7 +206,7 @@ def cpu_baseline(w, tables, ctx, budget_s: float = 12.0):
     orc = default()
     rng = np.random.default_rng(12345)
     sample = np.sort(rng.choice(w.num_seqs, size=min(16, w.num_seqs), replace=False))
-    snaps, _, _ = obm.replay(w)
+    snaps, _ = obm.replay(w)
     snap = snaps[-1]
     sub_ctx = snap.context_lens[sample]
     k, v, tab = _compact_caches(w, snap.tables[sample], sub_ctx, snap.slot_ident)
@@ -337,10 +337,7 @@ def bench_prefix(args, w, dev):
     def prepare(caching):
         pool = None if caching else w.frames_without_caching
         t0 = time.perf_counter()
-        plan_prefix_rounds(w, caching, pool_frames=pool, native=False)  # Python manager, for reference
-        host_py_s = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        rounds, mgr = plan_prefix_rounds(w, caching, pool_frames=pool)   # C++ manager
+        rounds, mgr = plan_prefix_rounds(w, caching, pool_frames=pool)
         host_s = time.perf_counter() - t0
         cache = DeviceCache(w.NB if caching else pool, w.B, w.H, w.D, V.torch_dtype(w.dtype), dev,
                             poison=True)
@@ -363,7 +360,7 @@ def bench_prefix(args, w, dev):
                 max_q=int(n.max()), rows=len(wb.slots), flops=4 * w.D * w.H * pairs,
                 order=None if args.prefill_batch_order else
                 torch.from_numpy(prefill_order(rd.context_lens, rd.query_start, int(n.max()))).to(dev)))
-        return rounds, mgr, cache, launches, (host_s, host_py_s)
+        return rounds, mgr, cache, launches, host_s
 
     flush_buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
@@ -424,20 +421,19 @@ def bench_prefix(args, w, dev):
 
     res = {}
     for caching in (True, False):
-        rounds, mgr, cache, launches, (host_s, host_py_s) = prepare(caching)
+        rounds, mgr, cache, launches, host_s = prepare(caching)
         step_ms, append_ms, prefill_ms, kernel_ms = timed(cache, launches)
         tokens = int(sum(int(rd.context_lens.sum()) for rd in rounds))
         reused = int(sum(int(rd.reused.sum()) for rd in rounds))
         res[caching] = dict(step_ms=step_ms, append_ms=append_ms, prefill_ms=prefill_ms,
                             kernel_ms=kernel_ms,
-                            tokens=tokens, reused=reused, host_plan_s=host_s, host_plan_py_s=host_py_s,
+                            tokens=tokens, reused=reused, host_plan_s=host_s,
                             rows=sum(L["rows"] for L in launches),
                             flops=sum(L["flops"] for L in launches),
                             evictions=getattr(mgr, "evictions", 0), frames=cache.k.shape[0])
         log(f"[bench] prefix caching {'on' if caching else 'off'}: step {step_ms * 1e3:.1f} us "
             f"(append {append_ms * 1e3:.1f}, prefill {prefill_ms * 1e3:.1f}), "
-            f"{reused}/{tokens} tokens reused, host plan {host_s * 1e3:.1f} ms "
-            f"(Python manager {host_py_s * 1e3:.0f} ms)")
+            f"{reused}/{tokens} tokens reused, host plan {host_s * 1e3:.1f} ms")
         del cache, launches
     on, off = res[True], res[False]
     value = on["tokens"] / (on["step_ms"] * 1e-3)
@@ -463,7 +459,6 @@ def bench_prefix(args, w, dev):
                             "written_rows": off["rows"], "frames": off["frames"]},
         "speedup_vs_no_caching": round(off["step_ms"] / on["step_ms"], 3),
         "host_plan_ms": {"native": round(on["host_plan_s"] * 1e3, 2),
-                         "python": round(on["host_plan_py_s"] * 1e3, 2),
                          "what": "block manager + slot lists for all rounds, before timing"},
         "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -551,10 +546,7 @@ def main():
         return
 
     t0 = time.perf_counter()
-    plan(w, native=False)  # Python manager, for reference
-    host_py_s = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    events, plan_mgr = plan(w)  # C++ manager
+    events, plan_mgr = plan(w)
     host_s = time.perf_counter() - t0
     cache = DeviceCache(w.NB, w.B, w.H, w.D, V.torch_dtype(w.dtype), dev, poison=True)
     points = []
@@ -896,7 +888,7 @@ def main():
         },
         "kernel_source_digest": digest,
         "cow_frame_copies": cow,
-        "host_plan_ms": {"native": round(host_s * 1e3, 2), "python": round(host_py_s * 1e3, 2),
+        "host_plan_ms": {"native": round(host_s * 1e3, 2),
                          "what": "block manager replay of the whole schedule (prefill, forks, "
                                  "decode steps) before timing"},
     }

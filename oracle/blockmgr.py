@@ -1,116 +1,151 @@
-"""The oracle's block manager and schedule replay (test infrastructure only).
+"""The oracle's frame bookkeeping and schedule replay (test infrastructure only).
 
-A direct restatement of the memory manager described on "PagedAttention:
-Virtual Memory Guide for LLM Inference" (sections "1. Demand Paging during
-Autoregressive Decoding", "2. Zero-Copy Branching via Copy-on-Write" and
-"Reference Implementation: Block Table & Paged Cache Manager"), checked
-against the worked allocation example of "PagedAttention, simply explained"
-(section "How PagedAttention solves it").
+The state is one record, :class:`Paging`: the free frames, a user count per
+frame, and per sequence its row of frames and its length. Plain functions
+change it, one per rule. The rules, as the pages state them:
 
-Rules as the pages state them:
-
-* the pool's free list is first-in first-out: allocation takes the head,
-  a frame whose reference count drops to zero goes to the tail;
-* a prompt of L tokens takes ceil(L / B) frames at once;
-* appending token t (t = tokens already held) takes a new frame exactly when
-  t mod B == 0, else writes into the last frame at offset t mod B;
-* forking copies the table and adds one reference to every frame in it;
-* appending into a shared (reference count > 1) partial last frame first
-  copies that frame to a newly allocated one (copy-on-write) and drops one
-  reference on the old frame.
+* Free frames leave from the front and return at the back (the pool of
+  "PagedAttention: Virtual Memory Guide for LLM Inference", section
+  "1. Demand Paging during Autoregressive Decoding"; the order is fixed by
+  the worked example of "PagedAttention, simply explained", section "How
+  PagedAttention solves it": prompts A, B, C, D take frames 0, 1, 2-3, 4 and
+  the next frame handed out is 5, then 6).
+* A prompt of L tokens holds ceil(L / B) frames (page 1, section 1; page 3's
+  example, where 12 tokens at B = 10 take two frames).
+* The token at position t (t = tokens the sequence already holds) goes to
+  offset t mod B of the sequence's last frame; when t mod B == 0 there is no
+  room and a new frame is appended first (page 1, section 1; page 3: D grows
+  from 9 to 10 tokens in its first frame and takes frame 5 for the 11th).
+* A branch starts with its parent's frames and length, and each of those
+  frames gains a user (page 1, section "2. Zero-Copy Branching via
+  Copy-on-Write").
+* Writing into a frame that has other users first gives the writer a private
+  frame holding a copy, and the shared frame loses that user (same section).
+* A frame whose users drop to zero returns to the pool; finishing a sequence
+  drops one user from each of its frames (page 1, section 1; "Solving the
+  LLM Memory Wall", algorithmic step 5).
 
 Readings where the pages leave a step open:
 
-* t = 0 (an empty sequence) takes the new-frame branch, since 0 mod B == 0;
-  the page's listing would read the last table entry of an empty table first.
-* The cache is modelled as the *identity* of the token written to each slot
-  (``frame * B + offset``), with -1 for a slot never written. A copy-on-write
-  copies the whole frame's identities, which is what a byte copy of the
+* t = 0 (an empty sequence) is the t mod B == 0 case: a new frame.
+* A prompt that needs more frames than are free takes none and raises
+  MemoryError (page 2's allocator checks the free count before taking).
+* The cache contents are modelled as the *identity* of the token written to
+  each slot (``frame * B + offset``), -1 for a slot never written. A
+  copy-on-write copies the whole frame's identities, as a byte copy of the
   frame does to its contents.
 """
 from __future__ import annotations
 
+import collections
 import math
 from dataclasses import dataclass
 
 import numpy as np
 
 
-class PhysicalBlockPool:
-    """Free frames in FIFO order plus a reference count per frame."""
+@dataclass
+class Paging:
+    """Frames and sequences of one pool."""
 
-    def __init__(self, num_blocks: int, order=None):
-        self.num_blocks = num_blocks
-        self.free_blocks = list(range(num_blocks)) if order is None else [int(f) for f in order]
-        assert sorted(self.free_blocks) == list(range(num_blocks))
-        self.ref_counts = {i: 0 for i in range(num_blocks)}
-
-    def allocate(self) -> int:
-        if not self.free_blocks:
-            raise MemoryError("frame pool exhausted")
-        block_id = self.free_blocks.pop(0)
-        self.ref_counts[block_id] = 1
-        return block_id
-
-    def add_reference(self, block_id: int) -> None:
-        self.ref_counts[block_id] += 1
-
-    def free(self, block_id: int) -> None:
-        if self.ref_counts[block_id] <= 0:
-            return
-        self.ref_counts[block_id] -= 1
-        if self.ref_counts[block_id] == 0:
-            self.free_blocks.append(block_id)
+    block_size: int
+    free: collections.deque  # free frame ids, next to hand out on the left
+    users: np.ndarray        # int64 [num_frames]: how many table rows (or caches) use each frame
+    table: dict              # sequence -> list of frame ids, logical block order
+    length: dict             # sequence -> tokens held
 
     @property
-    def free_count(self) -> int:
-        return len(self.free_blocks)
+    def num_frames(self) -> int:
+        return len(self.users)
 
 
-class SequenceGroupMemoryManager:
-    """Block tables and lengths per request; demand paging, fork and CoW."""
+def new_paging(num_frames: int, block_size: int, order=None) -> Paging:
+    """All frames free, handed out in ``order`` (default 0, 1, 2, ...)."""
+    free = collections.deque(range(num_frames) if order is None else (int(f) for f in order))
+    if sorted(free) != list(range(num_frames)):
+        raise ValueError("order must be a permutation of the frame ids")
+    return Paging(block_size, free, np.zeros(num_frames, dtype=np.int64), {}, {})
 
-    def __init__(self, pool: PhysicalBlockPool, block_size: int):
-        self.pool = pool
-        self.block_size = block_size
-        self.block_tables: dict = {}
-        self.seq_lens: dict = {}
 
-    def init_sequence(self, request_id, prompt_tokens: int) -> None:
-        n = math.ceil(prompt_tokens / self.block_size)
-        self.block_tables[request_id] = [self.pool.allocate() for _ in range(n)]
-        self.seq_lens[request_id] = prompt_tokens
+def frames_for(tokens: int, block_size: int) -> int:
+    """Frames that hold ``tokens`` tokens: the ceiling of tokens / B."""
+    return -(-tokens // block_size)
 
-    def append_token(self, request_id):
-        """Returns (old_frame, new_frame) when a copy-on-write happened, else None."""
-        cur_len = self.seq_lens[request_id]
-        table = self.block_tables[request_id]
-        copied = None
-        if cur_len % self.block_size == 0:
-            table.append(self.pool.allocate())
-        else:
-            cur_block_id = table[-1]
-            if self.pool.ref_counts[cur_block_id] > 1:
-                new_block_id = self.pool.allocate()
-                self.pool.free(cur_block_id)
-                table[-1] = new_block_id
-                copied = (cur_block_id, new_block_id)
-        self.seq_lens[request_id] = cur_len + 1
-        return copied
 
-    def fork_sequence(self, parent_id, child_id) -> None:
-        parent_table = self.block_tables[parent_id]
-        for b_id in parent_table:
-            self.pool.add_reference(b_id)
-        self.block_tables[child_id] = list(parent_table)
-        self.seq_lens[child_id] = self.seq_lens[parent_id]
+def take(pg: Paging) -> int:
+    """The frame at the front of the free list, now with one user."""
+    if not pg.free:
+        raise MemoryError("no free frame")
+    f = pg.free.popleft()
+    pg.users[f] = 1
+    return f
 
-    def free_sequence(self, request_id) -> None:
-        if request_id in self.block_tables:
-            for b_id in self.block_tables[request_id]:
-                self.pool.free(b_id)
-            del self.block_tables[request_id]
-            del self.seq_lens[request_id]
+
+def share(pg: Paging, f: int) -> None:
+    """One more user of frame ``f``."""
+    pg.users[f] += 1
+
+
+def release(pg: Paging, f: int) -> None:
+    """One user fewer; a frame left with none goes to the back of the free
+    list. A frame that has no user already is left as it is."""
+    if pg.users[f] > 0:
+        pg.users[f] -= 1
+        if pg.users[f] == 0:
+            pg.free.append(f)
+
+
+def start(pg: Paging, seq, tokens: int) -> None:
+    """Sequence ``seq`` with a prompt of ``tokens`` tokens."""
+    n = frames_for(tokens, pg.block_size)
+    if n > len(pg.free):
+        raise MemoryError("not enough free frames for the prompt")
+    pg.table[seq] = [take(pg) for _ in range(n)]
+    pg.length[seq] = tokens
+
+
+def extend(pg: Paging, seq):
+    """Room for one more token of ``seq``. Returns (shared frame, private
+    copy) when the token's frame had to be copied first, else None."""
+    row = pg.table[seq]
+    t = pg.length[seq]
+    copied = None
+    if t % pg.block_size == 0:
+        row.append(take(pg))
+    else:
+        last = row[-1]
+        if pg.users[last] > 1:
+            row[-1] = take(pg)
+            release(pg, last)
+            copied = (last, row[-1])
+    pg.length[seq] = t + 1
+    return copied
+
+
+def branch(pg: Paging, parent, child) -> None:
+    """``child`` starts as a copy of ``parent``'s row and length."""
+    for f in pg.table[parent]:
+        share(pg, f)
+    pg.table[child] = list(pg.table[parent])
+    pg.length[child] = pg.length[parent]
+
+
+def finish(pg: Paging, seq) -> None:
+    """``seq`` ends; an unknown sequence is ignored."""
+    row = pg.table.pop(seq, None)
+    if row is None:
+        return
+    del pg.length[seq]
+    for f in row:
+        release(pg, f)
+
+
+def slots_of(pg: Paging, seq, positions) -> np.ndarray:
+    """Slot (frame * B + offset) of each position of ``seq``."""
+    B = pg.block_size
+    row = np.asarray(pg.table[seq], dtype=np.int64)
+    pos = np.asarray(positions, dtype=np.int64)
+    return row[pos // B] * B + pos % B
 
 
 def memory_efficiency(tokens: int, block_size: int) -> float:
@@ -128,52 +163,47 @@ class Snapshot:
 
 
 def replay(w, pad_frame: int = -1, max_blocks: int | None = None):
-    """Play a workload schedule; one Snapshot per attention point.
+    """Play a workload schedule; returns (one Snapshot per attention point,
+    the final Paging).
 
     ``w`` is a :class:`workloads.configs.Workload`. Sequences are prefilled in
-    schedule order, forked, then each decode step appends one token to each
-    listed sequence in the listed order.
+    schedule order, branched, then each decode step appends one token to
+    each listed sequence in the listed order.
     """
-    pool = PhysicalBlockPool(w.NB, w.frame_order)
-    mgr = SequenceGroupMemoryManager(pool, w.B)
+    pg = new_paging(w.NB, w.B, w.frame_order)
     B = w.B
     slot_ident = np.full(w.NB * B, -1, dtype=np.int64)
 
-    def slots_of(s, positions):
-        table = np.asarray(mgr.block_tables[s], dtype=np.int64)
-        positions = np.asarray(positions, dtype=np.int64)
-        return table[positions // B] * B + positions % B
-
     for s, n in w.prefill:
-        mgr.init_sequence(s, n)
+        start(pg, s, n)
         if n:
             pos = np.arange(n)
-            slot_ident[slots_of(s, pos)] = w.idents(s, pos)
+            slot_ident[slots_of(pg, s, pos)] = w.idents(s, pos)
     for parent, child in w.forks:
-        mgr.fork_sequence(parent, child)
+        branch(pg, parent, child)
 
     snaps = []
 
     def snap():
         S = w.num_seqs
-        lens = np.array([mgr.seq_lens[s] for s in range(S)], dtype=np.int32)
-        mb = max_blocks or max(1, max(len(mgr.block_tables[s]) for s in range(S)))
+        lens = np.array([pg.length[s] for s in range(S)], dtype=np.int32)
+        mb = max_blocks or max(1, max(len(pg.table[s]) for s in range(S)))
         tables = np.full((S, mb), pad_frame, dtype=np.int32)
         for s in range(S):
-            t = mgr.block_tables[s]
-            tables[s, :len(t)] = t
-        snaps.append(Snapshot(tables, lens, slot_ident.copy(), list(pool.free_blocks)))
+            row = pg.table[s]
+            tables[s, :len(row)] = row
+        snaps.append(Snapshot(tables, lens, slot_ident.copy(), list(pg.free)))
 
     if -1 in w.attend_after:
         snap()
     for k, seqs in enumerate(w.steps):
         for s in seqs:
-            t = mgr.seq_lens[s]
-            copied = mgr.append_token(s)
+            t = pg.length[s]
+            copied = extend(pg, s)
             if copied is not None:
-                old, new = copied
-                slot_ident[new * B:(new + 1) * B] = slot_ident[old * B:(old + 1) * B]
-            slot_ident[slots_of(s, [t])] = w.idents(s, [t])
+                src, dst = copied
+                slot_ident[dst * B:(dst + 1) * B] = slot_ident[src * B:(src + 1) * B]
+            slot_ident[slots_of(pg, s, [t])] = w.idents(s, [t])
         if k in w.attend_after:
             snap()
-    return snaps, mgr, pool
+    return snaps, pg

@@ -29,6 +29,11 @@ The pages give no keying, lookup or eviction rule; the readings taken here:
   returns to the pool; allocation then proceeds first-in first-out.
 * A request whose frames cannot all be found (free plus evictable, not
   counting the frames it reuses) fails with nothing changed.
+* A branch (fork) starts with its parent's frames, tokens and length, each
+  frame gaining a user, as in :mod:`oracle.blockmgr`. A token appended into a
+  partial last frame that has other users first moves the writer to a
+  private copy of it (the copy's frame is found like any other, evicting if
+  it must); a block filled by an appended token enters the cache.
 
 The cache contents are modelled as the identity written to each slot (-1 for
 never written), as in :mod:`oracle.blockmgr`.
@@ -39,14 +44,14 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from oracle.blockmgr import PhysicalBlockPool
+from oracle.blockmgr import new_paging, release, share, take
 
 
 class PrefixCache:
     """Block tables over a FIFO pool, with reuse of cached full-block prefixes."""
 
     def __init__(self, num_blocks: int, block_size: int, order=None, enabled: bool = True):
-        self.pool = PhysicalBlockPool(num_blocks, order)
+        self.pg = new_paging(num_blocks, block_size, order)
         self.B = block_size
         self.enabled = enabled            # off: plain demand paging, nothing cached
         self.frame_of_prefix: dict = {}   # token prefix tuple -> frame
@@ -62,10 +67,10 @@ class PrefixCache:
         self.last_event[frame] = self.clock
 
     def _evictable(self) -> list:
-        return [f for f in self.prefix_of_frame if self.pool.ref_counts[f] == 1]
+        return [f for f in self.prefix_of_frame if self.pg.users[f] == 1]
 
     def _take_frame(self) -> int:
-        if self.pool.free_count == 0:
+        if not self.pg.free:
             candidates = self._evictable()
             if not candidates:
                 raise MemoryError("no free frame and no evictable cached frame")
@@ -75,9 +80,9 @@ class PrefixCache:
                     victim = f
             del self.frame_of_prefix[self.prefix_of_frame.pop(victim)]
             del self.last_event[victim]
-            self.pool.free(victim)
+            release(self.pg, victim)
             self.evicted.append(victim)
-        return self.pool.allocate()
+        return take(self.pg)
 
     def _enter(self, sid, b: int) -> None:
         prefix = tuple(self.tokens[sid][:(b + 1) * self.B])
@@ -86,7 +91,7 @@ class PrefixCache:
         frame = self.tables[sid][b]
         self.frame_of_prefix[prefix] = frame
         self.prefix_of_frame[frame] = prefix
-        self.pool.add_reference(frame)
+        share(self.pg, frame)
         self._event(frame)
 
     def start_request(self, sid, token_ids) -> int:
@@ -101,10 +106,10 @@ class PrefixCache:
             reused.append(f)
         fresh = (len(toks) + B - 1) // B - len(reused)
         evictable = [f for f in self._evictable() if f not in reused]
-        if fresh > self.pool.free_count + len(evictable):
+        if fresh > len(self.pg.free) + len(evictable):
             raise MemoryError("frame pool exhausted")
         for f in reused:
-            self.pool.add_reference(f)
+            share(self.pg, f)
             self._event(f)
         table = list(reused)
         for _ in range(fresh):
@@ -115,20 +120,34 @@ class PrefixCache:
             self._enter(sid, b)
         return len(reused) * B
 
-    def append(self, sid, token_id) -> int:
-        """One generated token; returns its slot. (No fork here, so the last
-        frame of a request is private and never copied.)"""
+    def append(self, sid, token_id):
+        """One generated token. Returns (slot, (shared frame, private copy))
+        when the token's frame was copied first, else (slot, None)."""
         t = len(self.tokens[sid])
+        row = self.tables[sid]
+        copied = None
         if t % self.B == 0:
-            self.tables[sid].append(self._take_frame())
+            row.append(self._take_frame())
+        elif self.pg.users[row[-1]] > 1:
+            mine = self._take_frame()
+            copied = (row[-1], mine)
+            release(self.pg, row[-1])
+            row[-1] = mine
         self.tokens[sid].append(int(token_id))
         if (t + 1) % self.B == 0:
             self._enter(sid, t // self.B)
-        return self.tables[sid][t // self.B] * self.B + t % self.B
+        return row[t // self.B] * self.B + t % self.B, copied
+
+    def fork(self, parent, child) -> None:
+        """``child`` starts with ``parent``'s frames and tokens."""
+        for f in self.tables[parent]:
+            share(self.pg, f)
+        self.tables[child] = list(self.tables[parent])
+        self.tokens[child] = list(self.tokens[parent])
 
     def end_request(self, sid) -> None:
         for f in self.tables.pop(sid):
-            self.pool.free(f)
+            release(self.pg, f)
         del self.tokens[sid]
 
     def slots(self, sid, positions) -> np.ndarray:
@@ -171,7 +190,7 @@ def replay_rounds(w, pad_frame: int = -1, caching: bool = True, pool_frames: int
         pc = PrefixCache(w.NB, w.B, w.frame_order, enabled=caching)
     else:
         pc = PrefixCache(pool_frames, w.B, None, enabled=caching)
-    slot_ident = np.full(pc.pool.num_blocks * w.B, -1, dtype=np.int64)
+    slot_ident = np.full(pc.pg.num_frames * w.B, -1, dtype=np.int64)
     rounds = []
     for r in range(w.rounds):
         reqs = w.requests(r)
@@ -194,7 +213,7 @@ def replay_rounds(w, pad_frame: int = -1, caching: bool = True, pool_frames: int
         for step in w.decode_steps(r):
             for c in step:
                 pos = len(pc.tokens[c])
-                slot = pc.append(c, int(w.tokens(c, [pos])[0]))
+                slot, _ = pc.append(c, int(w.tokens(c, [pos])[0]))
                 slot_ident[slot] = w.idents(c, [pos])[0]
             decode.append(DecodePoint(list(step), table_of(step),
                                       np.array([len(pc.tokens[c]) for c in step], dtype=np.int32)))
@@ -202,5 +221,5 @@ def replay_rounds(w, pad_frame: int = -1, caching: bool = True, pool_frames: int
             pc.end_request(c)
         rounds.append(Round(seqs, tables, np.array([n for _, n in reqs], dtype=np.int32),
                             np.array(reused, dtype=np.int64), slot_ident.copy(),
-                            list(pc.pool.free_blocks), decode))
+                            list(pc.pg.free), decode))
     return rounds, pc

@@ -19,7 +19,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .block_manager import BlockPool, SeqManager
+from .native_blocks import NativeBlockManager
 
 
 @dataclass
@@ -49,23 +49,15 @@ class AttendPoint:
         return PA_CACHE_REUSE if self.shared_frames else PA_CACHE_STREAM
 
 
-def make_manager(num_frames: int, block_size: int, order=None, prefix_caching: bool = False,
-                 native: bool = True):
-    """A block manager: the C++ one (native) or the Python one, same rules."""
-    if native:
-        from .native_blocks import NativeBlockManager
-
-        return NativeBlockManager(num_frames, block_size, order, prefix_caching)
-    from .block_manager import PrefixCachingSeqManager
-
-    pool = BlockPool(num_frames, order)
-    return PrefixCachingSeqManager(pool, block_size) if prefix_caching else SeqManager(pool, block_size)
+def make_manager(num_frames: int, block_size: int, order=None, prefix_caching: bool = False):
+    """The host block manager (C++, include/paged_blocks.h)."""
+    return NativeBlockManager(num_frames, block_size, order, prefix_caching)
 
 
-def plan(schedule, pad: int = -1, max_blocks: int | None = None, native: bool = True):
+def plan(schedule, pad: int = -1, max_blocks: int | None = None):
     """Host-only replay. Returns (events, manager); each event is a
     WriteBatch or an AttendPoint, in the order a serving loop issues them."""
-    mgr = make_manager(schedule.NB, schedule.B, schedule.frame_order, native=native)
+    mgr = make_manager(schedule.NB, schedule.B, schedule.frame_order)
     B = schedule.B
     sids = list(range(schedule.num_seqs))
     events = []
@@ -275,8 +267,7 @@ class PrefillRound:
     decode: list = None       # DecodeStep per decode step after the prefill
 
 
-def plan_prefix_rounds(w, caching: bool = True, pad: int = -1, pool_frames: int | None = None,
-                       native: bool = True):
+def plan_prefix_rounds(w, caching: bool = True, pad: int = -1, pool_frames: int | None = None):
     """Host-only replay of a prefix-sharing workload (``w.rounds``,
     ``w.requests(r)`` -> [(id, prompt_len)], ``w.tokens(id, positions)``).
 
@@ -287,9 +278,9 @@ def plan_prefix_rounds(w, caching: bool = True, pad: int = -1, pool_frames: int 
     that many frames in id order (a run without caching needs more).
     Returns (rounds, manager)."""
     if pool_frames is None:
-        mgr = make_manager(w.NB, w.B, w.frame_order, caching, native)
+        mgr = make_manager(w.NB, w.B, w.frame_order, caching)
     else:
-        mgr = make_manager(pool_frames, w.B, None, caching, native)
+        mgr = make_manager(pool_frames, w.B, None, caching)
     out = []
     for r in range(w.rounds):
         reqs = w.requests(r)

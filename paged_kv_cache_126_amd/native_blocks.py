@@ -1,16 +1,17 @@
-"""ctypes binding of the native host block manager (include/paged_blocks.h).
+"""ctypes binding of the host block manager (include/paged_blocks.h).
 
-``NativeBlockManager`` has the interface of :class:`block_manager.SeqManager`
-(and, with ``prefix_caching=True``, of :class:`block_manager.
-PrefixCachingSeqManager`) with the same rules; the work happens in C++.
+``NativeBlockManager`` is the frame pool and the sequences' block tables:
+demand paging, fork with copy-on-write, and (with ``prefix_caching=True``)
+reuse of cached full blocks across requests. Argument marshalling only: the
+work happens in the library's C++ code (csrc/block_manager.cpp).
 """
 from __future__ import annotations
 
 import ctypes
+from dataclasses import dataclass
 
 import numpy as np
 
-from .block_manager import AppendResult
 from .lib import load
 
 PB_OK, PB_EINVAL, PB_ENOMEM, PB_ESTATE = 0, -1, -2, -3
@@ -18,6 +19,14 @@ PB_OK, PB_EINVAL, PB_ENOMEM, PB_ESTATE = 0, -1, -2, -3
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
+
+
+@dataclass
+class AppendResult:
+    slot: int                    # where the new token's K/V rows go
+    cow_src: int | None = None   # frame to copy from (copy-on-write), or None
+    cow_dst: int | None = None   # the sequence's new private frame
+    cow_rows: int = 0            # rows of cow_src to copy (offsets 0 .. cow_rows - 1)
 
 
 class PbStats(ctypes.Structure):

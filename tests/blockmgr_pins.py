@@ -1,7 +1,7 @@
 """Pins of a block manager module against the pages' worked examples.
 
-Each ``pin_*`` takes a module exposing ``PhysicalBlockPool``,
-``SequenceGroupMemoryManager``, ``memory_efficiency`` and ``replay`` (the
+Each ``pin_*`` takes a module exposing ``new_paging``, ``start``,
+``extend``, ``branch``, ``finish``, ``memory_efficiency`` and ``replay`` (the
 oracle's :mod:`oracle.blockmgr`, or a copy of it with a planted mistake).
 """
 from __future__ import annotations
@@ -29,7 +29,7 @@ def pin_p3_worked_example(mod):
     w = replace(configs.config1(), attend_after=[-1, 0, 1, 2])
     assert w.B == g["block_size"] and w.NB == g["num_frames"]
     assert [n for _, n in w.prefill] == [g["prefill"][r] for r in g["requests"]]
-    snaps, _, _ = mod.replay(w)
+    snaps, _ = mod.replay(w)
     assert len(snaps) == len(g["states"])
     for snap, state in zip(snaps, g["states"]):
         for s, r in enumerate(g["requests"]):
@@ -48,37 +48,35 @@ def pin_p3_worked_example(mod):
 
 def pin_p1_demo(mod):
     g = _golden("p1_demo.json")
-    pool = mod.PhysicalBlockPool(g["num_frames"])
-    mgr = mod.SequenceGroupMemoryManager(pool, g["block_size"])
+    pg = mod.new_paging(g["num_frames"], g["block_size"])
     st, dv = g["stated"], g["derived"]
-    mgr.init_sequence("req_alpha", g["prompt_tokens"])
-    assert mgr.block_tables["req_alpha"] == st["alpha_table_after_prompt"]
-    assert g["num_frames"] - pool.free_count == st["frames_allocated_by_prompt"]
-    assert pool.free_count == dv["free_after_prompt"]
-    before = pool.free_count
-    mgr.fork_sequence("req_alpha", "req_beta")
-    assert before - pool.free_count == st["extra_frames_used_by_fork"]
-    assert mgr.block_tables["req_beta"] == dv["beta_table_after_fork"]
-    assert pool.free_count == dv["free_after_fork"]
-    assert {str(k): pool.ref_counts[k] for k in (0, 1)} == dv["ref_counts_after_fork"]
-    assert mgr.seq_lens["req_alpha"] == st["append_allocates_one_new_block_because_length_was"]
-    mgr.append_token("req_alpha")
-    assert mgr.block_tables["req_alpha"] == dv["alpha_table_after_append"]
-    assert mgr.block_tables["req_beta"] == dv["beta_table_after_append"]
-    assert pool.free_count == dv["free_after_append"]
-    mgr.free_sequence("req_alpha")
-    mgr.free_sequence("req_beta")
-    assert pool.free_count == st["free_after_cleanup_of"] == dv["free_after_cleanup"]
-    assert pool.free_blocks[-5:] == dv["free_list_tail_after_cleanup"]
+    mod.start(pg, "req_alpha", g["prompt_tokens"])
+    assert pg.table["req_alpha"] == st["alpha_table_after_prompt"]
+    assert g["num_frames"] - len(pg.free) == st["frames_allocated_by_prompt"]
+    assert len(pg.free) == dv["free_after_prompt"]
+    before = len(pg.free)
+    mod.branch(pg, "req_alpha", "req_beta")
+    assert before - len(pg.free) == st["extra_frames_used_by_fork"]
+    assert pg.table["req_beta"] == dv["beta_table_after_fork"]
+    assert len(pg.free) == dv["free_after_fork"]
+    assert {str(k): int(pg.users[k]) for k in (0, 1)} == dv["ref_counts_after_fork"]
+    assert pg.length["req_alpha"] == st["append_allocates_one_new_block_because_length_was"]
+    mod.extend(pg, "req_alpha")
+    assert pg.table["req_alpha"] == dv["alpha_table_after_append"]
+    assert pg.table["req_beta"] == dv["beta_table_after_append"]
+    assert len(pg.free) == dv["free_after_append"]
+    mod.finish(pg, "req_alpha")
+    mod.finish(pg, "req_beta")
+    assert len(pg.free) == st["free_after_cleanup_of"] == dv["free_after_cleanup"]
+    assert list(pg.free)[-5:] == dv["free_list_tail_after_cleanup"]
 
 
 def pin_p2_efficiency(mod):
     g = _golden("p2_efficiency.json")
     B, n = g["block_size"], g["sequence_length"]
-    pool = mod.PhysicalBlockPool(10)
-    mgr = mod.SequenceGroupMemoryManager(pool, B)
-    mgr.init_sequence(0, n)
-    blocks = len(mgr.block_tables[0])
+    pg = mod.new_paging(10, B)
+    mod.start(pg, 0, n)
+    blocks = len(pg.table[0])
     assert blocks == g["blocks_allocated"]
     assert blocks * B == g["slots_allocated"]
     assert blocks * B - n == g["wasted_slots"]
@@ -92,47 +90,53 @@ def pin_waste_below_one_block(mod):
     bound; page 1's 'Maximum Waste per Request')."""
     rng = np.random.default_rng(7)
     for B in (1, 3, 10, 16):
-        pool = mod.PhysicalBlockPool(4000)
-        mgr = mod.SequenceGroupMemoryManager(pool, B)
+        pg = mod.new_paging(4000, B)
         lens = rng.integers(0, 60, size=12)
         for s, n in enumerate(lens):
-            mgr.init_sequence(s, int(n))
+            mod.start(pg, s, int(n))
         for _ in range(40):
             for s in range(len(lens)):
                 if rng.random() < 0.6:
-                    mgr.append_token(s)
-                    waste = len(mgr.block_tables[s]) * B - mgr.seq_lens[s]
+                    mod.extend(pg, s)
+                    waste = len(pg.table[s]) * B - pg.length[s]
                     assert 0 <= waste <= B - 1, (B, s, waste)
 
 
 def pin_copy_on_write(mod):
     """Appending into a shared partial frame copies that one frame only."""
-    pool = mod.PhysicalBlockPool(20)
-    mgr = mod.SequenceGroupMemoryManager(pool, 4)
-    mgr.init_sequence("p", 10)          # frames 0, 1, 2 (last holds 2 tokens)
-    mgr.fork_sequence("p", "c")
-    assert pool.ref_counts[2] == 2 and pool.free_count == 17
-    copied = mgr.append_token("c")       # shared partial frame 2 -> copy into 3
+    pg = mod.new_paging(20, 4)
+    mod.start(pg, "p", 10)               # frames 0, 1, 2 (last holds 2 tokens)
+    mod.branch(pg, "p", "c")
+    assert pg.users[2] == 2 and len(pg.free) == 17
+    copied = mod.extend(pg, "c")         # shared partial frame 2 -> copy into 3
     assert copied == (2, 3)
-    assert mgr.block_tables["c"] == [0, 1, 3] and mgr.block_tables["p"] == [0, 1, 2]
-    assert pool.ref_counts[2] == 1 and pool.ref_counts[3] == 1 and pool.ref_counts[0] == 2
-    assert mgr.append_token("p") is None  # now private: no copy
-    assert mgr.block_tables["p"] == [0, 1, 2]
-    mgr.append_token("p")
-    mgr.append_token("p")                 # length 12 -> new frame 4
-    assert mgr.block_tables["p"] == [0, 1, 2, 4]
+    assert pg.table["c"] == [0, 1, 3] and pg.table["p"] == [0, 1, 2]
+    assert pg.users[2] == 1 and pg.users[3] == 1 and pg.users[0] == 2
+    assert mod.extend(pg, "p") is None   # now private: no copy
+    assert pg.table["p"] == [0, 1, 2]
+    mod.extend(pg, "p")
+    mod.extend(pg, "p")                  # length 12 -> new frame 4
+    assert pg.table["p"] == [0, 1, 2, 4]
+    mod.finish(pg, "c")                  # c's private frame 3 returns; 0, 1 keep one user
+    assert list(pg.free)[-1] == 3 and pg.users[0] == 1 and pg.users[3] == 0
 
 
 def pin_pool_exhaustion(mod):
-    pool = mod.PhysicalBlockPool(3)
-    mgr = mod.SequenceGroupMemoryManager(pool, 2)
-    mgr.init_sequence(0, 6)
+    pg = mod.new_paging(3, 2)
+    mod.start(pg, 0, 6)
     try:
-        mgr.append_token(0)
+        mod.extend(pg, 0)
     except MemoryError:
         pass
     else:
         raise AssertionError("no MemoryError when the pool is empty")
+    pg = mod.new_paging(3, 2)
+    try:
+        mod.start(pg, 0, 7)              # four frames from a pool of three
+    except MemoryError:
+        assert len(pg.free) == 3 and 0 not in pg.table
+    else:
+        raise AssertionError("no MemoryError for a prompt larger than the pool")
 
 
 def pin_replay_cow_contents(mod):
@@ -140,7 +144,7 @@ def pin_replay_cow_contents(mod):
     read through its table, carry the identities the schedule assigned."""
     w = configs.config4(prompts=2, n=3, prompt_len=45, H=1, NB=200, max_tail=40)
     w.B = 8
-    snaps, _, _ = mod.replay(w)
+    snaps, _ = mod.replay(w)
     snap = snaps[-1]
     for s in range(w.num_seqs):
         ctx = int(snap.context_lens[s])

@@ -212,7 +212,7 @@ def oracle_caches(w, snap):
 def oracle_outputs(w, pad):
     """fp64 oracle outputs [S, H, D] at every attention point of ``w``."""
     orc = oracle_default()
-    snaps, _, _ = obm.replay(w, pad_frame=pad)
+    snaps, _ = obm.replay(w, pad_frame=pad)
     outs = []
     for i, snap in enumerate(snaps):
         k, v = oracle_caches(w, snap)

@@ -12,7 +12,7 @@ import sys
 
 import numpy as np
 
-from oracle.blockmgr import PhysicalBlockPool, SequenceGroupMemoryManager
+from oracle import blockmgr as obm
 from workloads import configs
 
 # 6 frames handed out 0..5, B = 2. Each step: ("start", request, tokens,
@@ -38,18 +38,22 @@ HAND_EVICTED = [3, 4, 5]
 HAND_FINAL = {0: (1, 2), 1: (1, 2, 3, 4), 3: (5, 5), 2: (3, 4), 4: (3, 4, 5, 6)}
 
 
+def _users(pc) -> dict:
+    return {f: int(n) for f, n in enumerate(pc.pg.users)}
+
+
 def check_invariants(pc, slot_ident=None):
     """Reference counts = table uses + one for the cache; the free list and
     the referenced frames partition the pool; cached prefixes are whole
     blocks; a cached frame's slots hold the last block of its prefix."""
-    uses = {f: 0 for f in range(pc.pool.num_blocks)}
+    uses = {f: 0 for f in range(pc.pg.num_frames)}
     for t in pc.tables.values():
         for f in t:
             uses[f] += 1
     for f in pc.prefix_of_frame:
         uses[f] += 1
-    assert uses == pc.pool.ref_counts, "reference counts"
-    free = pc.pool.free_blocks
+    assert uses == _users(pc), "reference counts"
+    free = list(pc.pg.free)
     assert len(set(free)) == len(free)
     assert set(free) == {f for f, n in uses.items() if n == 0}, "free list"
     for prefix, f in pc.frame_of_prefix.items():
@@ -66,7 +70,7 @@ def pin_hand_worked_example(mod):
             continue
         _, sid, toks, reused, table = st
         if reused is MemoryError:
-            before = (dict(pc.pool.ref_counts), list(pc.pool.free_blocks), dict(pc.frame_of_prefix),
+            before = (_users(pc), list(pc.pg.free), dict(pc.frame_of_prefix),
                       dict(pc.last_event))
             try:
                 pc.start_request(sid, toks)
@@ -74,7 +78,7 @@ def pin_hand_worked_example(mod):
                 pass
             else:
                 raise AssertionError(f"{sid} should not fit")
-            after = (dict(pc.pool.ref_counts), list(pc.pool.free_blocks), dict(pc.frame_of_prefix),
+            after = (_users(pc), list(pc.pg.free), dict(pc.frame_of_prefix),
                      dict(pc.last_event))
             assert before == after, "a failed request changed the state"
             continue
@@ -83,13 +87,14 @@ def pin_hand_worked_example(mod):
         assert pc.tables[sid] == table, (sid, pc.tables[sid])
         check_invariants(pc)
     assert pc.evicted == HAND_EVICTED, pc.evicted
-    assert pc.pool.free_blocks == []
+    assert list(pc.pg.free) == []
     assert {f: p for p, f in pc.frame_of_prefix.items()} == HAND_FINAL
 
 
-def random_ops(seed, n_ops=400):
-    """A random stream of request starts, token appends and request ends
-    over a vocabulary of 1 to 3 tokens, B in 1..3, a pool of 3 to 11 frames."""
+def random_ops(seed, n_ops=400, fork=False):
+    """A random stream of request starts, token appends, request ends and
+    (with ``fork``) branches, over a vocabulary of 1 to 3 tokens, B in 1..3,
+    a pool of 3 to 11 frames."""
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 4))
     NB = int(rng.integers(3, 12))
@@ -102,21 +107,26 @@ def random_ops(seed, n_ops=400):
             live.append(i)
         elif u < 0.7:
             ops.append(("append", live[int(rng.integers(0, len(live)))], int(rng.integers(0, vocab))))
+        elif u < 0.8 and fork:
+            ops.append(("fork", live[int(rng.integers(0, len(live)))], i))
+            live.append(i)
         else:
             ops.append(("end", live.pop(int(rng.integers(0, len(live))))))
     return B, NB, ops
 
 
 def pin_random_streams_keep_invariants(mod):
-    """Under random streams: the invariants hold after every step, every
-    reused position already holds the request's own token, and a failed
-    start or append leaves the state as it was."""
-    for seed in range(12):
-        B, NB, ops = random_ops(seed)
+    """Under random streams (half of them with branches): the invariants hold
+    after every step, every reused position already holds the request's own
+    token, every position of every live request reads back its own token
+    through its table (so a copy-on-write copied what it had to), and a
+    failed start or append leaves the state as it was."""
+    for seed in range(24):
+        B, NB, ops = random_ops(seed, fork=seed % 2 == 1)
         pc = mod.PrefixCache(NB, B)
         slot_ident = np.full(NB * B, -1, dtype=np.int64)
         for op in ops:
-            state = (dict(pc.pool.ref_counts), list(pc.pool.free_blocks))
+            state = (_users(pc), list(pc.pg.free))
             try:
                 if op[0] == "start":
                     k = pc.start_request(op[1], op[2])
@@ -127,12 +137,21 @@ def pin_random_streams_keep_invariants(mod):
                     assert np.array_equal(slot_ident[slots[:k]], toks[:k]), "reused wrong content"
                     slot_ident[slots[k:]] = toks[k:]
                 elif op[0] == "append" and op[1] in pc.tables:
-                    slot_ident[pc.append(op[1], op[2])] = op[2]
+                    slot, copied = pc.append(op[1], op[2])
+                    if copied is not None:
+                        src, dst = copied
+                        slot_ident[dst * B:(dst + 1) * B] = slot_ident[src * B:(src + 1) * B]
+                    slot_ident[slot] = op[2]
+                elif op[0] == "fork" and op[1] in pc.tables:
+                    pc.fork(op[1], op[2])
                 elif op[0] == "end" and op[1] in pc.tables:
                     pc.end_request(op[1])
             except MemoryError:
-                assert state == (dict(pc.pool.ref_counts), list(pc.pool.free_blocks))
+                assert state == (_users(pc), list(pc.pg.free))
             check_invariants(pc, slot_ident)
+            for sid, toks in pc.tokens.items():
+                got = slot_ident[pc.slots(sid, np.arange(len(toks)))]
+                assert np.array_equal(got, np.asarray(toks, dtype=np.int64)), ("read back", sid)
 
 
 def pin_reuse_is_maximal(mod):
@@ -162,22 +181,22 @@ def pin_caching_off_is_demand_paging(mod):
     w = configs.small(8)
     NB = w.frames_without_caching
     rounds, _ = mod.replay_rounds(w, caching=False, pool_frames=NB)
-    mgr = SequenceGroupMemoryManager(PhysicalBlockPool(NB), w.B)
+    pg = obm.new_paging(NB, w.B)
     assert any(rd.decode for rd in rounds)
     for rd in rounds:
         assert not rd.reused.any()
         for i, (c, n) in enumerate(zip(rd.seqs, rd.context_lens)):
-            mgr.init_sequence(c, int(n))
-            t = mgr.block_tables[c]
+            obm.start(pg, c, int(n))
+            t = pg.table[c]
             assert list(rd.tables[i, :len(t)]) == t
         for pt in rd.decode:
             for i, c in enumerate(pt.seqs):
-                mgr.append_token(c)
+                obm.extend(pg, c)
             for i, c in enumerate(pt.seqs):
-                t = mgr.block_tables[c]
-                assert list(pt.tables[i, :len(t)]) == t and pt.context_lens[i] == mgr.seq_lens[c]
+                t = pg.table[c]
+                assert list(pt.tables[i, :len(t)]) == t and pt.context_lens[i] == pg.length[c]
         for c in rd.seqs:
-            mgr.free_sequence(c)
+            obm.finish(pg, c)
 
 
 def pin_rounds_hold_every_prompt(mod):

@@ -47,15 +47,16 @@ C_MUTANTS = {
 }
 
 PY_MUTANTS = {
-    "lifo_pool": ("block_id = self.free_blocks.pop(0)", "block_id = self.free_blocks.pop()"),
-    "free_to_head": ("self.free_blocks.append(block_id)", "self.free_blocks.insert(0, block_id)"),
-    "new_frame_rule": ("if cur_len % self.block_size == 0:", "if (cur_len + 1) % self.block_size == 0:"),
-    "prefill_floor": ("n = math.ceil(prompt_tokens / self.block_size)",
-                      "n = prompt_tokens // self.block_size"),
-    "no_cow": ("if self.pool.ref_counts[cur_block_id] > 1:", "if self.pool.ref_counts[cur_block_id] > 99:"),
-    "fork_no_ref": ("self.pool.add_reference(b_id)", "pass"),
-    "cow_no_copy": ("slot_ident[new * B:(new + 1) * B] = slot_ident[old * B:(old + 1) * B]", "pass"),
-    "free_ignores_refcount": ("if self.ref_counts[block_id] == 0:", "if True:"),
+    "lifo_pool": ("f = pg.free.popleft()", "f = pg.free.pop()"),
+    "free_to_head": ("            pg.free.append(f)", "            pg.free.appendleft(f)"),
+    "new_frame_rule": ("if t % pg.block_size == 0:", "if (t + 1) % pg.block_size == 0:"),
+    "prefill_floor": ("return -(-tokens // block_size)", "return tokens // block_size"),
+    "no_cow": ("if pg.users[last] > 1:", "if pg.users[last] > 99:"),
+    "cow_keeps_old_user": ("            release(pg, last)\n", "            pass\n"),
+    "fork_no_ref": ("        share(pg, f)\n    pg.table[child]", "        pass\n    pg.table[child]"),
+    "fork_aliases_row": ("pg.table[child] = list(pg.table[parent])", "pg.table[child] = pg.table[parent]"),
+    "cow_no_copy": ("slot_ident[dst * B:(dst + 1) * B] = slot_ident[src * B:(src + 1) * B]", "pass"),
+    "free_ignores_refcount": ("if pg.users[f] == 0:", "if True:"),
 }
 
 
@@ -68,16 +69,19 @@ PC_MUTANTS = {
                         "f = self.frame_of_prefix.get(tuple(toks[b * B:(b + 1) * B]))")],
     "mru_eviction": ("if self.last_event[f] < self.last_event[victim]:",
                      "if self.last_event[f] > self.last_event[victim]:"),
-    "reuse_not_an_event": ("self.pool.add_reference(f)\n            self._event(f)",
-                           "self.pool.add_reference(f)"),
+    "reuse_not_an_event": ("share(self.pg, f)\n            self._event(f)",
+                           "share(self.pg, f)"),
     "no_stop_at_miss": ("            if f is None:\n                break",
                         "            if f is None:\n                continue"),
-    "cache_holds_no_ref": ("self.prefix_of_frame[frame] = prefix\n        self.pool.add_reference(frame)",
+    "cache_holds_no_ref": ("self.prefix_of_frame[frame] = prefix\n        share(self.pg, frame)",
                            "self.prefix_of_frame[frame] = prefix"),
     "partial_block_cached": ("for b in range(len(reused), len(toks) // B):",
                              "for b in range(len(reused), (len(toks) + B - 1) // B):"),
-    "failure_not_atomic": ("if fresh > self.pool.free_count + len(evictable):", "if False:"),
-    "evict_in_use": ("if self.pool.ref_counts[f] == 1]", "if self.pool.ref_counts[f] >= 1]"),
+    "failure_not_atomic": ("if fresh > len(self.pg.free) + len(evictable):", "if False:"),
+    "evict_in_use": ("if self.pg.users[f] == 1]", "if self.pg.users[f] >= 1]"),
+    "branch_no_ref": ("        for f in self.tables[parent]:\n            share(self.pg, f)",
+                      "        for f in self.tables[parent]:\n            pass"),
+    "branch_no_cow": ("elif self.pg.users[row[-1]] > 1:", "elif False:"),
     "entry_replaces_existing": ("if not self.enabled or prefix in self.frame_of_prefix:",
                                 "if not self.enabled:"),
 }
