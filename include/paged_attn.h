@@ -181,7 +181,9 @@ int32_t paged_attn_partition_tokens(const pa_decode_shape* shape);
  *   block_tables  [S, max_blocks_per_seq] int32: logical block -> frame
  *   context_lens  [S] int32: tokens each query attends to (its own included)
  *   block_size    B (must equal shape->block_size)
- *   scale         multiplier of q . k (1 / sqrt(D) for standard attention)
+ *   scale         multiplier of q . k (1 / sqrt(D) for standard attention):
+ *                 any finite value, zero and negative ones included; a
+ *                 non-finite scale is PA_EINVAL
  *   out           [S, H, D] in out_dtype
  *   workspace     device buffer of workspace_bytes >= paged_attn_workspace_size,
  *                 256-byte aligned; may be NULL when that size is 0
@@ -307,7 +309,7 @@ typedef struct pa_prefill_shape {
  *                 query_start[s] .. query_start[s+1]-1
  *   query_start   [S + 1] int32 (device), non-decreasing, query_start[S] <= T
  *   block_tables, context_lens, k_cache, v_cache, block_size, scale: as for
- *                 paged_attn_decode
+ *                 paged_attn_decode (any finite scale)
  *   out           [T, H, D] in out_dtype
  *   work_order    NULL, or device int32 [S * Tq] with
  *                 Tq = ceil(max_query_len / PA_PREFILL_TILE): the order in

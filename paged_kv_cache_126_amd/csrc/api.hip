@@ -393,7 +393,10 @@ pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_c
   a.query_start = query_start;
   a.out = out;
   a.num_blocks = sh->num_blocks;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  // The kernel takes each query's maximum on unscaled scores, which needs a
+  // scale >= 0; a negative scale is moved into q, whose sign flip is exact.
+  a.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+  a.negate_q = scale < 0.f ? 1 : 0;
   a.num_seqs = sh->num_seqs;
   a.block_size = sh->block_size;
   a.num_heads = sh->num_heads;

@@ -75,7 +75,8 @@ struct PrefillArgs {
   const int32_t* query_start;  // [S + 1]
   void* out;                   // [total_queries, H, D]
   int64_t num_blocks;
-  float scale_log2;
+  float scale_log2;            // |scale| * log2(e), >= 0
+  int32_t negate_q;            // 1 when scale < 0: q enters with its sign flipped
   int32_t num_seqs;
   int32_t block_size;
   int32_t num_heads;

@@ -196,10 +196,14 @@ void prefill_kernel(PrefillArgs a) {
   {
     const char* qrow = static_cast<const char*>(a.q) +
                        ((static_cast<int64_t>(q0) + my_q) * a.num_heads + h) * D * T::kBytes;
+    // scale * (q . k) = |scale| * ((-q) . k) for scale < 0; flipping the
+    // sign bit of every 16-bit element negates q exactly
+    const uint32_t sign = a.negate_q ? 0x80008000u : 0u;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (q_ok) v = load16(qrow + (16 * st + 8 * half) * T::kBytes);
+      v = u32x4{v.x ^ sign, v.y ^ sign, v.z ^ sign, v.w ^ sign};
       qb[st] = M::from_bits(v);
     }
   }
@@ -338,8 +342,8 @@ void prefill_kernel(PrefillArgs a) {
           tmax = fmaxf(tmax, x[t]);
         }
       }
-      // raw scores so far; the scale (> 0, order-preserving) is applied to the
-      // maximum here and folded into the exponent's fma below
+      // raw scores so far; the scale (>= 0, so order-preserving) is applied to
+      // the maximum here and folded into the exponent's fma below
       tmax = max_halves(tmax) * a.scale_log2;
       // Lazy rescaling: the reference maximum m moves (and O, l are rescaled)
       // only when a query's maximum grows by more than kLazy (log2 units);
@@ -360,6 +364,14 @@ void prefill_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int t = 0; t < 16; ++t) x[t] = fast_exp2(__builtin_fmaf(x[t], a.scale_log2, -m));
+      if (!full) {
+        // masked keys weigh exactly 0 (with a zero scale, -inf * 0 would be NaN)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int key = k0 + (t % 4) + 8 * (t / 4) + 4 * half;
+          x[t] = (q_ok && key <= my_pos) ? x[t] : 0.f;
+        }
+      }
 
       // P^T into the B-operand layout: for keys 16j .. 16j+15 the lower half
       // of the wavefront needs keys 16j + [0,8), the upper half 16j + [8,16);

@@ -137,6 +137,37 @@ def pin_zero_query_is_mean(orc):
                 assert abs(out[s, h, e] - mean) <= 1e-15, (s, h, e)
 
 
+def pin_zero_scale_is_mean(orc):
+    """scale = 0 makes every score 0, so every weight is equal: the output is
+    the mean of the V rows (bf16 storage, any q)."""
+    c = Case(23, 3, 2, 16, 4, "bf16", 40, min_ctx=5)
+    c.scale = 0.0
+    out = c.decode(orc)
+    for s in range(c.S):
+        vv = np_widen(c.rows_v[s], "bf16")
+        for h in range(c.H):
+            for e in range(c.D):
+                mean = math.fsum(vv[:, h, e]) / c.ctx[s]
+                assert abs(out[s, h, e] - mean) <= 1e-15, (s, h, e)
+
+
+def pin_negative_scale_is_negated_query(orc):
+    """scale * (q . k) = (-scale) * ((-q) . k): a negative scale gives the
+    output of the positive scale with q's sign flipped, bit for bit (the
+    flip is exact in every storage dtype, and so are the negated products)."""
+    for dtype, flip in (("bf16", 0x8000), ("f16", 0x8000), ("f32", None)):
+        c = Case(24, 3, 2, 8, 4, dtype, 30)
+        c.scale = -0.35
+        neg = c.decode(orc)
+        c.q = (-c.q if flip is None else (c.q ^ np.uint16(flip)))
+        c.scale = 0.35
+        pos = c.decode(orc)
+        assert np.array_equal(neg, pos), dtype
+        # and it is not the positive-scale output of the original q
+        c.q = (-c.q if flip is None else (c.q ^ np.uint16(flip)))
+        assert not np.allclose(c.decode(orc), pos), dtype
+
+
 def pin_peaked_score_selects_row(orc):
     """Key j aligned with a large query dominates: output = v_j to ~e^-60."""
     c = Case(23, 2, 2, 8, 3, "f32", 30, min_ctx=6)

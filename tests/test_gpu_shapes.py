@@ -122,3 +122,28 @@ def test_prefill_idle_wavefronts(dtype):
     err = max_err(out.numpy(), ref)
     say(f"  {int(qs[-1])} queries, max-abs err {err:.3e} (tol {TOL[dtype]})")
     assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, -1.5])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_nonpositive_scale(dtype, scale):
+    """Any finite scale: zero (every visible key weighs the same, so the
+    output is the mean of the value rows) and negative ones, for decode
+    (forced partitions, so the merge runs too) and for prefill (causal
+    masks, whose keys must still weigh exactly 0), against the oracle."""
+    from dataclasses import replace
+
+    ctx, qlens = [300, 45, 129, 1, 70], [300, 45, 20, 1, 33]
+    w = replace(shape_workload(dtype, 128, 16, ctx, H=2, query_lens=qlens, seed=15), scale_value=scale)
+    say(f"[gpu] scale {scale}: {w.description}")
+    res = run_gpu(w, partition_tokens=64)
+    ref = oracle_outputs(w, pad_frame_for(w))
+    for (pt, out), (snap, o) in zip(res, ref):
+        err = max_err(out.numpy(), o)
+        say(f"  decode max-abs err {err:.3e}")
+        assert err <= TOL[dtype]
+    pt, qs, out = run_gpu_prefill(w)
+    snap, ref = oracle_prefill(w, pad_frame_for(w))
+    err = max_err(out.numpy(), ref)
+    say(f"  prefill {int(qs[-1])} queries, max-abs err {err:.3e}")
+    assert err <= TOL[dtype]

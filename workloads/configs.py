@@ -44,10 +44,11 @@ class Workload:
     share_src: np.ndarray | None = None           # per seq: parent whose identities are shared
     query_lens: np.ndarray | None = None          # prefill: per seq, its last tokens that are queries
     description: str = ""
+    scale_value: float | None = None              # multiplier of q . k; None = 1 / sqrt(D)
 
     @property
     def scale(self) -> float:
-        return 1.0 / math.sqrt(self.D)
+        return 1.0 / math.sqrt(self.D) if self.scale_value is None else float(self.scale_value)
 
     @property
     def elem_bytes(self) -> int:
