@@ -81,7 +81,33 @@ def measured_traffic(workload: str, digest: str, kind: str = "paged_decode"):
     return rec.get("hbm_bytes_per_launch")
 
 
-def _compact_caches(w, tables, ctx, slot_ident):
+def _draw_rows(w, stream, ids, device):
+    """Generator rows for identities ``ids`` on the host: numpy's evaluation,
+    or (``device``) torch's on the GPU in chunks, spot-checked bit for bit
+    against numpy's on each chunk's first and last identity."""
+    from workloads import values as V
+
+    if device is None:
+        return V.draw_np(w.seed, stream, ids, w.H, w.D, w.dtype)
+    import torch
+
+    from oracle.oracle import STORAGE
+
+    out = np.empty((len(ids), w.H, w.D), dtype=STORAGE[w.dtype])
+    step = max(1, (1 << 28) // (w.H * w.D))
+    for i in range(0, len(ids), step):
+        part = ids[i:i + step]
+        t = V.draw_torch(w.seed, stream, torch.from_numpy(part).to(device), w.H, w.D, w.dtype, device)
+        host = t.cpu().numpy() if w.dtype == "f32" else t.view(torch.int16).cpu().numpy().view(np.uint16)
+        ends = np.unique([0, len(part) - 1])
+        want = V.draw_np(w.seed, stream, part[ends], w.H, w.D, w.dtype)
+        if not np.array_equal(host[ends].view(np.uint8), want.view(np.uint8)):
+            raise RuntimeError("device and host evaluations of the value generator differ")
+        out[i:i + len(part)] = host
+    return out
+
+
+def _compact_caches(w, tables, ctx, slot_ident, device=None):
     """Host K/V caches holding only the frames ``tables`` use, renumbered
     compactly (a relabelling of frames leaves attention unchanged), filled by
     the oracle side's own replay (``slot_ident``). Returns (k, v, tables)."""
@@ -89,8 +115,9 @@ def _compact_caches(w, tables, ctx, slot_ident):
     from workloads import values as V
 
     used = np.unique(np.concatenate([tables[i, :-(-int(c) // w.B)] for i, c in enumerate(ctx)]))
-    remap = {int(f): i for i, f in enumerate(used)}
-    tab = np.vectorize(lambda f: remap.get(int(f), 0))(tables).astype(np.int32)
+    remap = np.zeros(max(int(tables.max()), int(used.max())) + 1, dtype=np.int32)
+    remap[used] = np.arange(len(used), dtype=np.int32)
+    tab = np.where(tables >= 0, remap[np.clip(tables, 0, None)], 0).astype(np.int32)
     nb = len(used)
     nan = V.nan_bits(w.dtype)
     k = np.full((nb, w.B, w.H, w.D), nan, dtype=STORAGE[w.dtype])
@@ -99,8 +126,8 @@ def _compact_caches(w, tables, ctx, slot_ident):
     ids = slot_ident[slots_all]
     keep = ids >= 0
     new_slots = np.arange(nb * w.B, dtype=np.int64)[keep]
-    k.reshape(nb * w.B, w.H, w.D)[new_slots] = V.draw_np(w.seed, V.STREAM_K, ids[keep], w.H, w.D, w.dtype)
-    v.reshape(nb * w.B, w.H, w.D)[new_slots] = V.draw_np(w.seed, V.STREAM_V, ids[keep], w.H, w.D, w.dtype)
+    k.reshape(nb * w.B, w.H, w.D)[new_slots] = _draw_rows(w, V.STREAM_K, ids[keep], device)
+    v.reshape(nb * w.B, w.H, w.D)[new_slots] = _draw_rows(w, V.STREAM_V, ids[keep], device)
     return k, v, tab
 
 
@@ -113,6 +140,30 @@ def _cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def _cpu_info() -> dict:
+    """The host CPU as /proc/cpuinfo and the scheduler describe it."""
+    info = {}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if ":" not in line:
+                    if info:
+                        break  # first processor's block only
+                    continue
+                key, val = (x.strip() for x in line.split(":", 1))
+                if key in ("vendor_id", "cpu family", "model", "model name", "stepping",
+                           "cpu MHz", "cache size", "cpu cores", "siblings"):
+                    info[key] = val
+    except OSError:
+        pass
+    info["logical_cpus"] = os.cpu_count()
+    try:
+        info["usable_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    return info
 
 
 def _time_bounded(fn, budget_s: float, max_runs: int = 500):
@@ -197,31 +248,60 @@ def cpu_baseline_prefix(w, budget_s: float = 12.0):
     }
 
 
-def cpu_baseline(w, tables, ctx, budget_s: float = 12.0):
-    """The fp64 oracle on a bounded sample of the same workload (host cores)."""
+def cpu_baseline(w, device=None):
+    """The fp64 oracle on the whole decode step of workload ``w`` (every
+    sequence and head of its last attention point, through the oracle side's
+    own replay), on the host's cores: the median of 3 runs for the two
+    smallest workloads, one run for the others; also one thread, once, on
+    the two smallest. The oracle's host caches are filled from the value
+    generator (on ``device`` when given, checked against the host draw)."""
     from oracle import blockmgr as obm
     from oracle.oracle import default
     from workloads import values as V
 
     orc = default()
-    rng = np.random.default_rng(12345)
-    sample = np.sort(rng.choice(w.num_seqs, size=min(16, w.num_seqs), replace=False))
+    cores = orc.num_threads()
     snaps, _ = obm.replay(w)
     snap = snaps[-1]
-    sub_ctx = snap.context_lens[sample]
-    k, v, tab = _compact_caches(w, snap.tables[sample], sub_ctx, snap.slot_ident)
-    q = V.draw_np(w.seed, V.STREAM_Q, w.q_idents(0)[sample], w.H, w.D, w.dtype)
-    t, runs = _time_bounded(lambda: orc.paged_decode(q, k, v, tab, sub_ctx, w.B, w.scale, w.dtype),
-                            budget_s)
-    kv_bytes = 2 * w.H * w.D * w.elem_bytes * int(sub_ctx.sum())
-    return {
-        "value": kv_bytes / t / 1e9, "unit": "GB/s", "cores": orc.num_threads(), "kind": "oracle",
-        "cpu_model": _cpu_model(),
-        "sample": f"{len(sample)} of {w.num_seqs} sequences (all {w.H} heads, "
-                  f"{int(sub_ctx.sum())} tokens, {kv_bytes / 1e6:.1f} MB of KV), fp64 C oracle, "
-                  f"median of {runs} runs",
-        "seconds_per_sample": t,
+    ctx = snap.context_lens
+    t0 = time.perf_counter()
+    k, v, tab = _compact_caches(w, snap.tables, ctx, snap.slot_ident, device)
+    prep_s = time.perf_counter() - t0
+    q = V.draw_np(w.seed, V.STREAM_Q, w.q_idents(len(snaps) - 1), w.H, w.D, w.dtype)
+    small = int(ctx.sum()) * w.H <= 4_000_000  # the worked example and the batch-64 step
+
+    def run():
+        orc.paged_decode(q, k, v, tab, ctx, w.B, w.scale, w.dtype)
+
+    def timed(n):
+        ts = []
+        for _ in range(n):
+            t1 = time.perf_counter()
+            run()
+            ts.append(time.perf_counter() - t1)
+        return float(np.median(ts))
+
+    runs = 3 if small else 1
+    t = timed(runs)
+    kv_bytes = 2 * w.H * w.D * w.elem_bytes * int(ctx.sum())
+    res = {
+        "value": kv_bytes / t / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "cpu_model": _cpu_model(), "cpu": _cpu_info(),
+        "sample": f"the whole step: all {w.num_seqs} sequences x {w.H} heads "
+                  f"({int(ctx.sum())} tokens, {kv_bytes / 1e6:.1f} MB of KV), fp64 C oracle, "
+                  f"{'median of 3 runs' if runs == 3 else 'one run'}",
+        "seconds_per_step": t,
+        "host_cache_fill_s": round(prep_s, 3),
     }
+    if small:
+        orc.set_num_threads(1)
+        try:
+            t1 = timed(1)
+        finally:
+            orc.set_num_threads(cores)
+        res["one_thread"] = {"value": kv_bytes / t1 / 1e9, "unit": "GB/s", "seconds_per_step": t1,
+                             "sample": "the same whole step, one run on one thread"}
+    return res
 
 
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
@@ -893,8 +973,8 @@ def main():
                                  "decode steps) before timing"},
     }
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a sample")
-        res["cpu_baseline"] = cpu_baseline(w, pt.tables, pt.context_lens)
+        log("[bench] timing the CPU oracle on the whole step")
+        res["cpu_baseline"] = cpu_baseline(w, dev)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

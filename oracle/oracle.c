@@ -103,6 +103,15 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads the following calls use (n >= 1); for timing the oracle. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /*
  * Softmax attention of one query over n key/value rows (definition above).
  * q[e], key(j)[e] and val(j)[e] are given as strided views of stored arrays:

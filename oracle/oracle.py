@@ -51,6 +51,8 @@ class Oracle:
         L.oracle_kv_append.argtypes = [_P, _P, _P, _I64, _I, _I, _I, _I64, _I, _P, _P]
         L.oracle_gather.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I64, _I, _I, _P]
         L.oracle_widen.argtypes = [_P, _I64, _I, _P]
+        L.oracle_set_num_threads.argtypes = [_I]
+        L.oracle_set_num_threads.restype = None
         for f in ("oracle_paged_decode", "oracle_paged_decode_split", "oracle_dense_attention",
                   "oracle_paged_prefill",
                   "oracle_kv_append", "oracle_gather", "oracle_widen", "oracle_num_threads"):
@@ -63,6 +65,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        """OpenMP threads of the calls that follow (for timing)."""
+        self.lib.oracle_set_num_threads(int(n))
 
     def paged_decode(self, q, k_cache, v_cache, block_tables, context_lens, B: int,
                      scale: float, dtype: str) -> np.ndarray:
