@@ -687,7 +687,7 @@ def main():
 
     seq_order = grp_order = None
     if not args.decode_batch_order:
-        seq_order = torch.from_numpy(decode_order(pt.context_lens)).to(dev)
+        seq_order = torch.from_numpy(decode_order(pt.context_lens, pt.tables)).to(dev)
         if grouped:
             grp_order = torch.from_numpy(group_order(group_start, group_shared,
                                                      pt.context_lens)).to(dev)
@@ -944,7 +944,7 @@ def main():
         "ungrouped": ungrouped_ctx,
         "dispatch_order": ("batch order" if seq_order is None else
                            "longest first (driver.group_order)" if grouped else
-                           "longest first (driver.decode_order)"),
+                           "longest first, fork families together (driver.decode_order)"),
         "batch_order": batch_order_ctx,
         "kernels_us": {"partition": round(float(part_ms.mean()) * 1e3, 2),
                        "partition_kernel_alone": round(float(kern_ms.mean()) * 1e3, 2),

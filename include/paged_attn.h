@@ -106,8 +106,12 @@ typedef struct pa_decode_shape {
                                   paged_attn_decode_grouped). Values are clamped
                                   into range; a unit missing from it gets no output.
                                   Longest work first shortens the launch's tail;
-                                  with an order the default partition size also
-                                  grows (see paged_attn_partition_tokens).
+                                  sequences that share frames (forks of one
+                                  prompt) should stay adjacent in it, or their
+                                  shared reads drift apart in time and miss in
+                                  cache. With an order the default partition
+                                  size also grows (see
+                                  paged_attn_partition_tokens).
                                   Outputs equal the unordered call's at the same
                                   partition size, bit for bit. */
 } pa_decode_shape;

@@ -157,11 +157,34 @@ def share_groups(tables: np.ndarray, context_lens: np.ndarray, block_size: int,
     return np.asarray(starts, dtype=np.int32), np.asarray(shared, dtype=np.int32)
 
 
-def decode_order(context_lens) -> np.ndarray:
+def decode_order(context_lens, tables=None) -> np.ndarray:
     """Dispatch order for decode (``pa_decode_shape.dispatch_order``): the
-    sequences by context length, longest first, ties in batch order. int32 [S]."""
+    sequences by context length, longest first, ties in batch order. int32 [S].
+
+    With the batch's block ``tables``, sequences whose rows start with the
+    same frame (the branches of one prompt, "PagedAttention: Virtual Memory
+    Guide for LLM Inference", "2. Zero-Copy Branching via Copy-on-Write")
+    form a family that stays together: families by their longest member,
+    longest first (ties: the family whose first member comes first in the
+    batch), members longest first, then in batch order. Branches dispatched
+    together read their shared frames close in time, so the repeats hit in
+    cache (with ``PA_CACHE_REUSE``); sorted by length alone they drift apart.
+    Without shared first frames this is the plain length order."""
     ctx = np.asarray(context_lens, dtype=np.int64)
-    return np.argsort(-ctx, kind="stable").astype(np.int32)
+    S = len(ctx)
+    if tables is None or S == 0:
+        return np.argsort(-ctx, kind="stable").astype(np.int32)
+    tables = np.asarray(tables)
+    idx = np.arange(S, dtype=np.int64)
+    # family key: the first frame; a sequence with no token is its own family
+    key = np.where(ctx > 0, tables[:, 0].astype(np.int64), -1 - idx)
+    _, fam = np.unique(key, return_inverse=True)
+    fam_len = np.zeros(fam.max() + 1, dtype=np.int64)
+    np.maximum.at(fam_len, fam, ctx)
+    fam_first = np.full(fam.max() + 1, S, dtype=np.int64)
+    np.minimum.at(fam_first, fam, idx)
+    # np.lexsort sorts by the last key first
+    return np.lexsort((idx, -ctx, fam_first[fam], -fam_len[fam])).astype(np.int32)
 
 
 def group_order(group_start, group_shared, context_lens) -> np.ndarray:

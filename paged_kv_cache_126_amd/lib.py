@@ -230,8 +230,11 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_siz
     ``phase`` selects "both" (paged_attn_decode), "partitions" or "merge"
     (the two launches it is made of). ``cache_policy`` is PA_CACHE_REUSE when
     sequences of the batch share frames, else PA_CACHE_STREAM.
-    ``dispatch_order`` (int32 [S], e.g. ``driver.decode_order``) sets the order
+    ``dispatch_order`` (int32 [S], e.g. ``driver.decode_order(context_lens,
+    tables)``, which keeps the forks of one prompt together) sets the order
     the sequences are dispatched in; give the merge phase the same one.
+    Batches whose sequences share frames read them once per family with
+    ``paged_attn_decode_grouped`` instead.
     """
     _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out)
     shape = make_shape(q, k_cache, block_tables, max_context_len, dtype_code(out), partition_tokens,

@@ -96,7 +96,7 @@ def run_gpu(w, partition_tokens: int = 0, out_dtype=None, phases: bool = False, 
         rng = np.random.default_rng(w.seed + pt.step)
         seq_ord = grp_ord = None
         if order == "longest":
-            seq_ord = decode_order(pt.context_lens)
+            seq_ord = decode_order(pt.context_lens, pt.tables)
             grp_ord = group_order(gs, gsh, pt.context_lens)
         elif order == "random":
             seq_ord = rng.permutation(w.num_seqs).astype(np.int32)

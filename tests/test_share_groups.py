@@ -162,4 +162,52 @@ def test_decode_and_group_orders():
         assert sorted(o.tolist()) == list(range(S)) and o.dtype == np.int32
         key = [(-int(ctx[i]), int(i)) for i in o]
         assert key == sorted(key)
+        # tables with distinct first frames: the same order
+        tables = rng.permutation(1000)[:S * 3].reshape(S, 3).astype(np.int32)
+        assert decode_order(ctx, tables).tolist() == o.tolist()
+
+
+def test_decode_order_keeps_fork_families_together():
+    """With the block tables, sequences that share their first frame (forks
+    of one prompt) are dispatched next to each other; families go by their
+    longest member, members longest first. Hand example, then the
+    shared-prefix workload's plan and random fork structures."""
+    from paged_kv_cache_126_amd.driver import decode_order
+
+    # families: {0, 2, 4} on frame 7 (ctx 10, 30, 20), {1} (ctx 25), {3, 5} on
+    # frame 9 (ctx 30, 5), {6} empty
+    tables = np.array([[7, 1], [8, 2], [7, 3], [9, 4], [7, 5], [9, 6], [0, 0]], dtype=np.int32)
+    ctx = np.array([10, 25, 30, 30, 20, 5, 0])
+    assert decode_order(ctx, tables).tolist() == [2, 4, 0, 3, 5, 1, 6]
+
+    def check(order, tables, ctx):
+        S = len(ctx)
+        assert sorted(order.tolist()) == list(range(S)) and order.dtype == np.int32
+        fam = [int(tables[s, 0]) if ctx[s] > 0 else -1 - s for s in order]
+        seen, prev = set(), None
+        for f in fam:  # every family is one contiguous run
+            assert f == prev or f not in seen
+            seen.add(f)
+            prev = f
+        runs = []
+        for s, f in zip(order, fam):
+            if runs and runs[-1][0] == f:
+                runs[-1][1].append(int(ctx[s]))
+            else:
+                runs.append((f, [int(ctx[s])]))
+        longest = [max(r) for _, r in runs]
+        assert longest == sorted(longest, reverse=True)
+        for _, r in runs:
+            assert r == sorted(r, reverse=True)
+
+    events, _ = plan(C.small(4))
+    pt = [e for e in events if isinstance(e, AttendPoint)][-1]
+    check(decode_order(pt.context_lens, pt.tables), pt.tables, pt.context_lens)
+    rng = np.random.default_rng(78)
+    for _ in range(30):
+        S = int(rng.integers(1, 30))
+        firsts = rng.integers(0, max(1, S // 2), size=S)
+        tables = np.stack([firsts, rng.integers(0, 100, size=S)], axis=1).astype(np.int32)
+        ctx = rng.integers(0, 60, size=S)
+        check(decode_order(ctx, tables), tables, ctx)
 
