@@ -19,15 +19,16 @@
 // every wavefront
 //   1. forms S^T = K Q^T (32 keys x 32 queries) with D/16 MFMA 32x32x16
 //      steps; Q^T stays in registers as the B operand, so each lane owns one
-//      query column and 16 of the tile's keys,
+//      query column and 16 of the tile's keys. The K rows enter in a
+//      permuted order chosen so that those 16 keys come out in the B-operand
+//      layout of step 3,
 //   2. applies the causal mask and an online softmax per query (the two
-//      lanes sharing a query exchange one value),
-//   3. accumulates O^T += V^T P^T with P^T moved from the accumulator layout
-//      into the B-operand layout by one exchange between the wavefront's
-//      halves. In bf16, P is split into a high part and the residual (two
-//      MFMAs), which keeps ~16 significant bits of every softmax weight; in
-//      fp16 one rounding keeps 11, and the normaliser sums the rounded
-//      weights.
+//      lanes sharing a query exchange one value for the maximum; each keeps
+//      its own share of the normaliser, added once at the end),
+//   3. accumulates O^T += V^T P^T. In bf16, P is split into a high part and
+//      the residual (two MFMAs), which keeps ~16 significant bits of every
+//      softmax weight; in fp16 one rounding keeps 11, and the normaliser
+//      sums the rounded weights.
 // Matrix layouts (verified on the device): for v_mfma_f32_32x32x16, A[i][k]
 // sits in lane i + 32 * (k / 8), element k % 8; B[k][j] in lane
 // j + 32 * (k / 8), element k % 8; D[i][j] in lane j + 32 * ((i / 4) % 2),
@@ -305,6 +306,12 @@ void prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<u32x4*>(&lds_v[key][8 * c]) = pv[i];
     }
   };
+  // Score rows in a permuted key order: row i = 8 u + 4 v + e (u < 4, v < 2,
+  // e < 4) holds key 16 (u / 2) + 8 v + 4 (u % 2) + e. The accumulator gives
+  // lane (query, half) rows 8 u + 4 half + e as elements e + 4 u, so its
+  // elements 8 j .. 8 j + 7 are keys 16 j + 8 half + [0, 8): the layout the
+  // weighted sum's B operand needs, with no exchange between lanes.
+  const int krow = 16 * (col / 16) + 8 * ((col / 4) % 2) + 4 * ((col / 8) % 2) + col % 4;
   fetch(0);
   stage(0);
   __syncthreads();
@@ -321,7 +328,7 @@ void prefill_kernel(PrefillArgs a) {
       for (int t = 0; t < 16; ++t) st[t] = 0.f;
 #pragma unroll
       for (int step = 0; step < kSteps; ++step) {
-        const u32x4 kbits = *reinterpret_cast<const u32x4*>(&lds_k[col][16 * step + 8 * half]);
+        const u32x4 kbits = *reinterpret_cast<const u32x4*>(&lds_k[krow][16 * step + 8 * half]);
         st = M::run(M::from_bits(kbits), qb[step], st);
       }
       // causal mask + online softmax for the lane's query
@@ -337,7 +344,7 @@ void prefill_kernel(PrefillArgs a) {
       } else {
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-          const int key = k0 + (t % 4) + 8 * (t / 4) + 4 * half;
+          const int key = k0 + 16 * (t / 8) + 8 * half + t % 8;
           x[t] = (q_ok && key <= my_pos) ? st[t] : -__builtin_inff();
           tmax = fmaxf(tmax, x[t]);
         }
@@ -368,19 +375,13 @@ void prefill_kernel(PrefillArgs a) {
         // masked keys weigh exactly 0 (with a zero scale, -inf * 0 would be NaN)
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-          const int key = k0 + (t % 4) + 8 * (t / 4) + 4 * half;
+          const int key = k0 + 16 * (t / 8) + 8 * half + t % 8;
           x[t] = (q_ok && key <= my_pos) ? x[t] : 0.f;
         }
       }
 
-      // P^T into the B-operand layout: for keys 16j .. 16j+15 the lower half
-      // of the wavefront needs keys 16j + [0,8), the upper half 16j + [8,16);
-      // the accumulator holds keys (t%4) + 8(t/4) + 4*half, so the lower
-      // half's elements 4-7 (of each 8) swap with the upper half's 0-3.
-#pragma unroll
-      for (int g = 0; g < 16; g += 8)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) swap_halves(x[g + i], x[g + i + 4]);
+      // x[8j .. 8j+7] are the weights of keys 16j + 8*half + [0, 8): already
+      // the B-operand layout of the weighted sum's k-step j (see krow).
       // bf16 keeps 8 significant bits: P = hi + lo per pair of weights, hi
       // rounded to bf16 and lo the rounded residual (x - hi is exact in
       // fp32), two MFMAs. fp16 keeps 11: one rounding, one MFMA, and l sums
@@ -407,7 +408,7 @@ void prefill_kernel(PrefillArgs a) {
             psum = __builtin_amdgcn_fdot2(hp, typename M::pair{1, 1}, psum, false);
           }
         }
-      l += sum_halves(psum);
+      l += psum;  // this lane's share; the two halves are added at the end
       // O^T += V^T P^T. The V^T operand (8 consecutive keys per lane at one
       // head-dim element) comes from the row-major V tile through transposing
       // LDS reads: in each group of 16 lanes, a 64-bit transpose read hands
@@ -439,6 +440,7 @@ void prefill_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
+  l = sum_halves(l);
   if (!q_ok) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int64_t orow = (static_cast<int64_t>(q0) + my_q) * a.num_heads + h;
@@ -454,6 +456,7 @@ void prefill_kernel(PrefillArgs a) {
         static_cast<uint16_t*>(a.out)[orow * D + d] = static_cast<uint16_t>(narrow_bits(T{}, r));
     }
 }
+
 
 template <typename T, int D>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
