@@ -12,6 +12,10 @@ Inputs are synthetic and seeded (see workloads/): context lengths uniform in
 [1, 2048], frames drawn from a randomly permuted pool of 20,000, q/k/v
 standard-normal values rounded to bf16.
 
+With the default workload the run then times workloads 3-8 (below), each in
+a child process with the same --steps/--warmup, and adds their figures to the
+line under "other_workloads" (--no-others skips this).
+
 Other workloads (--workload N): 1 the worked example, 3 eight 32k-token
 sequences, 4 forks of shared prompts (through paged_attn_decode_grouped
 unless --ungrouped), 5 batch 256 with the step's kv_append (--permuted-pool
@@ -28,6 +32,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -306,6 +311,77 @@ def cpu_baseline(w, device=None):
 
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
 
+def prefill_roofline(w, flops: int, compulsory: int, kernel_ms: float, traffic) -> dict:
+    """Roofline of one prefill launch. The attainable rate is the lower of the
+    matrix peak and the HBM peak times the launch's intensity (algorithmic
+    flops over compulsory bytes); ``bound`` names that roof, and
+    ``achieved``/``peak`` are in its unit (compulsory bytes per second for an
+    HBM-bound launch). bf16 weights enter the weighted sum as a high part and
+    a residual, so the matrix cores issue 1.5x the algorithmic flops."""
+    sec = kernel_ms * 1e-3
+    tflops = flops / sec / 1e12
+    intensity = flops / compulsory
+    hbm_roof_tflops = HBM_PEAK_GBS * 1e9 * intensity / 1e12
+    issued = flops * (1.5 if w.dtype == "bf16" else 1.0)
+    out = {"kernel": "prefill_kernel"}
+    if hbm_roof_tflops < MFMA_PEAK_TFLOPS:
+        gbs = compulsory / sec / 1e9
+        out.update(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                   frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        out.update(bound="mfma", achieved=round(tflops, 2), peak=MFMA_PEAK_TFLOPS,
+                   unit="TFLOP/s", frac=round(tflops / MFMA_PEAK_TFLOPS, 4))
+    out.update(traffic=traffic, launch_us=round(kernel_ms * 1e3, 2),
+               algorithmic_flops_per_launch=flops, compulsory_bytes_per_launch=compulsory,
+               intensity_flop_per_byte=round(intensity, 1),
+               achieved_tflops=round(tflops, 2),
+               attainable_tflops=round(min(MFMA_PEAK_TFLOPS, hbm_roof_tflops), 1),
+               frac_of_mfma_peak=round(tflops / MFMA_PEAK_TFLOPS, 4),
+               mfma_issued_flops_per_launch=int(issued),
+               mfma_issued_frac_of_mfma_peak=round(issued / sec / 1e12 / MFMA_PEAK_TFLOPS, 4))
+    return out
+
+
+OTHER_WORKLOADS = (3, 4, 5, 6, 7, 8)
+
+
+def other_workloads(args) -> dict:
+    """Time the other workloads, each in a child process running this script
+    (after the headline's timed region, one at a time), and keep the figures
+    that summarise each: the rate, the step time and the dominant kernel's
+    roofline."""
+    out = {}
+    for wl in OTHER_WORKLOADS:
+        cmd = [sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--workload", str(wl),
+               "--steps", str(args.steps), "--warmup", str(args.warmup), "--no-cpu-baseline",
+               "--no-others"]
+        if args.no_flush:
+            cmd.append("--no-flush")
+        log(f"[bench] other workload {wl}: {' '.join(cmd[2:])}")
+        t0 = time.perf_counter()
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
+        lines = [x for x in r.stdout.splitlines() if x.startswith("{")]
+        if r.returncode != 0 or not lines:
+            out[str(wl)] = {"error": f"exit {r.returncode}: {r.stderr.strip()[-300:]}"}
+            log(f"[bench] other workload {wl} failed (exit {r.returncode})")
+            continue
+        res = json.loads(lines[-1])
+        roof = res.get("roofline") or {}
+        keep = {
+            "workload": res["config"].get("workload"), "metric": res["metric"],
+            "value": res["value"], "unit": res["unit"], "ms_per_step": res["ms_per_step"],
+            "dtype": res["dtype"],
+            "roofline": {k: roof.get(k) for k in ("kernel", "bound", "achieved", "peak", "unit",
+                                                   "frac", "launch_us") if k in roof},
+        }
+        for k in ("pct_hbm_peak", "speedup_vs_no_caching", "dispatch_order"):
+            if k in res:
+                keep[k] = res[k]
+        out[str(wl)] = keep
+        log(f"[bench] other workload {wl} ({keep['workload']}): {keep['value']} {keep['unit']}, "
+            f"{keep['ms_per_step'] * 1e3:.1f} us/step, {time.perf_counter() - t0:.1f} s")
+    return out
+
 
 def bench_prefill(args, w, pt, cache, dev):
     """Prefill workloads: time paged_attn_prefill (one launch per step)."""
@@ -389,12 +465,8 @@ def bench_prefill(args, w, pt, cache, dev):
                            "costliest sequence first, its later query tiles first "
                            "(driver.prefill_order)"),
         "default_order_us_per_step": None if batch_order_ms is None else round(batch_order_ms * 1e3, 2),
-        "roofline": {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tflops, 2),
-                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name, digest, "paged_prefill"),
-                     "algorithmic_flops_per_launch": flops, "launch_us": round(kms * 1e3, 2),
-                     "compulsory_bytes_per_launch": compulsory},
+        "roofline": prefill_roofline(w, flops, compulsory, kms, measured_traffic(
+            w.name, digest, "paged_prefill")),
         "kernel_source_digest": digest,
         "cpu_baseline": None,
     }
@@ -544,7 +616,9 @@ def bench_prefix(args, w, dev):
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
                      "algorithmic_flops_per_step": on["flops"],
-                     "launch_us_per_step": round(on["kernel_ms"] * 1e3, 2)},
+                     "launch_us_per_step": round(on["kernel_ms"] * 1e3, 2),
+                     "mfma_issued_frac_of_mfma_peak": round(
+                         tflops * (1.5 if w.dtype == "bf16" else 1.0) / MFMA_PEAK_TFLOPS, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -578,6 +652,9 @@ def main():
                     help="time paged_attn_decode even where sequences share frames (by default "
                          "forked sequences go through paged_attn_decode_grouped)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="with the default workload, skip timing the other workloads (3-8) in "
+                         "child processes after the headline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run one plain device-to-device copy of BYTES (a known-size "
                          "reference for hardware traffic counters)")
@@ -972,6 +1049,10 @@ def main():
                          "what": "block manager replay of the whole schedule (prefill, forks, "
                                  "decode steps) before timing"},
     }
+    default_run = (args.workload == 2 and not args.block_size and not args.partition_tokens
+                   and not args.decode_batch_order and not args.ungrouped)
+    if default_run and not args.no_others:
+        res["other_workloads"] = other_workloads(args)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the whole step")
         res["cpu_baseline"] = cpu_baseline(w, dev)
