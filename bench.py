@@ -12,7 +12,7 @@ Inputs are synthetic and seeded (see workloads/): context lengths uniform in
 [1, 2048], frames drawn from a randomly permuted pool of 20,000, q/k/v
 standard-normal values rounded to bf16.
 
-With the default workload the run then times workloads 3-8 (below), each in
+With the default workload the run then times workloads 1 and 3-8 (below), each in
 a child process with the same --steps/--warmup, and adds their figures to the
 line under "other_workloads" (--no-others skips this).
 
@@ -342,7 +342,7 @@ def prefill_roofline(w, flops: int, compulsory: int, kernel_ms: float, traffic) 
     return out
 
 
-OTHER_WORKLOADS = (3, 4, 5, 6, 7, 8)
+OTHER_WORKLOADS = (1, 3, 4, 5, 6, 7, 8)
 
 
 def other_workloads(args) -> dict:
@@ -653,7 +653,7 @@ def main():
                          "forked sequences go through paged_attn_decode_grouped)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true",
-                    help="with the default workload, skip timing the other workloads (3-8) in "
+                    help="with the default workload, skip timing the other workloads (1, 3-8) in "
                          "child processes after the headline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="first run one plain device-to-device copy of BYTES (a known-size "
