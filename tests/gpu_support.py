@@ -187,21 +187,42 @@ def oracle_prefill(w, pad):
     return snap, orc.paged_prefill(q, k, v, snap.tables, snap.context_lens, qs, w.B, w.scale, w.dtype)
 
 
-def oracle_prefill_sampled(w, context_lens, picks):
-    """fp64 outputs for sampled (seq, query index r, head): the contiguous
-    definition over tokens 0 .. position of the query."""
+def _widen_rows(w, ids, dev):
+    """fp64 K and V rows [n, H, D] of identities ``ids`` (generator rows drawn
+    on the device and checked against the host draw, widened exactly by the
+    oracle's decoders)."""
+    import torch
+
     orc = oracle_default()
-    res = {}
-    for s, r, h in picks:
-        n = int(w.query_lens[s])
-        pos = int(context_lens[s]) - n + r
-        ids = w.idents(s, np.arange(pos + 1))
-        k = V.draw_np(w.seed, V.STREAM_K, ids, w.H, w.D, w.dtype, heads=[h])
-        v = V.draw_np(w.seed, V.STREAM_V, ids, w.H, w.D, w.dtype, heads=[h])
-        q = V.draw_np(w.seed, V.STREAM_Q, w.idents(s, [pos]), w.H, w.D, w.dtype, heads=[h])
-        o = orc.dense_attention(q, k, v, np.array([0, pos + 1], dtype=np.int64), w.scale, w.dtype)
-        res[(s, r, h)] = o[0, 0]
-    return res
+    ids = np.asarray(ids, dtype=np.int64)
+    idt = torch.from_numpy(ids).to(dev)
+    k = orc.widen(_rows_checked(w, ids, idt, V.STREAM_K, dev), w.dtype)
+    v = orc.widen(_rows_checked(w, ids, idt, V.STREAM_V, dev), w.dtype)
+    return k, v
+
+
+def oracle_prefill_full(w, context_lens, device: str = "cuda:0"):
+    """fp64 output [T, H, D] of prefill workload ``w``: every query of every
+    sequence, by the dense causal form over the sequence's logical rows
+    (oracle/dense.py, pinned against the C oracle)."""
+    import torch
+
+    from oracle import dense
+
+    orc = oracle_default()
+    dev = torch.device(device)
+    qs, qids = w.prefill_queries(context_lens)
+    q_all = orc.widen(V.draw_np(w.seed, V.STREAM_Q, qids, w.H, w.D, w.dtype), w.dtype)
+    scale = float(np.float32(w.scale))
+    out = np.empty((int(qs[-1]), w.H, w.D), dtype=np.float64)
+    for s in range(len(context_lens)):
+        n = int(qs[s + 1] - qs[s])
+        if n == 0:
+            continue
+        ctx = int(context_lens[s])
+        k, v = _widen_rows(w, w.idents(s, np.arange(ctx)), dev)
+        out[qs[s]:qs[s + 1]] = dense.causal_attention(q_all[qs[s]:qs[s + 1]], k, v, scale, ctx - n)
+    return out
 
 
 def oracle_caches(w, snap):
@@ -385,10 +406,52 @@ def _caches_from_idents(w, NB, slot_ident):
     return k, v
 
 
+def oracle_prefix_full(w, rd, device: str = "cuda:0"):
+    """fp64 outputs of one prefix-cache round ``rd`` (a driver PrefillRound):
+    the prefill output [T, H, D] over every written position of every
+    request, and each decode step's output [len(step), H, D], by the dense
+    causal form over each conversation's logical rows (oracle/dense.py).
+    A conversation's decode queries sit at the positions right after its
+    prompt, so one causal call per conversation covers the prefill queries
+    and every decode query of the round."""
+    import torch
+
+    from oracle import dense
+
+    orc = oracle_default()
+    dev = torch.device(device)
+    scale = float(np.float32(w.scale))
+    T = int(rd.query_start[-1])
+    pre = np.empty((T, w.H, w.D), dtype=np.float64)
+    steps = rd.decode or []
+    final = {int(c): int(n) for i, (c, n) in enumerate(zip(rd.seqs, rd.context_lens))}
+    for st in steps:
+        for c, n in zip(st.writes.seqs, st.context_lens):
+            final[int(c)] = max(final[int(c)], int(n))
+    outs = {}
+    for i, c in enumerate(rd.seqs):
+        c = int(c)
+        lo, ctx, last = int(rd.reused[i]), int(rd.context_lens[i]), final[c]
+        k, v = _widen_rows(w, w.idents(c, np.arange(last)), dev)
+        q = orc.widen(V.draw_np(w.seed, V.STREAM_Q, w.idents(c, np.arange(lo, last)), w.H, w.D,
+                                w.dtype), w.dtype)
+        o = dense.causal_attention(q, k, v, scale, lo)  # queries at positions lo .. last - 1
+        pre[rd.query_start[i]:rd.query_start[i + 1]] = o[:ctx - lo]
+        outs[c] = (lo, o)
+    dec = []
+    for st in steps:
+        d = np.empty((len(st.writes.seqs), w.H, w.D), dtype=np.float64)
+        for j, (c, n) in enumerate(zip(st.writes.seqs, st.context_lens)):
+            lo, o = outs[int(c)]
+            d[j] = o[int(n) - 1 - lo]
+        dec.append(d)
+    return pre, dec
+
+
 def oracle_prefix_sampled(w, picks):
     """fp64 outputs for sampled (conversation, position, head): causal
     attention of that token's query over tokens 0 .. position of its
-    conversation, by the contiguous definition."""
+    conversation, by the C oracle's contiguous definition."""
     orc = oracle_default()
     res = {}
     for c, pos, h in picks:

@@ -40,3 +40,13 @@ def test_oracle_blockmgr_pin(pin):
     from oracle import blockmgr
 
     pin(blockmgr)
+
+
+from tests import dense_pins  # noqa: E402
+
+
+@pytest.mark.parametrize("pin", dense_pins.ALL, ids=lambda p: p.__name__)
+def test_oracle_dense_pin(pin):
+    from oracle import dense
+
+    pin(dense)

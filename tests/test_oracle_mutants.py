@@ -16,6 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 ORACLE_C = os.path.join(ROOT, "oracle", "oracle.c")
 BLOCKMGR = os.path.join(ROOT, "oracle", "blockmgr.py")
 PREFIXCACHE = os.path.join(ROOT, "oracle", "prefixcache.py")
+DENSE = os.path.join(ROOT, "oracle", "dense.py")
 
 C_MUTANTS = {
     "offset_in_block": ("int64_t off = i % B;", "int64_t off = (i + 1) % B;"),
@@ -87,6 +88,17 @@ PC_MUTANTS = {
 }
 
 
+# Dense causal attention (oracle/dense.py).
+DENSE_MUTANTS = {
+    "mask_excludes_own_key": ("np.arange(last)[None, :] > pos[:, None]",
+                              "np.arange(last)[None, :] >= pos[:, None]"),
+    "scale_dropped": ("a = scale * np.matmul(", "a = np.matmul("),
+    "v_read_from_k": ("o = np.matmul(w, vh) / z", "o = np.matmul(w, kh) / z"),
+    "normaliser_dropped": ("o = np.matmul(w, vh) / z", "o = np.matmul(w, vh)"),
+    "first_ignored": ("pos = first + np.arange(n)", "pos = np.arange(n)"),
+}
+
+
 def _mutate(src_path, find, repl, dst_path):
     with open(src_path) as f:
         src = f.read()
@@ -130,13 +142,22 @@ def _run_pc_mutant(name, tmp):
     return r.returncode, r.stdout + r.stderr
 
 
-RUNNERS = {"c": _run_c_mutant, "py": _run_py_mutant, "pc": _run_pc_mutant}
+def _run_dense_mutant(name, tmp):
+    find, repl = DENSE_MUTANTS[name]
+    dst = os.path.join(tmp, f"dense_{name}.py")
+    _mutate(DENSE, find, repl, dst)
+    r = subprocess.run([sys.executable, "-m", "tests.dense_pins", dst], cwd=ROOT,
+                       capture_output=True, text=True, timeout=300)
+    return r.returncode, r.stdout + r.stderr
+
+
+RUNNERS = {"c": _run_c_mutant, "py": _run_py_mutant, "pc": _run_pc_mutant, "dense": _run_dense_mutant}
 
 
 def test_every_oracle_mutant_is_caught(tmp_path):
     tmp = str(tmp_path)
     jobs = ([("c", n) for n in C_MUTANTS] + [("py", n) for n in PY_MUTANTS]
-            + [("pc", n) for n in PC_MUTANTS])
+            + [("pc", n) for n in PC_MUTANTS] + [("dense", n) for n in DENSE_MUTANTS])
     with ThreadPoolExecutor(max_workers=6) as ex:
         futs = {(k, n): ex.submit(RUNNERS[k], n, tmp) for k, n in jobs}
     survivors = []
@@ -157,5 +178,8 @@ def test_unmutated_oracle_passes_pin_runner():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     r = subprocess.run([sys.executable, "-m", "tests.prefixcache_pins", PREFIXCACHE], cwd=ROOT,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    r = subprocess.run([sys.executable, "-m", "tests.dense_pins", DENSE], cwd=ROOT,
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
