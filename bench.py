@@ -311,6 +311,48 @@ def cpu_baseline(w, device=None):
 
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
 
+def frame_patterns(w, buf, sink, part_tokens: int, flush, args, dev) -> dict:
+    """Read bandwidth of three frame access patterns over ``buf`` (the step's
+    K/V size, frames of the workload's geometry, a seeded random frame order;
+    pa_frame_read, kernel-stamped, cold): one head's B rows of a token-major
+    [.., B, H, D] frame (the decode kernel's pattern and the target's layout),
+    one head's B rows of a head-major [.., H, B, D] frame (contiguous, as in
+    page 1's per-head K and V caches), and whole frames. A workgroup reads
+    one head of the frames one partition covers, or, for whole frames, the
+    same bytes in 1/H as many frames."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+
+    row = w.D * w.elem_bytes
+    frame = w.B * w.H * row
+    n = (buf.numel() * buf.element_size()) // frame
+    fpu = max(1, -(-part_tokens // w.B))
+    order = torch.from_numpy(np.random.default_rng(7).permutation(n).astype(np.int32)).to(dev)
+    specs = {
+        "token_major_one_head": (w.H, row, w.B, w.H * row, row, fpu),
+        "head_major_one_head": (w.H, w.B * row, w.B, row, row, fpu),
+        "whole_frames": (1, 0, w.B * w.H, row, row, max(1, fpu // w.H)),
+    }
+    out = {"what": ("pa_frame_read over the step's K/V bytes in a random frame order, "
+                    f"{frame} B frames, one workgroup per (head, {fpu} frames)"), "GB/s": {}}
+    for name, (g, gs, pc, ps, pb, f) in specs.items():
+        for _ in range(3):
+            pkv.lib.frame_read(buf, order, frame, g, gs, pc, ps, pb, f, sink)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(20)]
+        for c0, c1 in evs:
+            if not args.no_flush:
+                flush()
+            with pkv.kernel_timing(c0, c1):
+                pkv.lib.frame_read(buf, order, frame, g, gs, pc, ps, pb, f, sink)
+        torch.cuda.synchronize()
+        us = float(np.mean([c0.elapsed_time(c1) for c0, c1 in evs])) * 1e3
+        out["GB/s"][name] = round(n * frame / us / 1e3, 1)
+    log(f"[bench] frame access patterns: " + ", ".join(f"{k} {v:.0f} GB/s" for k, v in out["GB/s"].items()))
+    return out
+
+
 def prefill_roofline(w, flops: int, compulsory: int, kernel_ms: float, traffic) -> dict:
     """Roofline of one prefill launch. The attainable rate is the lower of the
     matrix peak and the HBM peak times the launch's intensity (algorithmic
@@ -377,6 +419,8 @@ def other_workloads(args) -> dict:
         for k in ("pct_hbm_peak", "speedup_vs_no_caching", "dispatch_order"):
             if k in res:
                 keep[k] = res[k]
+        if "access_patterns" in roof:
+            keep["roofline"]["access_patterns_GB/s"] = roof["access_patterns"]["GB/s"]
         out[str(wl)] = keep
         log(f"[bench] other workload {wl} ({keep['workload']}): {keep['value']} {keep['unit']}, "
             f"{keep['ms_per_step'] * 1e3:.1f} us/step, {time.perf_counter() - t0:.1f} s")
@@ -935,6 +979,7 @@ def main():
     torch.cuda.synchronize()
     ceil_us = float(np.mean([c0.elapsed_time(c1) for c0, c1 in cevs])) * 1e3
     ceil_gbs = kv_bytes_unique / ceil_us / 1e3
+    patterns = frame_patterns(w, ceil_buf, ceil_sink, part_tokens, flush, args, dev)
     del ceil_buf
     log(f"[bench] streaming-read ceiling over {kv_bytes_unique / 1e9:.3f} GB: {ceil_us:.1f} us, "
         f"{ceil_gbs:.0f} GB/s")
@@ -1042,6 +1087,7 @@ def main():
                              "what": "pa_stream_read: the same non-temporal 16-byte loads over "
                                      "as many bytes, in order, nothing else"},
             "frac_of_read_ceiling": round(part_gbs / ceil_gbs, 4),
+            "access_patterns": patterns,
         },
         "kernel_source_digest": digest,
         "cow_frame_copies": cow,

@@ -375,11 +375,42 @@ pa_status paged_gather(const void* cache, const int32_t* block_tables,
 pa_status pa_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 /*
+ * pa_frame_read: benchmark support, not part of the attention path. Reads a
+ * device buffer of `bytes` bytes holding num_frames frames of frame_bytes
+ * each, in the order frame_order (device int32 [num_frames]; entries are
+ * clamped into [0, num_frames)), with the decode kernel's non-temporal
+ * 16-byte loads and no other work. Frames are read in units of
+ * frames_per_unit consecutive entries of frame_order; one workgroup per
+ * (group g, unit) reads from each of its frames f the `pieces` pieces of
+ * piece_bytes at f * frame_bytes + g * group_stride + p * piece_stride
+ * (p < pieces), its 8 wavefronts taking the frames round robin. So the
+ * byte pattern of one head's rows in a [NB, B, H, D] cache (group_stride =
+ * one row of one head, piece_stride = one token's row of all heads), in a
+ * head-major [NB, H, B, D] one (group_stride = B rows, piece_stride = one
+ * row), or of whole frames (one group) can be timed on the same bytes
+ * ("PagedAttention: Virtual Memory Guide for LLM Inference", "3.
+ * PagedAttention CUDA Kernel Execution", shows a K cache split per head and
+ * "1. Sizing the Block Dimension" ties the block size to coalescing).
+ * Strides, frame_bytes and piece_bytes must be multiples of 16; every piece
+ * must lie inside its frame, num_frames * frame_bytes <= bytes, at most
+ * 65,535 units (else PA_EINVAL); buf 16-byte aligned (PA_EALIGN). `sink`
+ * (device uint32) is written only in a practically impossible case.
+ * Stamps the launch events of pa_set_launch_events like pa_stream_read.
+ * num_frames == 0 queues nothing.
+ */
+pa_status pa_frame_read(const void* buf, int64_t bytes, const int32_t* frame_order,
+                        int64_t num_frames, int64_t frame_bytes, int32_t groups,
+                        int64_t group_stride, int32_t pieces, int64_t piece_stride,
+                        int32_t piece_bytes, int32_t frames_per_unit, uint32_t* sink,
+                        void* stream);
+
+/*
  * pa_set_launch_events: kernel-accurate timing, for benchmarks and
  * profilers. While set on a thread, every launch that thread makes of the
  * decode partition kernel (paged_attn_decode, paged_attn_decode_partitions;
  * the grouped partition kernel of paged_attn_decode_grouped), of the prefill
- * kernel (paged_attn_prefill) or of pa_stream_read's kernel stamps `start`
+ * kernel (paged_attn_prefill) or of pa_stream_read's or pa_frame_read's
+ * kernel stamps `start`
  * with the kernel's own start time and `stop` with its end time (hipEvent_t handles
  * owned by the caller, created with timing enabled; either may be NULL).
  * An event plainly recorded on the stream around a launch also counts the

@@ -7,6 +7,7 @@
 
 #include "paged_attn.h"
 #include "pa_launch.h"
+#include "pa_probes.h"
 
 namespace pa {
 
@@ -437,6 +438,33 @@ pa_status pa_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* s
   if (bytes == 0) return PA_OK;
   if (!aligned(buf, 16)) return PA_EALIGN;
   return from_hip(pa::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_frame_read(const void* buf, int64_t bytes, const int32_t* frame_order,
+                        int64_t num_frames, int64_t frame_bytes, int32_t groups,
+                        int64_t group_stride, int32_t pieces, int64_t piece_stride,
+                        int32_t piece_bytes, int32_t frames_per_unit, uint32_t* sink,
+                        void* stream) {
+  if (bytes < 0 || num_frames < 0 || frame_bytes <= 0 || groups <= 0 || pieces <= 0 ||
+      piece_bytes <= 0 || frames_per_unit <= 0 || group_stride < 0 || piece_stride < 0)
+    return PA_EINVAL;
+  if (frame_bytes % 16 || group_stride % 16 || piece_stride % 16 || piece_bytes % 16)
+    return PA_EINVAL;
+  if (frame_bytes > (int64_t{1} << 40) || group_stride > frame_bytes || piece_stride > frame_bytes)
+    return PA_EINVAL;
+  // every piece lies inside its frame, every frame inside the buffer
+  if (static_cast<int64_t>(groups - 1) * group_stride + static_cast<int64_t>(pieces - 1) * piece_stride +
+          piece_bytes > frame_bytes)
+    return PA_EINVAL;
+  if (num_frames > bytes / frame_bytes) return PA_EINVAL;
+  if (static_cast<int64_t>(pieces) * (piece_bytes / 16) > 0x7FFFFFFFLL) return PA_EINVAL;
+  if ((num_frames + frames_per_unit - 1) / frames_per_unit > kMaxGridYZ) return PA_EINVAL;
+  if (num_frames == 0) return PA_OK;
+  if (!buf || !frame_order || !sink) return PA_EINVAL;
+  if (!aligned(buf, 16) || !aligned(frame_order, 4) || !aligned(sink, 4)) return PA_EALIGN;
+  return from_hip(pa::launch_frame_read(buf, frame_order, num_frames, frame_bytes, groups,
+                                        group_stride, pieces, piece_stride, piece_bytes,
+                                        frames_per_unit, sink, static_cast<hipStream_t>(stream)));
 }
 
 pa_status pa_set_launch_events(void* start, void* stop) {

@@ -21,7 +21,7 @@ EXPORTS = (
     "pa_status_string", "pa_abi_version", "kv_append", "kv_copy_blocks", "paged_attn_workspace_size",
     "paged_attn_partition_tokens", "paged_attn_decode", "paged_attn_decode_partitions",
     "paged_attn_merge", "paged_attn_prefill", "paged_gather", "pa_set_launch_events",
-    "pa_stream_read", "paged_attn_decode_grouped", "paged_attn_decode_noalloc",
+    "pa_stream_read", "paged_attn_decode_grouped", "paged_attn_decode_noalloc", "pa_frame_read",
 )
 PA_NOALLOC_SCRATCH_BYTES = 64 << 20
 PA_MAX_GROUP = 4
@@ -110,6 +110,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_set_launch_events.restype = ctypes.c_int
     lib.pa_stream_read.argtypes = [P, I64, P, P]
     lib.pa_stream_read.restype = ctypes.c_int
+    lib.pa_frame_read.argtypes = [P, I64, P, I64, I64, I32, I64, I32, I64, I32, I32, P, P]
+    lib.pa_frame_read.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -366,3 +368,17 @@ def stream_read(buf, sink, stream=None) -> None:
     _dense(buf)
     _check("pa_stream_read", load().pa_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
                                                    _ptr(sink), _stream(stream)))
+
+
+def frame_read(buf, frame_order, frame_bytes: int, groups: int, group_stride: int, pieces: int,
+               piece_stride: int, piece_bytes: int, frames_per_unit: int, sink, stream=None) -> None:
+    """Frame-pattern read probe over a dense device tensor ``buf`` holding
+    ``frame_order.numel()`` frames (see pa_frame_read); ``frame_order`` is a
+    device int32 tensor, ``sink`` a device int32/uint32 scalar tensor."""
+    _dense(buf, frame_order)
+    if str(frame_order.dtype) != "torch.int32" or frame_order.dim() != 1:
+        raise TypeError("frame_order must be a 1-D int32 tensor")
+    _check("pa_frame_read", load().pa_frame_read(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(frame_order), frame_order.numel(),
+        int(frame_bytes), int(groups), int(group_stride), int(pieces), int(piece_stride),
+        int(piece_bytes), int(frames_per_unit), _ptr(sink), _stream(stream)))

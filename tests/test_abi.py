@@ -255,3 +255,29 @@ def test_stream_read_argument_errors():
     assert lib.pa_stream_read(None, 17, None, None) == -1        # not a multiple of 16
     assert lib.pa_stream_read(None, 32, None, None) == -1        # null buffer
     assert lib.pa_stream_read(ctypes.c_void_p(8), 32, ctypes.c_void_p(16), None) == -2  # misaligned
+
+
+def test_frame_read_argument_errors():
+    """pa_frame_read checks that every piece lies inside its frame and every
+    frame inside the buffer before launching."""
+    lib = pkv.load()
+    p = ctypes.c_void_p(1 << 20)
+    # 10 frames of 4 KiB in a 40 KiB buffer; 16 groups of 16 pieces of 16 B
+    ok = dict(bytes=40960, n=10, fb=4096, g=16, gs=16, pc=16, ps=256, pb=16, fpu=4)
+
+    def call(buf=p, order=p, sink=p, **o):
+        a = {**ok, **o}
+        return lib.pa_frame_read(buf, a["bytes"], order, a["n"], a["fb"], a["g"], a["gs"], a["pc"],
+                                 a["ps"], a["pb"], a["fpu"], sink, None)
+
+    assert call(n=0) == 0                          # nothing to do
+    assert call(bytes=40959 // 16 * 16) == -1      # ten frames do not fit the buffer
+    assert call(g=17) == -1                        # the last group's pieces leave the frame
+    assert call(pc=17) == -1
+    assert call(pb=24) == -1                       # not a multiple of 16
+    assert call(gs=8) == -1
+    assert call(fpu=0) == -1
+    assert call(n=70000 * 4, bytes=70000 * 4 * 4096, fpu=4) == -1   # more than 65,535 units
+    assert call(buf=None) == -1
+    assert call(buf=ctypes.c_void_p((1 << 20) + 8)) == -2
+    assert call(order=ctypes.c_void_p((1 << 20) + 2)) == -2

@@ -711,6 +711,32 @@ def test_robustness_seeds_and_permuted_pool(make):
         assert err <= TOL[w.dtype]
 
 
+def test_frame_read_probe_runs_and_leaves_sink():
+    """The frame-pattern probe reads a buffer of frames in a given order in
+    the three patterns the bench times (one head's rows of a token-major
+    frame, one head's rows of a head-major frame, whole frames), touching
+    nothing else; its launch-event stamps bracket a positive duration."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+
+    dev = torch.device("cuda:0")
+    B, H, row = 16, 8, 256
+    frame = B * H * row
+    n = 300
+    buf = torch.ones(n * frame // 2, dtype=torch.int16, device=dev)
+    order = torch.from_numpy(np.random.default_rng(3).permutation(n).astype(np.int32)).to(dev)
+    sink = torch.full((1,), 12345, dtype=torch.int32, device=dev)
+    patterns = [(H, row, B, H * row, row, 32), (H, B * row, B, row, row, 32), (1, 0, B * H, row, row, 4)]
+    for groups, gs, pieces, ps, pb, fpu in patterns:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with pkv.kernel_timing(e0, e1):
+            pkv.lib.frame_read(buf, order, frame, groups, gs, pieces, ps, pb, fpu, sink)
+        torch.cuda.synchronize()
+        assert e0.elapsed_time(e1) > 0
+    assert int(sink.item()) == 12345
+
+
 def test_stream_read_probe_runs_and_leaves_sink():
     """The streaming-read probe reads the whole buffer without touching
     anything else (its sink stays as it was for ordinary data)."""
