@@ -50,7 +50,8 @@ def log(*a):
 
 
 KERNEL_SOURCES = {"paged_decode": ("paged_decode.hip", "pa_device.h", "pa_launch.h"),
-                  "paged_prefill": ("paged_prefill.hip", "pa_device.h", "pa_launch.h")}
+                  "paged_prefill": ("paged_prefill.hip", "pa_device.h", "pa_launch.h",
+                                    "pa_prefill.h")}
 
 
 def _code_only(text: str) -> str:
@@ -358,13 +359,14 @@ def prefill_roofline(w, flops: int, compulsory: int, kernel_ms: float, traffic) 
     matrix peak and the HBM peak times the launch's intensity (algorithmic
     flops over compulsory bytes); ``bound`` names that roof, and
     ``achieved``/``peak`` are in its unit (compulsory bytes per second for an
-    HBM-bound launch). bf16 weights enter the weighted sum as a high part and
-    a residual, so the matrix cores issue 1.5x the algorithmic flops."""
+    HBM-bound launch). The matrix cores issue the algorithmic flops: the
+    weighted sum takes each weight once, in fp16 (with split weights, a bf16
+    high part and residual, they would issue 1.5x)."""
     sec = kernel_ms * 1e-3
     tflops = flops / sec / 1e12
     intensity = flops / compulsory
     hbm_roof_tflops = HBM_PEAK_GBS * 1e9 * intensity / 1e12
-    issued = flops * (1.5 if w.dtype == "bf16" else 1.0)
+    issued = flops
     out = {"kernel": "prefill_kernel"}
     if hbm_roof_tflops < MFMA_PEAK_TFLOPS:
         gbs = compulsory / sec / 1e9
@@ -457,19 +459,21 @@ def bench_prefill(args, w, pt, cache, dev):
     flush_buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
     flush_sink = torch.empty((), dtype=torch.float32, device=dev)
 
-    def step(work_order=order):
+    def step(work_order=order, split=False):
         pkv.paged_attn_prefill(q, cache.k, cache.v, bt, cl, qsd, w.B, w.scale, out, max_ctx, max_q,
-                               work_order=work_order)
+                               work_order=work_order, split_weights=split)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     # Plain launches between stream events (the step time) alternate with
     # launches that stamp the kernel's own start and end (its duration) and,
-    # for context, plain launches in the default order, so that all three see
-    # the same clock and cache conditions.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    for e0, e1, k0, k1, b0, b1 in evs:
+    # for context, plain launches in the default order and (bf16) stamped
+    # launches with split weights, so that all of them see the same clock and
+    # cache conditions.
+    split_too = w.dtype == "bf16"
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    for e0, e1, k0, k1, b0, b1, s0, s1 in evs:
         if not args.no_flush:
             torch.sum(flush_buf, dim=0, out=flush_sink)
         e0.record()
@@ -485,7 +489,13 @@ def bench_prefill(args, w, pt, cache, dev):
             b0.record()
             step(None)
             b1.record()
+        if split_too:
+            if not args.no_flush:
+                torch.sum(flush_buf, dim=0, out=flush_sink)
+            with pkv.kernel_timing(s0, s1):
+                step(split=True)
     torch.cuda.synchronize()
+    split_ms = float(np.mean([e[6].elapsed_time(e[7]) for e in evs])) if split_too else None
     batch_order_ms = None
     if order is not None:
         batch_order_ms = float(np.mean([e[4].elapsed_time(e[5]) for e in evs]))
@@ -494,7 +504,8 @@ def bench_prefill(args, w, pt, cache, dev):
     tflops = flops / (kms * 1e-3) / 1e12          # the kernel alone (roofline)
     step_tflops = flops / (ms * 1e-3) / 1e12      # whole step between stream events (value)
     log(f"[bench] prefill {args.steps} steps: {ms * 1e3:.1f} us (kernel alone {kms * 1e3:.1f}), "
-        f"{step_tflops:.1f} TFLOP/s per step, kernel alone {tflops:.1f} TFLOP/s")
+        f"{step_tflops:.1f} TFLOP/s per step, kernel alone {tflops:.1f} TFLOP/s"
+        + ("" if split_ms is None else f"; split weights: kernel alone {split_ms * 1e3:.1f} us"))
     res = {
         "metric": "paged prefill attention: TFLOP/s (% of MFMA peak) + us/step",
         "value": round(step_tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -509,6 +520,9 @@ def bench_prefill(args, w, pt, cache, dev):
                            "costliest sequence first, its later query tiles first "
                            "(driver.prefill_order)"),
         "default_order_us_per_step": None if batch_order_ms is None else round(batch_order_ms * 1e3, 2),
+        "weighted_sum": ("fp16 operands: each weight rounded once to fp16"
+                         + (", bf16 V converted to fp16 on chip" if split_too else "")),
+        "split_weights_kernel_us": None if split_ms is None else round(split_ms * 1e3, 2),
         "roofline": prefill_roofline(w, flops, compulsory, kms, measured_traffic(
             w.name, digest, "paged_prefill")),
         "kernel_source_digest": digest,
@@ -661,8 +675,7 @@ def bench_prefix(args, w, dev):
                      "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
                      "algorithmic_flops_per_step": on["flops"],
                      "launch_us_per_step": round(on["kernel_ms"] * 1e3, 2),
-                     "mfma_issued_frac_of_mfma_peak": round(
-                         tflops * (1.5 if w.dtype == "bf16" else 1.0) / MFMA_PEAK_TFLOPS, 4)},
+                     "mfma_issued_frac_of_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

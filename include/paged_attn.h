@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 typedef enum pa_dtype {
   PA_F32 = 0,
@@ -301,6 +301,7 @@ typedef struct pa_prefill_shape {
   int32_t total_queries;       /* T: rows of q and out */
   pa_dtype kv_dtype;           /* PA_F16 or PA_BF16 (the matrix-core path) */
   pa_dtype out_dtype;          /* PA_F32 or kv_dtype */
+  int32_t split_weights;       /* bf16 caches: 0 (default) or 1, see below; else ignored */
 } pa_prefill_shape;
 
 /* Queries per prefill work item (one query tile of one sequence). */
@@ -336,9 +337,15 @@ typedef struct pa_prefill_shape {
  * softmax_j(a_ij) v_j). n_s = ctx_s is a whole prompt, n_s < ctx_s a chunk of
  * one, n_s = 1 a decode step. Device-side preconditions: 0 <= n_s <= ctx_s and
  * n_s <= max_query_len (larger values are clamped). Scores and the output
- * accumulate in fp32 on the matrix cores. The softmax weights enter the
- * weighted sum of V as a bf16 value plus its bf16 residual (bf16 caches), or
- * as one fp16 rounding that the normaliser also sums (fp16 caches).
+ * accumulate in fp32 on the matrix cores. The weighted sum of V takes fp16
+ * operands: each softmax weight rounded once to fp16, a rounding the
+ * normaliser also sums, so every output is a convex combination of value
+ * rows. bf16 V is converted to fp16 on chip, exactly for magnitudes below
+ * 2^16 except bits below 2^-24 (values under 2^-17); a work item that meets
+ * a larger V value (or an infinity) redoes its tiles as with
+ * split_weights = 1. split_weights = 1 (bf16 caches) keeps V in bf16 and
+ * enters each weight as a bf16 value plus its bf16 residual, ~16 significant
+ * bits, at about 8 % more time. Any other value is PA_EINVAL.
  * S * Tq * H must not exceed 2^31 - 1 (else PA_EINVAL).
  */
 pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,

@@ -7,6 +7,7 @@
 
 #include "paged_attn.h"
 #include "pa_launch.h"
+#include "pa_prefill.h"
 #include "pa_probes.h"
 
 namespace pa {
@@ -368,6 +369,7 @@ pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_c
   if (!pa::prefill_supported(to_internal(sh->kv_dtype), sh->head_dim)) return PA_EINVAL;
   if (sh->out_dtype != PA_F32 && sh->out_dtype != sh->kv_dtype) return PA_EINVAL;
   if (block_size != sh->block_size || !std::isfinite(scale)) return PA_EINVAL;
+  if (sh->split_weights != 0 && sh->split_weights != 1) return PA_EINVAL;
   if (static_cast<int64_t>(sh->max_context_len) >
       static_cast<int64_t>(sh->max_blocks_per_seq) * sh->block_size)
     return PA_EINVAL;
@@ -406,6 +408,7 @@ pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_c
   a.max_query_len = sh->max_query_len;
   a.total_queries = sh->total_queries;
   a.out_f32 = sh->out_dtype == PA_F32 ? 1 : 0;
+  a.split_weights = sh->split_weights;
   a.work_order = work_order;
   return from_hip(pa::launch_prefill(a, to_internal(sh->kv_dtype), sh->head_dim,
                                      static_cast<hipStream_t>(stream)));

@@ -65,35 +65,6 @@ struct GroupArgs {
 
 enum class Dtype : int { F32 = 0, F16 = 1, BF16 = 2 };
 
-// Arguments of the causal multi-query (prefill) kernel.
-struct PrefillArgs {
-  const void* q;               // [total_queries, H, D]
-  const void* k_cache;
-  const void* v_cache;
-  const int32_t* block_tables;
-  const int32_t* context_lens;
-  const int32_t* query_start;  // [S + 1]
-  void* out;                   // [total_queries, H, D]
-  int64_t num_blocks;
-  float scale_log2;            // |scale| * log2(e), >= 0
-  int32_t negate_q;            // 1 when scale < 0: q enters with its sign flipped
-  int32_t num_seqs;
-  int32_t block_size;
-  int32_t num_heads;
-  int32_t max_blocks;
-  int32_t max_ctx;
-  int32_t max_query_len;
-  int32_t total_queries;
-  int32_t out_f32;
-  const int32_t* work_order;   // [S * query tiles] dispatch order of the work items, or null
-};
-
-// Queries per prefill work item (the prefill kernel's query tile).
-constexpr int kPrefillTile = 128;
-
-bool prefill_supported(Dtype dt, int head_dim);
-hipError_t launch_prefill(const PrefillArgs& a, Dtype dt, int head_dim, hipStream_t stream);
-
 // Tokens one wavefront processes per loop iteration for (dtype, head_dim);
 // partition sizes are multiples of it. 0 if the combination is unsupported.
 int chunk_tokens(Dtype dt, int head_dim);

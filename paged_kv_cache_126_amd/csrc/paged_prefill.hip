@@ -25,10 +25,14 @@
 //   2. applies the causal mask and an online softmax per query (the two
 //      lanes sharing a query exchange one value for the maximum; each keeps
 //      its own share of the normaliser, added once at the end),
-//   3. accumulates O^T += V^T P^T. In bf16, P is split into a high part and
-//      the residual (two MFMAs), which keeps ~16 significant bits of every
-//      softmax weight; in fp16 one rounding keeps 11, and the normaliser
-//      sums the rounded weights.
+//   3. accumulates O^T += V^T P^T on fp16 operands: P rounded once to fp16
+//      (11 significant bits of every softmax weight; the normaliser sums the
+//      rounded weights), and, for bf16 caches, V converted to fp16 as it is
+//      staged, which is exact for magnitudes below 2^16 (apart from bits
+//      below 2^-24). A workgroup that stages a larger V value redoes its
+//      tiles on bf16 operands with P split into a high part and the residual
+//      (two MFMAs, ~16 significant bits); callers can ask for that form
+//      throughout.
 // Matrix layouts (verified on the device): for v_mfma_f32_32x32x16, A[i][k]
 // sits in lane i + 32 * (k / 8), element k % 8; B[k][j] in lane
 // j + 32 * (k / 8), element k % 8; D[i][j] in lane j + 32 * ((i / 4) % 2),
@@ -36,7 +40,7 @@
 #include <type_traits>
 
 #include "pa_device.h"
-#include "pa_launch.h"
+#include "pa_prefill.h"
 
 namespace pa {
 namespace {
@@ -130,7 +134,7 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int kPieces = D / 8;   // 16-byte pieces per cache row
   constexpr int kPadK = 8;         // LDS row padding (elements) against bank conflicts
   constexpr int kPadV = 16;
-  constexpr bool kSplitP = std::is_same<T, BF16>::value;  // weights as hi + lo (see below)
+  constexpr bool kBf16 = std::is_same<T, BF16>::value;
 
   // Work item and head of this workgroup. Workgroups go to the 8 XCDs
   // round-robin by linear id, and each XCD has its own L2. With H a
@@ -215,20 +219,19 @@ void prefill_kernel(PrefillArgs a) {
   // clamped into the pool, read once so that a tile's K/V loads need no
   // dependent table read. Longer contexts read the table directly.
   __shared__ uint32_t lds_tbl[kTableCache];
+  // Set when a V value staged as fp16 was out of fp16's range.
+  __shared__ int lds_wide;
   const int n_blk = wg_last / a.block_size + 1;
   const bool tbl_in_lds = n_blk <= kTableCache;
   if (tbl_in_lds) {
     for (int b = threadIdx.x; b < n_blk; b += kWaves * 64)
       lds_tbl[b] = min(static_cast<uint32_t>(table_row[b]), max_frame);
   }
+  if (threadIdx.x == 0) lds_wide = 0;
   __syncthreads();
 
   f32x16 o[kDBlk];
-#pragma unroll
-  for (int b = 0; b < kDBlk; ++b)
-#pragma unroll
-    for (int t = 0; t < 16; ++t) o[b][t] = 0.f;
-  float m = kNegBig, l = 0.f;
+  float m, l;
 
   const int n_tiles = (wg_last + kBN) / kBN;
   // Each thread moves kPer 16-byte pieces of K and of V per tile. The LDS
@@ -294,16 +297,36 @@ void prefill_kernel(PrefillArgs a) {
       pv[i] = vv;
     }
   };
-  auto stage = [&](const int buf) {
+  // Write the fetched pieces to LDS buffer `buf`. With kV16 (bf16 caches),
+  // V is written in fp16: a bf16 value of magnitude below 2^16 is exactly
+  // an fp16 value, apart from bits below 2^-24 of values under 2^-17 (fp16
+  // subnormals), which the conversion (toward zero) drops. A larger value,
+  // or an infinity, sets lds_wide; NaN stays NaN.
+  auto stage = [&](const int buf, auto v16) {
+    constexpr bool kV16 = decltype(v16)::value;
     auto& lds_k = lds_kb[buf];
     auto& lds_v = lds_vb[buf];
+    float vmax = 0.f;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int piece = threadIdx.x + i * kWaves * 64;
       const int key = piece / kPieces;
       const int c = piece % kPieces;
       *reinterpret_cast<u32x4*>(&lds_k[key][8 * c]) = pk[i];
-      *reinterpret_cast<u32x4*>(&lds_v[key][8 * c]) = pv[i];
+      u32x4 vw = pv[i];
+      if constexpr (kV16) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float lo = __uint_as_float(pv[i][w] << 16);
+          const float hi = __uint_as_float(pv[i][w] & 0xffff0000u);
+          vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
+          vw[w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+        }
+      }
+      *reinterpret_cast<u32x4*>(&lds_v[key][8 * c]) = vw;
+    }
+    if constexpr (kV16) {
+      if (vmax >= 65536.f) lds_wide = 1;
     }
   };
   // Score rows in a permuted key order: row i = 8 u + 4 v + e (u < 4, v < 2,
@@ -312,132 +335,166 @@ void prefill_kernel(PrefillArgs a) {
   // elements 8 j .. 8 j + 7 are keys 16 j + 8 half + [0, 8): the layout the
   // weighted sum's B operand needs, with no exchange between lanes.
   const int krow = 16 * (col / 16) + 8 * ((col / 4) % 2) + 4 * ((col / 8) % 2) + col % 4;
-  fetch(0);
-  stage(0);
-  __syncthreads();
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int k0 = kt * kBN;
-    if (kt + 1 < n_tiles) fetch(k0 + kBN);
-    auto& lds_k = lds_kb[kt & 1];
-    auto& lds_v = lds_vb[kt & 1];
 
-    if (wave_live && k0 <= wave_last) {  // the tile holds keys some query of this wavefront sees
-      // S^T = K Q^T: rows = keys of the tile, columns = this wavefront's queries
-      f32x16 st;
+  // One pass over the key tiles. kV16 (bf16 caches only): V staged in fp16
+  // and the weighted sum on fp16 operands; otherwise the cache dtype's.
+  auto pass = [&](auto v16) {
+    constexpr bool kV16 = decltype(v16)::value;
+    // bf16 weights as a high part and a residual (see below)
+    constexpr bool kSplitP = kBf16 && !kV16;
+    using PM = typename std::conditional<kV16, Mfma<F16>, M>::type;
+    using pvec = typename PM::vec;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) st[t] = 0.f;
+    for (int b = 0; b < kDBlk; ++b)
 #pragma unroll
-      for (int step = 0; step < kSteps; ++step) {
-        const u32x4 kbits = *reinterpret_cast<const u32x4*>(&lds_k[krow][16 * step + 8 * half]);
-        st = M::run(M::from_bits(kbits), qb[step], st);
-      }
-      // causal mask + online softmax for the lane's query
-      const bool full = k0 + kBN - 1 <= wave_first;  // every key visible to every query
-      float x[16];
-      float tmax = -__builtin_inff();
-      if (full) {  // wavefront-uniform: no mask
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          x[t] = st[t];
-          tmax = fmaxf(tmax, x[t]);
-        }
-      } else {
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int key = k0 + 16 * (t / 8) + 8 * half + t % 8;
-          x[t] = (q_ok && key <= my_pos) ? st[t] : -__builtin_inff();
-          tmax = fmaxf(tmax, x[t]);
-        }
-      }
-      // raw scores so far; the scale (>= 0, so order-preserving) is applied to
-      // the maximum here and folded into the exponent's fma below
-      tmax = max_halves(tmax) * a.scale_log2;
-      // Lazy rescaling: the reference maximum m moves (and O, l are rescaled)
-      // only when a query's maximum grows by more than kLazy (log2 units);
-      // otherwise weights are taken against the stale m and stay below
-      // 2^kLazy. The common factor 2^-m cancels in O / l, so the result is
-      // the same softmax; the O rescale, a multiply of every accumulator,
-      // becomes rare.
-      const bool grow = tmax > m + kLazy;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wavefront-uniform branch
-        const float m_new = grow ? tmax : m;
-        const float alpha = fast_exp2(m - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int b = 0; b < kDBlk; ++b)
-#pragma unroll
-          for (int t = 0; t < 16; ++t) o[b][t] *= alpha;
-        m = m_new;
-      }
-#pragma unroll
-      for (int t = 0; t < 16; ++t) x[t] = fast_exp2(__builtin_fmaf(x[t], a.scale_log2, -m));
-      if (!full) {
-        // masked keys weigh exactly 0 (with a zero scale, -inf * 0 would be NaN)
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int key = k0 + 16 * (t / 8) + 8 * half + t % 8;
-          x[t] = (q_ok && key <= my_pos) ? x[t] : 0.f;
-        }
-      }
+      for (int t = 0; t < 16; ++t) o[b][t] = 0.f;
+    m = kNegBig;
+    l = 0.f;
+    fetch(0);
+    stage(0, v16);
+    __syncthreads();
+    for (int kt = 0; kt < n_tiles; ++kt) {
+      const int k0 = kt * kBN;
+      if (kt + 1 < n_tiles) fetch(k0 + kBN);
+      auto& lds_k = lds_kb[kt & 1];
+      auto& lds_v = lds_vb[kt & 1];
 
-      // x[8j .. 8j+7] are the weights of keys 16j + 8*half + [0, 8): already
-      // the B-operand layout of the weighted sum's k-step j (see krow).
-      // bf16 keeps 8 significant bits: P = hi + lo per pair of weights, hi
-      // rounded to bf16 and lo the rounded residual (x - hi is exact in
-      // fp32), two MFMAs. fp16 keeps 11: one rounding, one MFMA, and l sums
-      // the rounded weights, so that O / l is a convex combination of the
-      // values with exactly the weights the matrix cores applied.
-      vec p_hi[2], p_lo[2];
-      float psum = 0.f;
+      if (wave_live && k0 <= wave_last) {  // the tile holds keys some query of this wavefront sees
+        // S^T = K Q^T: rows = keys of the tile, columns = this wavefront's queries
+        f32x16 st;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int t = 0; t < 16; ++t) st[t] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const f32x2 xv = {x[8 * j + e], x[8 * j + e + 1]};
-          const auto hp = __builtin_convertvector(xv, typename M::pair);
-          p_hi[j][e] = hp.x;
-          p_hi[j][e + 1] = hp.y;
-          if constexpr (kSplitP) {
-            const f32x2 hw = __builtin_convertvector(hp, f32x2);
-            const auto lp =
-                __builtin_convertvector(f32x2{xv.x - hw.x, xv.y - hw.y}, typename M::pair);
-            p_lo[j][e] = lp.x;
-            p_lo[j][e + 1] = lp.y;
-            psum += xv.x + xv.y;
-          } else {
-            psum = __builtin_amdgcn_fdot2(hp, typename M::pair{1, 1}, psum, false);
+        for (int step = 0; step < kSteps; ++step) {
+          const u32x4 kbits = *reinterpret_cast<const u32x4*>(&lds_k[krow][16 * step + 8 * half]);
+          st = M::run(M::from_bits(kbits), qb[step], st);
+        }
+        // causal mask + online softmax for the lane's query
+        const bool full = k0 + kBN - 1 <= wave_first;  // every key visible to every query
+        float x[16];
+        float tmax = -__builtin_inff();
+        if (full) {  // wavefront-uniform: no mask
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            x[t] = st[t];
+            tmax = fmaxf(tmax, x[t]);
+          }
+        } else {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const int key = k0 + 16 * (t / 8) + 8 * half + t % 8;
+            x[t] = (q_ok && key <= my_pos) ? st[t] : -__builtin_inff();
+            tmax = fmaxf(tmax, x[t]);
           }
         }
-      l += psum;  // this lane's share; the two halves are added at the end
-      // O^T += V^T P^T. The V^T operand (8 consecutive keys per lane at one
-      // head-dim element) comes from the row-major V tile through transposing
-      // LDS reads: in each group of 16 lanes, a 64-bit transpose read hands
-      // lane l element j = (element l % 4 of the chunk lane 4j + l/4 points
-      // at), so lane c points at V[kb + c/4][d0 + 4 (c % 4)] and lane l
-      // receives V[kb + j][d0 + l], j = 0..3; two reads cover 8 keys.
-      const int grp16 = lane >> 4;
-      const int c16 = lane & 15;
-      auto v_operand = [&](const int b, const int j) {
-        const int d0 = 32 * b + 16 * (grp16 & 1);
-        const int kb = 16 * j + 8 * (grp16 >> 1);
-        const v4i16 lo4 = tr_read(&lds_v[kb + (c16 >> 2)][d0 + 4 * (c16 & 3)]);
-        const v4i16 hi4 = tr_read(&lds_v[kb + 4 + (c16 >> 2)][d0 + 4 * (c16 & 3)]);
-        return M::from_bits(join(lo4, hi4));
-      };
-      // the next V operand is read while the current one's two MFMAs run;
-      // keys 0-15 of the tile for every output block first, then keys 16-31
-      vec va_next = v_operand(0, 0);
+        // raw scores so far; the scale (>= 0, so order-preserving) is applied
+        // to the maximum here and folded into the exponent's fma below
+        tmax = max_halves(tmax) * a.scale_log2;
+        // Lazy rescaling: the reference maximum m moves (and O, l are
+        // rescaled) only when a query's maximum grows by more than kLazy
+        // (log2 units); otherwise weights are taken against the stale m and
+        // stay below 2^kLazy. The common factor 2^-m cancels in O / l, so the
+        // result is the same softmax; the O rescale, a multiply of every
+        // accumulator, becomes rare.
+        const bool grow = tmax > m + kLazy;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wavefront-uniform branch
+          const float m_new = grow ? tmax : m;
+          const float alpha = fast_exp2(m - m_new);
+          l *= alpha;
 #pragma unroll
-      for (int n = 0; n < 2 * kDBlk; ++n) {
-        const int j = n / kDBlk, b = n % kDBlk;
-        const vec va = va_next;
-        if (n + 1 < 2 * kDBlk) va_next = v_operand((n + 1) % kDBlk, (n + 1) / kDBlk);
-        o[b] = M::run(va, p_hi[j], o[b]);
-        if constexpr (kSplitP) o[b] = M::run(va, p_lo[j], o[b]);
+          for (int b = 0; b < kDBlk; ++b)
+#pragma unroll
+            for (int t = 0; t < 16; ++t) o[b][t] *= alpha;
+          m = m_new;
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) x[t] = fast_exp2(__builtin_fmaf(x[t], a.scale_log2, -m));
+        if (!full) {
+          // masked keys weigh exactly 0 (with a zero scale, -inf * 0 would be NaN)
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const int key = k0 + 16 * (t / 8) + 8 * half + t % 8;
+            x[t] = (q_ok && key <= my_pos) ? x[t] : 0.f;
+          }
+        }
+
+        // x[8j .. 8j+7] are the weights of keys 16j + 8*half + [0, 8): already
+        // the B-operand layout of the weighted sum's k-step j (see krow).
+        // fp16 operands (fp16 caches, or bf16 V staged in fp16) keep 11
+        // significant bits of each weight: one rounding, one MFMA, and l sums
+        // the rounded weights, so that O / l is a convex combination of the
+        // values with exactly the weights the matrix cores applied. The bf16
+        // split keeps ~16: P = hi + lo per pair of weights, hi rounded to bf16
+        // and lo the rounded residual (x - hi is exact in fp32), two MFMAs.
+        pvec p_hi[2], p_lo[2];
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const f32x2 xv = {x[8 * j + e], x[8 * j + e + 1]};
+            const auto hp = __builtin_convertvector(xv, typename PM::pair);
+            p_hi[j][e] = hp.x;
+            p_hi[j][e + 1] = hp.y;
+            if constexpr (kSplitP) {
+              const f32x2 hw = __builtin_convertvector(hp, f32x2);
+              const auto lp =
+                  __builtin_convertvector(f32x2{xv.x - hw.x, xv.y - hw.y}, typename PM::pair);
+              p_lo[j][e] = lp.x;
+              p_lo[j][e + 1] = lp.y;
+              psum += xv.x + xv.y;
+            } else {
+              psum = __builtin_amdgcn_fdot2(hp, typename PM::pair{1, 1}, psum, false);
+            }
+          }
+        l += psum;  // this lane's share; the two halves are added at the end
+        // O^T += V^T P^T. The V^T operand (8 consecutive keys per lane at one
+        // head-dim element) comes from the row-major V tile through
+        // transposing LDS reads: in each group of 16 lanes, a 64-bit
+        // transpose read hands lane l element j = (element l % 4 of the chunk
+        // lane 4j + l/4 points at), so lane c points at V[kb + c/4][d0 + 4 (c %
+        // 4)] and lane l receives V[kb + j][d0 + l], j = 0..3; two reads cover
+        // 8 keys.
+        const int grp16 = lane >> 4;
+        const int c16 = lane & 15;
+        auto v_operand = [&](const int b, const int j) {
+          const int d0 = 32 * b + 16 * (grp16 & 1);
+          const int kb = 16 * j + 8 * (grp16 >> 1);
+          const v4i16 lo4 = tr_read(&lds_v[kb + (c16 >> 2)][d0 + 4 * (c16 & 3)]);
+          const v4i16 hi4 = tr_read(&lds_v[kb + 4 + (c16 >> 2)][d0 + 4 * (c16 & 3)]);
+          return PM::from_bits(join(lo4, hi4));
+        };
+        // the next V operand is read while the current one's MFMAs run; keys
+        // 0-15 of the tile for every output block first, then keys 16-31
+        pvec va_next = v_operand(0, 0);
+#pragma unroll
+        for (int n = 0; n < 2 * kDBlk; ++n) {
+          const int j = n / kDBlk, b = n % kDBlk;
+          const pvec va = va_next;
+          if (n + 1 < 2 * kDBlk) va_next = v_operand((n + 1) % kDBlk, (n + 1) / kDBlk);
+          o[b] = PM::run(va, p_hi[j], o[b]);
+          if constexpr (kSplitP) o[b] = PM::run(va, p_lo[j], o[b]);
+        }
       }
+      if (kt + 1 < n_tiles) stage((kt + 1) & 1, v16);
+      __syncthreads();
     }
-    if (kt + 1 < n_tiles) stage((kt + 1) & 1);
-    __syncthreads();
+  };
+
+  if constexpr (kBf16) {
+    bool split = a.split_weights != 0;
+    if (!split) {
+      pass(std::true_type{});
+      // Read after the pass's last barrier, so every thread sees the same
+      // value. A V value out of fp16's range was staged wrongly: the
+      // workgroup redoes all its tiles with the bf16 split (the LDS buffers
+      // are no longer read, so the second pass may restage them at once),
+      // through the same code as a split launch, so with the same bits.
+      split = lds_wide != 0;
+    }
+    if (split) pass(std::false_type{});
+  } else {
+    pass(std::false_type{});
   }
 
   l = sum_halves(l);

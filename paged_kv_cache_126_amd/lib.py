@@ -64,8 +64,12 @@ class PrefillShape(ctypes.Structure):
         ("total_queries", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int),
         ("out_dtype", ctypes.c_int),
+        ("split_weights", ctypes.c_int32),
     ]
 
+
+# PA_ABI_VERSION of include/paged_attn.h that these structures follow.
+ABI_VERSION = 5
 
 _LIB = None
 
@@ -112,6 +116,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_stream_read.restype = ctypes.c_int
     lib.pa_frame_read.argtypes = [P, I64, P, I64, I64, I32, I64, I32, I64, I32, I32, P, P]
     lib.pa_frame_read.restype = ctypes.c_int
+    if lib.pa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {lib.pa_abi_version()}, this binding needs "
+                           f"{ABI_VERSION}: rebuild it with paged_kv_cache_126_amd/build.py")
     _LIB = lib
     return lib
 
@@ -297,12 +304,14 @@ def paged_attn_decode_grouped(q, k_cache, v_cache, block_tables, context_lens, b
 
 def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size: int,
                        scale: float, out, max_context_len: int, max_query_len: int,
-                       stream=None, work_order=None) -> None:
+                       stream=None, work_order=None, split_weights: bool = False) -> None:
     """Causal attention of each sequence's last tokens into ``out`` [T, H, D];
     see include/paged_attn.h. ``work_order`` (int32 device
     [S * ceil(max_query_len / PA_PREFILL_TILE)], optional) is the dispatch
     order of the work items, one per query tile of a sequence
-    (``driver.prefill_order``)."""
+    (``driver.prefill_order``). ``split_weights`` (bf16 caches): keep V in
+    bf16 and enter each softmax weight as a bf16 value plus its residual
+    instead of one fp16 rounding."""
     _dense(q, k_cache, v_cache, block_tables, context_lens, query_start, out, work_order)
     T, H, D = q.shape
     NB, B = k_cache.shape[0], k_cache.shape[1]
@@ -320,7 +329,8 @@ def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_st
                                    str(work_order.dtype) != "torch.int32"):
         raise TypeError(f"work_order must be int32 [{items}]")
     shape = PrefillShape(S, H, D, B, NB, block_tables.shape[1], int(max_context_len),
-                         int(max_query_len), T, dtype_code(k_cache), dtype_code(out))
+                         int(max_query_len), T, dtype_code(k_cache), dtype_code(out),
+                         1 if split_weights else 0)
     _check("paged_attn_prefill", load().paged_attn_prefill(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         _ptr(query_start), int(block_size), float(scale), _ptr(out), ctypes.byref(shape),

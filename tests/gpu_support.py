@@ -132,12 +132,13 @@ def run_gpu(w, partition_tokens: int = 0, out_dtype=None, phases: bool = False, 
     return (results, cache) if keep_cache else results
 
 
-def run_gpu_prefill(w, out_dtype=None, order=None):
+def run_gpu_prefill(w, out_dtype=None, order=None, split_weights=False):
     """Play prefill workload ``w`` on cuda:0: write every token with kv_append,
-    then one paged_attn_prefill over each sequence's last query_lens tokens.
-    ``order`` ("cost": driver.prefill_order; "random": a seeded permutation
-    of the work items) dispatches the query tiles in that order, and checks
-    that the output equals the default-order launch's bit for bit. Returns (AttendPoint, query_start,
+    then one paged_attn_prefill over each sequence's last query_lens tokens
+    (``split_weights`` passed on). ``order`` ("cost": driver.prefill_order;
+    "random": a seeded permutation of the work items) dispatches the query
+    tiles in that order, and checks that the output equals the
+    default-order launch's bit for bit. Returns (AttendPoint, query_start,
     out cpu tensor [T, H, D])."""
     import torch
 
@@ -158,7 +159,7 @@ def run_gpu_prefill(w, out_dtype=None, order=None):
         args = (q, cache.k, cache.v, torch.from_numpy(pt.tables).to(dev),
                 torch.from_numpy(pt.context_lens).to(dev), torch.from_numpy(qs.astype(np.int32)).to(dev),
                 w.B, w.scale, out, int(pt.context_lens.max()), int(np.diff(qs).max()))
-        pkv.paged_attn_prefill(*args)
+        pkv.paged_attn_prefill(*args, split_weights=split_weights)
         if order is not None:
             mq = int(np.diff(qs).max())
             items = len(pt.context_lens) * -(-mq // pkv.PA_PREFILL_TILE)
@@ -166,7 +167,8 @@ def run_gpu_prefill(w, out_dtype=None, order=None):
                     np.random.default_rng(w.seed).permutation(items).astype(np.int32))
             first = out.clone()
             out.fill_(float("nan"))
-            pkv.paged_attn_prefill(*args, work_order=torch.from_numpy(work).to(dev))
+            pkv.paged_attn_prefill(*args, work_order=torch.from_numpy(work).to(dev),
+                                   split_weights=split_weights)
             torch.cuda.synchronize()
             assert torch.equal(out, first), f"dispatch order {order} changed the output"
         torch.cuda.synchronize()

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     for header in (HEADER, BLOCKS_HEADER):
         for name in declared_functions(header):
             assert hasattr(lib, name), name
-    assert lib.pa_abi_version() == 4
+    assert lib.pa_abi_version() == 5
 
 
 def test_status_strings():
@@ -213,7 +213,8 @@ def prefill_shape(**kw):
 @pytest.mark.parametrize("bad,code", [
     (dict(kv_dtype=L.PA_F32, out_dtype=L.PA_F32), -1), (dict(head_dim=256), -1),
     (dict(head_dim=32), -1), (dict(out_dtype=L.PA_F16), -1), (dict(max_context_len=4096), -1),
-    (dict(num_heads=0), -1), (dict(max_query_len=-1), -1),
+    (dict(num_heads=0), -1), (dict(max_query_len=-1), -1), (dict(split_weights=2), -1),
+    (dict(split_weights=-1), -1),
 ])
 def test_prefill_argument_errors(bad, code):
     lib = pkv.load()

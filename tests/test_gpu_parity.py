@@ -493,6 +493,112 @@ def test_prefill_full_size_parity(cfg):
     assert err <= TOL[w.dtype]
 
 
+def test_prefill_split_weights():
+    """split_weights = 1 keeps V in bf16 and enters each weight as a bf16
+    value plus its residual (~16 significant bits): within 1e-4 of the fp64
+    oracle, where the default fp16 weights (11 bits) are held to the usual
+    tolerance; for fp16 caches the flag changes nothing, bit for bit."""
+    w = configs.small(6)
+    say(f"[gpu] prefill {w.name}: split weights against fp16 weights")
+    pt, qs, split = run_gpu_prefill(w, order="random", split_weights=True)
+    plain = run_gpu_prefill(w)[2]
+    _, ref = oracle_prefill(w, pad_frame_for(w))
+    e_split, e_plain = max_err(split.numpy(), ref), max_err(plain.numpy(), ref)
+    say(f"  max-abs err {e_split:.3e} split, {e_plain:.3e} fp16 weights")
+    assert e_split <= 1e-4 and e_plain <= TOL[w.dtype]
+    w = replace(configs.small(6), dtype="f16", name="prefill_S3_H2_C150_f16")
+    a = run_gpu_prefill(w)[2]
+    b = run_gpu_prefill(w, split_weights=True)[2]
+    assert torch_equal_bits(a, b)
+
+
+def torch_equal_bits(a, b) -> bool:
+    """Bit-for-bit equality of two fp32 tensors (NaN payloads included)."""
+    import torch
+
+    return torch.equal(a.contiguous().view(torch.int32), b.contiguous().view(torch.int32))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_wide_values_redone_split(D):
+    """bf16 V values of magnitude 2^16 or more (and an infinity) do not fit
+    fp16: every work item (query tile of one sequence, one head) that stages
+    such a row redoes its tiles with split weights, so its outputs equal the
+    split_weights launch's bit for bit and are within the split form's
+    precision of the oracle, relative to the largest value. 65,280, the
+    largest bf16 value under 2^16, fits fp16 exactly and keeps the fp16
+    weights. The other items stay within the usual tolerance."""
+    import torch
+
+    import paged_kv_cache_126_amd as pkv
+    from oracle.oracle import default as oracle_default
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator().manual_seed(4321 + D)
+    B, H = 16, 4
+    ctx = np.array([300, 200, 150, 40], dtype=np.int32)
+    qlen = np.array([300, 72, 150, 40], dtype=np.int32)
+    nblk = (ctx + B - 1) // B
+    mb = int(nblk.max())
+    NB = int(nblk.sum()) + 3
+    frames = torch.randperm(NB, generator=gen).numpy().astype(np.int32)
+    tables = np.full((len(ctx), mb), NB - 1, dtype=np.int32)
+    used = 0
+    for s, n in enumerate(nblk):
+        tables[s, :n] = frames[used:used + n]
+        used += n
+    k = torch.randn(NB, B, H, D, generator=gen).to(torch.bfloat16)
+    v = torch.randn(NB, B, H, D, generator=gen).to(torch.bfloat16)
+
+    def row(s, t):
+        return int(tables[s, t // B]), t % B
+
+    # (sequence, token, head) -> values of that V row
+    wide = {(0, 5, 1): 7.0e4 * torch.randn(D, generator=gen),     # up to ~2^18
+            (1, 140, 0): torch.full((D,), -65536.0),               # exactly 2^16
+            (3, 10, 2): torch.full((D,), float("inf"))}
+    fits = {(2, 60, 3): torch.full((D,), 65280.0)}                 # largest bf16 under 2^16
+    for (s, t, h), val in {**wide, **fits}.items():
+        f, o = row(s, t)
+        v[f, o, h] = val.to(torch.bfloat16)
+    qs = np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32)
+    T = int(qs[-1])
+    q = torch.randn(T, H, D, generator=gen).to(torch.bfloat16)
+    scale = D ** -0.5
+    say(f"[gpu] prefill wide V values: D {D}, contexts {ctx.tolist()}, queries {qlen.tolist()}")
+    outs = []
+    for split in (False, True):
+        out = torch.full((T, H, D), float("nan"), dtype=torch.float32, device=dev)
+        pkv.paged_attn_prefill(q.to(dev), k.to(dev), v.to(dev), torch.from_numpy(tables).to(dev),
+                               torch.from_numpy(ctx).to(dev), torch.from_numpy(qs).to(dev), B,
+                               scale, out, int(ctx.max()), int(qlen.max()), split_weights=split)
+        torch.cuda.synchronize()
+        outs.append(out.cpu())
+    fast, split = outs
+    bits = lambda x: x.contiguous().view(torch.int16).numpy().view(np.uint16)
+    ref = oracle_default().paged_prefill(bits(q), bits(k), bits(v), tables, ctx, qs, B, scale, "bf16")
+    for s in range(len(ctx)):
+        rows = slice(int(qs[s]), int(qs[s + 1]))
+        for h in range(H):
+            a, b, r = fast[rows, h], split[rows, h], ref[rows, h]
+            hit = [key for key in wide if key[0] == s and key[2] == h]
+            if hit:
+                assert torch_equal_bits(a, b), f"sequence {s} head {h} was not redone"
+                if s != 3:  # the infinity makes NaNs (0 x inf) as well as infinities
+                    vmax = float(wide[hit[0]].to(torch.bfloat16).float().abs().max())
+                    err = float(np.max(np.abs(a.numpy() - r)))
+                    say(f"  sequence {s} head {h}: redone, max-abs err {err:.3e} (values up to {vmax:.3g})")
+                    assert err <= 1e-4 * vmax
+            else:
+                err = float(np.max(np.abs(a.numpy() - r)))
+                big = any(key[0] == s and key[2] == h for key in fits)
+                tol = TOL["bf16"] * (65280.0 if big else 1.0)
+                assert err <= tol, f"sequence {s} head {h}: {err:.3e}"
+                if big:
+                    say(f"  sequence {s} head {h}: 65280 rows kept fp16 weights, max-abs err {err:.3e}")
+                    assert not torch_equal_bits(a, b)
+
+
 def test_binding_rejects_malformed_orders():
     """The binding checks an order's dtype and length before anything is
     launched: a prefill work order must be int32 [S * ceil(max_query_len /
