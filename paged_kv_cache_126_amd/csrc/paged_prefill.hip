@@ -58,6 +58,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // 64-bit transposing LDS read (ds_read_b64_tr_b16) of 16-bit elements.
@@ -300,13 +301,14 @@ void prefill_kernel(PrefillArgs a) {
   // Write the fetched pieces to LDS buffer `buf`. With kV16 (bf16 caches),
   // V is written in fp16: a bf16 value of magnitude below 2^16 is exactly
   // an fp16 value, apart from bits below 2^-24 of values under 2^-17 (fp16
-  // subnormals), which the conversion (toward zero) drops. A larger value,
-  // or an infinity, sets lds_wide; NaN stays NaN.
+  // subnormals), which the conversion (toward zero) drops. A larger value
+  // (sign-free bf16 bits 0x4780 and up: 2^16, infinity or NaN) sets
+  // lds_wide.
   auto stage = [&](const int buf, auto v16) {
     constexpr bool kV16 = decltype(v16)::value;
     auto& lds_k = lds_kb[buf];
     auto& lds_v = lds_vb[buf];
-    float vmax = 0.f;
+    u16x2 vmag = {0, 0};  // largest sign-free bf16 bits of each half seen
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int piece = threadIdx.x + i * kWaves * 64;
@@ -317,16 +319,17 @@ void prefill_kernel(PrefillArgs a) {
       if constexpr (kV16) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float lo = __uint_as_float(pv[i][w] << 16);
-          const float hi = __uint_as_float(pv[i][w] & 0xffff0000u);
-          vmax = fmaxf(vmax, fmaxf(fabsf(lo), fabsf(hi)));
+          const uint32_t d = pv[i][w];
+          vmag = __builtin_elementwise_max(vmag, __builtin_bit_cast(u16x2, d & 0x7fff7fffu));
+          const float lo = __uint_as_float(d << 16);
+          const float hi = __uint_as_float(d & 0xffff0000u);
           vw[w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
         }
       }
       *reinterpret_cast<u32x4*>(&lds_v[key][8 * c]) = vw;
     }
     if constexpr (kV16) {
-      if (vmax >= 65536.f) lds_wide = 1;
+      if (max(vmag.x, vmag.y) >= 0x4780) lds_wide = 1;
     }
   };
   // Score rows in a permuted key order: row i = 8 u + 4 v + e (u < 4, v < 2,
