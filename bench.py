@@ -495,6 +495,8 @@ def bench_prefill(args, w, pt, cache, dev):
             with pkv.kernel_timing(s0, s1):
                 step(split=True)
     torch.cuda.synchronize()
+    if not bool(torch.isfinite(out).all()):
+        raise RuntimeError("prefill produced non-finite outputs: unwritten cache rows were read")
     split_ms = float(np.mean([e[6].elapsed_time(e[7]) for e in evs])) if split_too else None
     batch_order_ms = None
     if order is not None:
@@ -535,9 +537,11 @@ def bench_prefill(args, w, pt, cache, dev):
 
 
 def bench_prefix(args, w, dev):
-    """Prefix-sharing rounds: one step replays every round (write the rows
-    the block manager asks for with kv_append, then paged_attn_prefill over
-    them), once with prefix caching and once without."""
+    """Prefix-sharing rounds: one step replays every round (write the prompt
+    rows the block manager asks for with kv_append, paged_attn_prefill over
+    them, then write the rows of the tokens the round's decode steps
+    generate, which later rounds' prompts reuse), once with prefix caching
+    and once without."""
     import torch
 
     import paged_kv_cache_126_amd as pkv
@@ -562,7 +566,20 @@ def bench_prefix(args, w, dev):
             n = np.diff(rd.query_start).astype(np.int64)
             ctx = rd.context_lens.astype(np.int64)
             pairs = int(np.sum(n * (ctx - n) + n * (n + 1) // 2))
+            # the K/V rows of the tokens the round's decode steps generate, in
+            # one write after the round's prefill (the next round's prompts
+            # reuse the blocks that hold them; decode attention is not timed)
+            dec = [st.writes for st in (rd.decode or [])]
+            dseqs = np.concatenate([d.seqs for d in dec]) if dec else np.zeros(0, np.int64)
+            dpos = np.concatenate([d.positions for d in dec]) if dec else np.zeros(0, np.int64)
+            dslots = np.concatenate([d.slots for d in dec]) if dec else np.zeros(0, np.int64)
+            dk = dv = None
+            if len(dslots):
+                dids = torch.from_numpy(w.idents_rows(dseqs, dpos)).to(dev)
+                dk = V.draw_torch(w.seed, V.STREAM_K, dids, w.H, w.D, w.dtype, dev).contiguous()
+                dv = V.draw_torch(w.seed, V.STREAM_V, dids, w.H, w.D, w.dtype, dev).contiguous()
             launches.append(dict(
+                dk=dk, dv=dv, dslots=torch.from_numpy(dslots).to(dev), drows=len(dslots),
                 k_new=k_new, v_new=v_new, slots=torch.from_numpy(wb.slots).to(dev), q=q,
                 out=torch.empty((T, w.H, w.D), dtype=torch.float32, device=dev),
                 bt=torch.from_numpy(rd.tables).to(dev), cl=torch.from_numpy(rd.context_lens).to(dev),
@@ -595,6 +612,10 @@ def bench_prefix(args, w, dev):
                                            work_order=L["order"])
                 if evs:
                     evs[i][2].record()
+                if L["drows"]:
+                    pkv.kv_append(L["dk"], L["dv"], L["dslots"], cache.k, cache.v)
+                if evs:
+                    evs[i][5].record()
 
         for _ in range(args.warmup):
             step()
@@ -615,7 +636,7 @@ def bench_prefix(args, w, dev):
         all_evs = []
         for stamp in (False, True):
             for _ in range(args.steps):
-                evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in launches]
+                evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in launches]
                 if not args.no_flush:
                     torch.sum(flush_buf, dim=0, out=flush_sink)
                 step(evs, stamp)
@@ -624,7 +645,8 @@ def bench_prefix(args, w, dev):
         kern_evs = [e for st, e in all_evs if st]
         all_evs = [e for st, e in all_evs if not st]
         step_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in sevs]))
-        append_ms = float(np.mean([sum(r[0].elapsed_time(r[1]) for r in e) for e in all_evs]))
+        append_ms = float(np.mean([sum(r[0].elapsed_time(r[1]) + r[2].elapsed_time(r[5]) for r in e)
+                                   for e in all_evs]))
         prefill_ms = float(np.mean([sum(r[1].elapsed_time(r[2]) for r in e) for e in all_evs]))
         kernel_ms = float(np.mean([sum(r[3].elapsed_time(r[4]) for r in e) for e in kern_evs]))
         return step_ms, append_ms, prefill_ms, kernel_ms
@@ -633,12 +655,17 @@ def bench_prefix(args, w, dev):
     for caching in (True, False):
         rounds, mgr, cache, launches, host_s = prepare(caching)
         step_ms, append_ms, prefill_ms, kernel_ms = timed(cache, launches)
+        # every query's keys were written before its prefill: a non-finite
+        # output means the step read unwritten (NaN-filled) cache rows
+        if not all(bool(torch.isfinite(L["out"]).all()) for L in launches):
+            raise RuntimeError("prefix rounds produced non-finite outputs: unwritten cache rows were read")
         tokens = int(sum(int(rd.context_lens.sum()) for rd in rounds))
         reused = int(sum(int(rd.reused.sum()) for rd in rounds))
         res[caching] = dict(step_ms=step_ms, append_ms=append_ms, prefill_ms=prefill_ms,
                             kernel_ms=kernel_ms,
                             tokens=tokens, reused=reused, host_plan_s=host_s,
                             rows=sum(L["rows"] for L in launches),
+                            decode_rows=sum(L["drows"] for L in launches),
                             flops=sum(L["flops"] for L in launches),
                             evictions=getattr(mgr, "evictions", 0), frames=cache.k.shape[0])
         log(f"[bench] prefix caching {'on' if caching else 'off'}: step {step_ms * 1e3:.1f} us "
@@ -653,12 +680,14 @@ def bench_prefix(args, w, dev):
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(on["step_ms"], 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
-        "step": f"{w.rounds} rounds of (kv_append of the rows not reused, paged prefill over them); "
-                "the rounds' decode steps are planned but not timed",
+        "step": f"{w.rounds} rounds of (kv_append of the prompt rows not reused, paged prefill "
+                "over them, kv_append of the rows of the tokens the round's decode steps generate); "
+                "decode attention is not timed",
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "rounds": w.rounds,
                    "prompt_tokens": on["tokens"], "reused_tokens": on["reused"],
-                   "written_rows": on["rows"], "evictions": on["evictions"],
+                   "written_rows": on["rows"], "decode_rows": on["decode_rows"],
+                   "evictions": on["evictions"],
                    "frames": on["frames"], "cache_flush_between_steps": not args.no_flush},
         "phases_us": {"append": round(on["append_ms"] * 1e3, 2),
                       "prefill": round(on["prefill_ms"] * 1e3, 2)},
