@@ -342,7 +342,7 @@ typedef struct pa_prefill_shape {
  * normaliser also sums, so every output is a convex combination of value
  * rows. bf16 V is converted to fp16 on chip, exactly for magnitudes below
  * 2^16 except bits below 2^-24 (values under 2^-17); a work item that meets
- * a larger V value (or an infinity) redoes its tiles as with
+ * a larger V value, an infinity or a NaN redoes its tiles as with
  * split_weights = 1. split_weights = 1 (bf16 caches) keeps V in bf16 and
  * enters each weight as a bf16 value plus its bf16 residual, ~16 significant
  * bits, at about 8 % more time. Any other value is PA_EINVAL.
