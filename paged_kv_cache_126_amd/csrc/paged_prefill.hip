@@ -122,9 +122,11 @@ struct Mfma<F16> {
 
 constexpr int kXcds = 8;  // accelerator complex dies of the MI355X
 
-// Three wavefronts per SIMD (at most 168 registers per lane): the kernel
+// Three wavefronts per SIMD (at most 168 registers per lane): the tile loop
 // fits without spilling once the accumulators live in the general register
-// file, and the third wavefront hides the LDS and global-load latency.
+// file, and the third wavefront hides the LDS and global-load latency. (The
+// bf16 form, which holds both passes, keeps the 64-bit query row offset in
+// scratch between its prologue and its epilogue.)
 template <typename T, int D>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void prefill_kernel(PrefillArgs a) {
