@@ -84,6 +84,15 @@ typedef enum pa_status {
   PA_EHIP = -4         /* the HIP runtime reported an error for the launch */
 } pa_status;
 
+/*
+ * Size limits, checked on the host (PA_EINVAL beyond them): num_blocks at
+ * most 2^31 - 1 in every entry point; one frame, B * H * D * element bytes,
+ * under 2^31 bytes (decode and prefill address inside a frame with 32-bit
+ * offsets); decode: S and the partition count at most 65,535 each and the
+ * partial results, S * H * partitions * (D + 2) * 4 bytes, at most 2^62;
+ * prefill: as stated at paged_attn_prefill.
+ */
+
 /* Shapes and types of one decode call. */
 typedef struct pa_decode_shape {
   int32_t num_seqs;            /* S: queries, one per sequence */

@@ -86,6 +86,11 @@ pa_status check_shape(const pa_decode_shape* sh, int32_t* part_tokens, int32_t* 
   if (static_cast<int64_t>(sh->max_context_len) + pt > 0x7FFFFFFFLL) return PA_EINVAL;
   int64_t parts = sh->max_context_len <= pt ? 1 : (sh->max_context_len + pt - 1) / pt;
   if (parts > kMaxGridYZ) return PA_EINVAL;
+  // The partial results, S * H * parts * (D + 2) floats, must be addressable
+  // (this also keeps the workspace size from overflowing size_t).
+  const unsigned __int128 partials = static_cast<unsigned __int128>(sh->num_seqs) * sh->num_heads *
+                                     static_cast<uint64_t>(parts) * (sh->head_dim + 2) * sizeof(float);
+  if (partials > (static_cast<unsigned __int128>(1) << 62)) return PA_EINVAL;
   *part_tokens = static_cast<int32_t>(pt);
   *max_parts = static_cast<int32_t>(parts);
   return PA_OK;
@@ -209,7 +214,7 @@ pa_status kv_append(const void* k_new, const void* v_new, const int64_t* slot_ma
                     int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype dtype,
                     void* stream) {
   if (num_tokens < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
-      !valid_dtype(dtype))
+      num_blocks > 0x7FFFFFFFLL || !valid_dtype(dtype))
     return PA_EINVAL;
   const int64_t row_bytes = static_cast<int64_t>(num_heads) * head_dim * elem_bytes(dtype);
   if ((static_cast<int64_t>(head_dim) * elem_bytes(dtype)) % 16 != 0) return PA_EINVAL;
@@ -228,7 +233,7 @@ pa_status kv_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_pair
                          int64_t num_pairs, int32_t num_heads, int32_t head_dim,
                          int32_t block_size, int64_t num_blocks, pa_dtype dtype, void* stream) {
   if (num_pairs < 0 || num_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
-      !valid_dtype(dtype))
+      num_blocks > 0x7FFFFFFFLL || !valid_dtype(dtype))
     return PA_EINVAL;
   if ((static_cast<int64_t>(head_dim) * elem_bytes(dtype)) % 16 != 0) return PA_EINVAL;
   if (num_pairs > 0x7FFFFFFF) return PA_EINVAL;

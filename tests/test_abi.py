@@ -147,6 +147,23 @@ def test_noalloc_argument_errors():
     assert call(shape(num_seqs=0)) == 0
 
 
+def test_decode_partials_must_be_addressable():
+    """S * H * partitions * (D + 2) floats of partial results beyond 2^62
+    bytes is PA_EINVAL (the workspace size would overflow), checked before
+    any device call; the same shape with a few sequences is accepted."""
+    lib = pkv.load()
+    p = ctypes.c_void_p(1 << 20)
+    huge = shape(num_seqs=65535, num_heads=1 << 25, head_dim=16, block_size=1,
+                 max_context_len=65535 * 128, max_blocks_per_seq=65535 * 128, partition_tokens=128)
+    assert pkv.workspace_size(huge) == 0
+    assert pkv.partition_tokens(huge) == 0
+    assert lib.paged_attn_decode(p, p, p, p, p, 1, 0.25, p, ctypes.byref(huge), p, 1 << 62,
+                                 None) == -1
+    small = shape(num_seqs=2, num_heads=1 << 25, head_dim=16, block_size=1,
+                  max_context_len=65535 * 128, max_blocks_per_seq=65535 * 128, partition_tokens=128)
+    assert pkv.workspace_size(small) > 0
+
+
 def test_partition_size_with_a_dispatch_order():
     """With a dispatch order the default partition targets about 1,024
     workgroups instead of 8,192."""
@@ -187,6 +204,7 @@ def test_append_and_gather_argument_errors():
     assert lib.kv_append(p, p, p, p, p, 4, 1, 4, 16, 100, L.PA_F16, None) == -1  # 8-byte rows
     assert lib.kv_append(ctypes.c_void_p((1 << 20) + 4), p, p, p, p, 4, 32, 128, 16, 100,
                          L.PA_BF16, None) == -2
+    assert lib.kv_append(p, p, p, p, p, 4, 32, 128, 16, 1 << 31, L.PA_BF16, None) == -1
     assert lib.paged_gather(p, p, p, p, p, 2, 2, 16, 10, 100, 2, 21, L.PA_F32, None) == -1
     assert lib.paged_gather(p, p, p, p, p, 0, 2, 16, 10, 100, 2, 20, L.PA_F32, None) == 0
     assert lib.paged_gather(None, p, p, p, p, 2, 2, 16, 10, 100, 2, 20, L.PA_F32, None) == -1
@@ -198,6 +216,7 @@ def test_copy_blocks_argument_errors():
     assert lib.kv_copy_blocks(p, p, p, 0, 32, 128, 16, 100, L.PA_BF16, None) == 0
     assert lib.kv_copy_blocks(None, p, p, 3, 32, 128, 16, 100, L.PA_BF16, None) == -1
     assert lib.kv_copy_blocks(p, p, p, -1, 32, 128, 16, 100, L.PA_BF16, None) == -1
+    assert lib.kv_copy_blocks(p, p, p, 3, 32, 128, 16, 1 << 31, L.PA_BF16, None) == -1
     assert lib.kv_copy_blocks(p, p, ctypes.c_void_p((1 << 20) + 4), 3, 32, 128, 16, 100,
                               L.PA_BF16, None) == -2
 
