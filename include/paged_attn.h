@@ -370,7 +370,8 @@ pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_c
  * out[out_row_start[s] + i]. Uses the same device translation routine as
  * paged_attn_decode's general path. out_row_start is a device int64 [S]
  * array chosen by the caller (normally the prefix sums of context_lens).
- * Not part of the hot path.
+ * cache and out 16-byte aligned, block_tables and context_lens 4-byte,
+ * out_row_start 8-byte (else PA_EALIGN). Not part of the hot path.
  */
 pa_status paged_gather(const void* cache, const int32_t* block_tables,
                        const int32_t* context_lens, const int64_t* out_row_start, void* out,

@@ -433,7 +433,9 @@ pa_status paged_gather(const void* cache, const int32_t* block_tables,
   if (num_seqs > kMaxGridYZ) return PA_EINVAL;
   if (num_seqs == 0 || max_context_len == 0) return PA_OK;
   if (!cache || !block_tables || !context_lens || !out_row_start || !out) return PA_EINVAL;
-  if (!aligned(cache, 16) || !aligned(out, 16)) return PA_EALIGN;
+  if (!aligned(cache, 16) || !aligned(out, 16) || !aligned(block_tables, 4) ||
+      !aligned(context_lens, 4) || !aligned(out_row_start, 8))
+    return PA_EALIGN;
   const int64_t row_bytes = static_cast<int64_t>(num_heads) * head_dim * elem_bytes(dtype);
   return from_hip(pa::launch_gather(cache, block_tables, context_lens, out_row_start, out,
                                     num_seqs, row_bytes, block_size, num_blocks,

@@ -208,6 +208,10 @@ def test_append_and_gather_argument_errors():
     assert lib.paged_gather(p, p, p, p, p, 2, 2, 16, 10, 100, 2, 21, L.PA_F32, None) == -1
     assert lib.paged_gather(p, p, p, p, p, 0, 2, 16, 10, 100, 2, 20, L.PA_F32, None) == 0
     assert lib.paged_gather(None, p, p, p, p, 2, 2, 16, 10, 100, 2, 20, L.PA_F32, None) == -1
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.paged_gather(p, p, p, odd, p, 2, 2, 16, 10, 100, 2, 20, L.PA_F32, None) == -2
+    assert lib.paged_gather(p, ctypes.c_void_p((1 << 20) + 2), p, p, p, 2, 2, 16, 10, 100, 2, 20,
+                            L.PA_F32, None) == -2
 
 
 def test_copy_blocks_argument_errors():
