@@ -141,17 +141,38 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
-def _stream(stream) -> int:
+def _stream(stream, device) -> int:
+    """The HIP stream to launch on: ``stream``, else ``device``'s current one."""
     import torch
 
-    s = stream if stream is not None else torch.cuda.current_stream()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    if s.device != device:
+        raise ValueError(f"the stream is on {s.device}, the tensors on {device}")
     return s.cuda_stream
 
 
-def _dense(*tensors) -> None:
+def _dense(*tensors):
+    """Check that the tensors (None skipped) are contiguous and on one GPU;
+    return that device."""
+    dev = None
     for t in tensors:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous and on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors must be on one GPU (found {dev} and {t.device})")
+    return dev
+
+
+def _on(device):
+    """Make ``device`` current for a library call (the no-allocation entry
+    point uses the current device's scratch)."""
+    import torch
+
+    return torch.cuda.device(device)
 
 
 def make_shape(q, k_cache, block_tables, max_context_len: int, out_dtype_code: int | None = None,
@@ -162,7 +183,6 @@ def make_shape(q, k_cache, block_tables, max_context_len: int, out_dtype_code: i
     NB, B = k_cache.shape[0], k_cache.shape[1]
     kv = dtype_code(k_cache)
     if dispatch_order is not None:
-        _dense(dispatch_order)
         if str(dispatch_order.dtype) != "torch.int32" or dispatch_order.dim() != 1:
             raise TypeError("dispatch_order must be a 1-D int32 tensor")
     return DecodeShape(S, H, D, B, NB, block_tables.shape[1], int(max_context_len), kv,
@@ -190,7 +210,7 @@ def alloc_workspace(shape: DecodeShape, device=None):
 
 def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
     """Write ``k_new``/``v_new`` ``[N, H, D]`` rows into their slots (int64 ``[N]``)."""
-    _dense(k_new, v_new, slot_mapping, k_cache, v_cache)
+    dev = _dense(k_new, v_new, slot_mapping, k_cache, v_cache)
     N, H, D = k_new.shape
     NB, B = k_cache.shape[0], k_cache.shape[1]
     if k_cache.shape != (NB, B, H, D) or v_cache.shape != k_cache.shape or v_new.shape != k_new.shape:
@@ -199,26 +219,31 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None
         raise TypeError("dtype mismatch")
     if slot_mapping.shape != (N,) or str(slot_mapping.dtype) != "torch.int64":
         raise TypeError("slot_mapping must be int64 [N]")
-    _check("kv_append", load().kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache),
-                                         _ptr(v_cache), N, H, D, B, NB, dtype_code(k_cache),
-                                         _stream(stream)))
+    with _on(dev):
+        _check("kv_append", load().kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping),
+                                             _ptr(k_cache), _ptr(v_cache), N, H, D, B, NB,
+                                             dtype_code(k_cache), _stream(stream, dev)))
 
 
 def kv_copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
     """Copy frames ``block_pairs[:, 0]`` to ``block_pairs[:, 1]`` (int64 ``[n, 2]``) in both caches."""
-    _dense(k_cache, v_cache, block_pairs)
+    dev = _dense(k_cache, v_cache, block_pairs)
     NB, B, H, D = k_cache.shape
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise ValueError("k_cache and v_cache must match")
     if block_pairs.dim() != 2 or block_pairs.shape[1] != 2 or str(block_pairs.dtype) != "torch.int64":
         raise TypeError("block_pairs must be int64 [n, 2]")
-    _check("kv_copy_blocks", load().kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(block_pairs),
-                                                   block_pairs.shape[0], H, D, B, NB,
-                                                   dtype_code(k_cache), _stream(stream)))
+    with _on(dev):
+        _check("kv_copy_blocks", load().kv_copy_blocks(_ptr(k_cache), _ptr(v_cache),
+                                                       _ptr(block_pairs), block_pairs.shape[0], H,
+                                                       D, B, NB, dtype_code(k_cache),
+                                                       _stream(stream, dev)))
 
 
-def _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out):
-    _dense(q, k_cache, v_cache, block_tables, context_lens, out)
+def _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out, *more):
+    """Shape and dtype checks of the decode bindings; returns the device
+    (``more``: further tensors that must be on it, None allowed)."""
+    dev = _dense(q, k_cache, v_cache, block_tables, context_lens, out, *more)
     S, H, D = q.shape
     if k_cache.shape[2:] != (H, D) or v_cache.shape != k_cache.shape or out.shape != (S, H, D):
         raise ValueError("shape mismatch")
@@ -228,6 +253,7 @@ def _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out):
         raise TypeError("block_tables and context_lens must be int32")
     if block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables / context_lens do not match q")
+    return dev
 
 
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_size: int, scale: float,
@@ -245,21 +271,23 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, block_siz
     Batches whose sequences share frames read them once per family with
     ``paged_attn_decode_grouped`` instead.
     """
-    _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out)
+    dev = _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out, workspace,
+                         dispatch_order)
     shape = make_shape(q, k_cache, block_tables, max_context_len, dtype_code(out), partition_tokens,
                        cache_policy, dispatch_order)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     lib = load()
-    st = _stream(stream)
-    if phase == "merge":
-        _check("paged_attn_merge", lib.paged_attn_merge(_ptr(context_lens), _ptr(out),
-                                                        ctypes.byref(shape), _ptr(workspace),
-                                                        ws_bytes, st))
-        return
-    fn = {"both": "paged_attn_decode", "partitions": "paged_attn_decode_partitions"}[phase]
-    _check(fn, getattr(lib, fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                _ptr(context_lens), int(block_size), float(scale), _ptr(out),
-                                ctypes.byref(shape), _ptr(workspace), ws_bytes, st))
+    st = _stream(stream, dev)
+    with _on(dev):
+        if phase == "merge":
+            _check("paged_attn_merge", lib.paged_attn_merge(_ptr(context_lens), _ptr(out),
+                                                            ctypes.byref(shape), _ptr(workspace),
+                                                            ws_bytes, st))
+            return
+        fn = {"both": "paged_attn_decode", "partitions": "paged_attn_decode_partitions"}[phase]
+        _check(fn, getattr(lib, fn)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                    _ptr(context_lens), int(block_size), float(scale), _ptr(out),
+                                    ctypes.byref(shape), _ptr(workspace), ws_bytes, st))
 
 
 def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, block_size: int,
@@ -269,13 +297,15 @@ def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, b
     """``paged_attn_decode`` without a workspace: partial results go to the
     library's fixed per-GPU scratch (see include/paged_attn.h). Calls that
     overlap in time on one GPU race."""
-    _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out)
+    dev = _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out, dispatch_order)
     shape = make_shape(q, k_cache, block_tables, max_context_len, dtype_code(out), partition_tokens,
                        cache_policy, dispatch_order)
-    _check("paged_attn_decode_noalloc",
-           load().paged_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                            _ptr(context_lens), int(block_size), float(scale),
-                                            _ptr(out), ctypes.byref(shape), _stream(stream)))
+    with _on(dev):
+        _check("paged_attn_decode_noalloc",
+               load().paged_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                _ptr(block_tables), _ptr(context_lens),
+                                                int(block_size), float(scale), _ptr(out),
+                                                ctypes.byref(shape), _stream(stream, dev)))
 
 
 def paged_attn_decode_grouped(q, k_cache, v_cache, block_tables, context_lens, block_size: int,
@@ -285,8 +315,8 @@ def paged_attn_decode_grouped(q, k_cache, v_cache, block_tables, context_lens, b
     """Decode attention with groups of sequences that share leading frames
     (int32 device ``group_start`` [G + 1], ``group_shared`` [G] tokens); see
     include/paged_attn.h. ``workspace`` is sized as for ``paged_attn_decode``."""
-    _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out)
-    _dense(group_start, group_shared)
+    dev = _decode_checks(q, k_cache, v_cache, block_tables, context_lens, out, group_start,
+                         group_shared, workspace, dispatch_order)
     G = group_shared.numel()
     if group_start.numel() != G + 1:
         raise ValueError("group_start must have one more entry than group_shared")
@@ -295,11 +325,14 @@ def paged_attn_decode_grouped(q, k_cache, v_cache, block_tables, context_lens, b
     shape = make_shape(q, k_cache, block_tables, max_context_len, dtype_code(out), partition_tokens,
                        cache_policy, dispatch_order)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("paged_attn_decode_grouped",
-           load().paged_attn_decode_grouped(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                            _ptr(context_lens), int(block_size), float(scale), _ptr(out),
-                                            ctypes.byref(shape), _ptr(group_start), _ptr(group_shared),
-                                            G, _ptr(workspace), ws_bytes, _stream(stream)))
+    with _on(dev):
+        _check("paged_attn_decode_grouped",
+               load().paged_attn_decode_grouped(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                _ptr(block_tables), _ptr(context_lens),
+                                                int(block_size), float(scale), _ptr(out),
+                                                ctypes.byref(shape), _ptr(group_start),
+                                                _ptr(group_shared), G, _ptr(workspace), ws_bytes,
+                                                _stream(stream, dev)))
 
 
 def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, block_size: int,
@@ -312,7 +345,7 @@ def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_st
     (``driver.prefill_order``). ``split_weights`` (bf16 caches): keep V in
     bf16 and enter each softmax weight as a bf16 value plus its residual
     instead of one fp16 rounding."""
-    _dense(q, k_cache, v_cache, block_tables, context_lens, query_start, out, work_order)
+    dev = _dense(q, k_cache, v_cache, block_tables, context_lens, query_start, out, work_order)
     T, H, D = q.shape
     NB, B = k_cache.shape[0], k_cache.shape[1]
     S = context_lens.shape[0]
@@ -331,22 +364,25 @@ def paged_attn_prefill(q, k_cache, v_cache, block_tables, context_lens, query_st
     shape = PrefillShape(S, H, D, B, NB, block_tables.shape[1], int(max_context_len),
                          int(max_query_len), T, dtype_code(k_cache), dtype_code(out),
                          1 if split_weights else 0)
-    _check("paged_attn_prefill", load().paged_attn_prefill(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
-        _ptr(query_start), int(block_size), float(scale), _ptr(out), ctypes.byref(shape),
-        _ptr(work_order), _stream(stream)))
+    with _on(dev):
+        _check("paged_attn_prefill", load().paged_attn_prefill(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+            _ptr(query_start), int(block_size), float(scale), _ptr(out), ctypes.byref(shape),
+            _ptr(work_order), _stream(stream, dev)))
 
 
 def paged_gather(cache, block_tables, context_lens, out_row_start, out, max_context_len: int,
                  stream=None) -> None:
     """Copy each sequence's rows, in logical order, into ``out`` ``[T, H, D]``."""
-    _dense(cache, block_tables, context_lens, out_row_start, out)
+    dev = _dense(cache, block_tables, context_lens, out_row_start, out)
     NB, B, H, D = cache.shape
     S = context_lens.shape[0]
-    _check("paged_gather", load().paged_gather(_ptr(cache), _ptr(block_tables), _ptr(context_lens),
-                                               _ptr(out_row_start), _ptr(out), S, H, D, B, NB,
-                                               block_tables.shape[1], int(max_context_len),
-                                               dtype_code(cache), _stream(stream)))
+    with _on(dev):
+        _check("paged_gather", load().paged_gather(_ptr(cache), _ptr(block_tables),
+                                                   _ptr(context_lens), _ptr(out_row_start),
+                                                   _ptr(out), S, H, D, B, NB, block_tables.shape[1],
+                                                   int(max_context_len), dtype_code(cache),
+                                                   _stream(stream, dev)))
 
 
 class kernel_timing:
@@ -375,9 +411,10 @@ class kernel_timing:
 def stream_read(buf, sink, stream=None) -> None:
     """Streaming-read bandwidth probe over a dense device tensor ``buf``
     (see pa_stream_read); ``sink`` is a device int32/uint32 scalar tensor."""
-    _dense(buf)
-    _check("pa_stream_read", load().pa_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
-                                                   _ptr(sink), _stream(stream)))
+    dev = _dense(buf, sink)
+    with _on(dev):
+        _check("pa_stream_read", load().pa_stream_read(_ptr(buf), buf.numel() * buf.element_size(),
+                                                       _ptr(sink), _stream(stream, dev)))
 
 
 def frame_read(buf, frame_order, frame_bytes: int, groups: int, group_stride: int, pieces: int,
@@ -385,10 +422,11 @@ def frame_read(buf, frame_order, frame_bytes: int, groups: int, group_stride: in
     """Frame-pattern read probe over a dense device tensor ``buf`` holding
     ``frame_order.numel()`` frames (see pa_frame_read); ``frame_order`` is a
     device int32 tensor, ``sink`` a device int32/uint32 scalar tensor."""
-    _dense(buf, frame_order)
+    dev = _dense(buf, frame_order, sink)
     if str(frame_order.dtype) != "torch.int32" or frame_order.dim() != 1:
         raise TypeError("frame_order must be a 1-D int32 tensor")
-    _check("pa_frame_read", load().pa_frame_read(
-        _ptr(buf), buf.numel() * buf.element_size(), _ptr(frame_order), frame_order.numel(),
-        int(frame_bytes), int(groups), int(group_stride), int(pieces), int(piece_stride),
-        int(piece_bytes), int(frames_per_unit), _ptr(sink), _stream(stream)))
+    with _on(dev):
+        _check("pa_frame_read", load().pa_frame_read(
+            _ptr(buf), buf.numel() * buf.element_size(), _ptr(frame_order), frame_order.numel(),
+            int(frame_bytes), int(groups), int(group_stride), int(pieces), int(piece_stride),
+            int(piece_bytes), int(frames_per_unit), _ptr(sink), _stream(stream, dev)))

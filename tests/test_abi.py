@@ -305,3 +305,19 @@ def test_frame_read_argument_errors():
     assert call(buf=None) == -1
     assert call(buf=ctypes.c_void_p((1 << 20) + 8)) == -2
     assert call(order=ctypes.c_void_p((1 << 20) + 2)) == -2
+
+
+def test_binding_rejects_host_tensors():
+    """The Python binding only marshals device tensors: host (or
+    non-contiguous) tensors are refused before the library is called."""
+    import torch
+
+    k = torch.zeros(4, 16, 2, 128, dtype=torch.bfloat16)
+    new = torch.zeros(3, 2, 128, dtype=torch.bfloat16)
+    slots = torch.zeros(3, dtype=torch.int64)
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.kv_append(new, new, slots, k, k)
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.lib.paged_gather(k, torch.zeros(1, 1, dtype=torch.int32),
+                             torch.zeros(1, dtype=torch.int32), torch.zeros(1, dtype=torch.int64),
+                             torch.zeros(16, 2, 128, dtype=torch.bfloat16), 16)
