@@ -22,7 +22,9 @@ unless --ungrouped), 5 batch 256 with the step's kv_append (--permuted-pool
 for its pool-order variant); 6 and 7 paged prefill (a 512-token chunk after
 a cached prefix, whole prompts); 8 prefix-cached prefill rounds, with and
 without caching. Decode and prefill dispatch their longest work first unless
---decode-batch-order / --prefill-batch-order. --gpus N > 1 exits: the
+--decode-batch-order / --prefill-batch-order. --head-dim / --dtype /
+--block-size run workload 2 at another head dim (H = 4096 / d, so a token's
+row keeps its size), storage dtype or block size. --gpus N > 1 exits: the
 library runs on one GPU.
 """
 from __future__ import annotations
@@ -720,6 +722,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--head-dim", type=int, default=0, choices=(0, 16, 32, 64, 128, 256),
+                    help="workload 2 with this head dim (H = 4096 / d, the same bytes per token)")
+    ap.add_argument("--dtype", default="", choices=("", "bf16", "f16", "f32"),
+                    help="workload 2 with this storage dtype")
     ap.add_argument("--block-size", type=int, default=0,
                     help="workloads 2 and 3: tokens per frame (default 16; the pool keeps its "
                          "slot count)")
@@ -765,10 +771,16 @@ def main():
     if args.block_size and args.workload not in (2, 3):
         print("--block-size applies to workloads 2 and 3 only", file=sys.stderr)
         sys.exit(2)
+    if (args.head_dim or args.dtype) and args.workload != 2:
+        print("--head-dim and --dtype apply to workload 2 only", file=sys.stderr)
+        sys.exit(2)
     if args.permuted_pool and args.workload != 5:
         print("--permuted-pool applies to workload 5 only", file=sys.stderr)
         sys.exit(2)
-    if args.block_size:
+    if args.head_dim or args.dtype:
+        w = configs.config2(B=args.block_size or 16, D=args.head_dim or 128,
+                            dtype=args.dtype or "bf16")
+    elif args.block_size:
         w = {2: configs.config2, 3: configs.config3}[args.workload](B=args.block_size)
     elif args.permuted_pool:
         w = configs.config5(permuted=True)
@@ -1138,6 +1150,7 @@ def main():
                                  "decode steps) before timing"},
     }
     default_run = (args.workload == 2 and not args.block_size and not args.partition_tokens
+                   and not args.head_dim and not args.dtype
                    and not args.decode_batch_order and not args.ungrouped)
     if default_run and not args.no_others:
         res["other_workloads"] = other_workloads(args)

@@ -69,7 +69,7 @@ pa_status check_shape(const pa_decode_shape* sh, int32_t* part_tokens, int32_t* 
   if (static_cast<int64_t>(sh->block_size) * sh->num_heads * sh->head_dim * elem_bytes(sh->kv_dtype) >
       0x7FFFFFFFLL)
     return PA_EINVAL;
-  const int chunk = pa::chunk_tokens(to_internal(sh->kv_dtype), sh->head_dim);
+  const int chunk = pa::chunk_tokens(to_internal(sh->kv_dtype), sh->head_dim, sh->num_heads);
   if (chunk <= 0) return PA_EINVAL;
   if (sh->cache_policy != PA_CACHE_STREAM && sh->cache_policy != PA_CACHE_REUSE) return PA_EINVAL;
   int64_t pt = sh->partition_tokens;

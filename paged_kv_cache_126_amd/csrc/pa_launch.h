@@ -65,9 +65,10 @@ struct GroupArgs {
 
 enum class Dtype : int { F32 = 0, F16 = 1, BF16 = 2 };
 
-// Tokens one wavefront processes per loop iteration for (dtype, head_dim);
-// partition sizes are multiples of it. 0 if the combination is unsupported.
-int chunk_tokens(Dtype dt, int head_dim);
+// Tokens one wavefront processes per loop iteration for (dtype, head_dim,
+// heads); partition sizes are multiples of it. 0 if the combination is
+// unsupported.
+int chunk_tokens(Dtype dt, int head_dim, int num_heads);
 
 // Queue the partition pass / the merge pass. Return a hipError_t.
 hipError_t launch_decode_partitions(const DecodeArgs& a, Dtype dt, int head_dim,

@@ -9,13 +9,17 @@
 // (page 2, "Implementation"). As page 1 ("3. PagedAttention CUDA Kernel
 // Execution") asks, the kernel takes the block table itself: no gathered copy.
 //
-// Work decomposition. One workgroup per (head, context partition, sequence),
-// head fastest so the workgroups in flight together read whole frames (all
-// heads of a token are adjacent). The workgroup's kNW wavefronts take the
-// partition's chunks of kCH tokens round robin. Inside a wavefront, each
-// cache row (one token's D elements of head h) is spread over kLPR lanes
-// holding 16 bytes each, so one load instruction moves kRPL whole rows and
-// every lane issues 16-byte loads. q . k is a per-lane dot product (packed
+// Work decomposition. One workgroup per (head group, context partition,
+// sequence), head fastest so the workgroups in flight together read whole
+// frames (all heads of a token are adjacent). A head group is HP adjacent
+// heads: one for rows of 256 bytes or more, enough for 256 contiguous bytes
+// per token below that (a 64-byte row alone would leave the other half of
+// each 128-byte line to another workgroup, and the line would be fetched
+// twice). The workgroup's kNW wavefronts take the partition's chunks of kCH
+// tokens round robin. Inside a wavefront, each cache row (one token's D
+// elements of one head) is spread over kLPR lanes holding 16 bytes each, so
+// one load instruction moves kRPL whole rows (kRPL / HP tokens of HP heads)
+// and every lane issues 16-byte loads. q . k is a per-lane dot product (packed
 // dot2 instructions for 16-bit types) finished by DPP sums inside each group
 // of kLPR lanes. Softmax is online: each lane group keeps its own running
 // maximum m (in log2 units), sum l and fp32 accumulator for its kVEC output
@@ -60,24 +64,36 @@ __device__ __forceinline__ u32x4 load_row(const char* p) {
     return load16(p);
 }
 
-template <typename T, int D>
+// A workgroup serves HP adjacent heads. With HP > 1 the lane groups of one
+// load take the HP heads in turn, so each token's HP rows (adjacent in a
+// [NB, B, H, D] frame) are read as one contiguous span: rows under 256 bytes
+// then no longer leave the rest of a 128-byte line to another workgroup.
+template <typename T, int D, int HP>
 struct Tiling {
   static constexpr int kVEC = Vec<T>::kElems;  // elements a lane holds per row
   static constexpr int kLPR = D / kVEC;        // lanes per cache row
   static constexpr int kRPL = 64 / kLPR;       // rows per wavefront load
-  static constexpr int kCH = kU * kRPL;        // tokens per chunk
+  static constexpr int kTPL = kRPL / HP;       // tokens per wavefront load
+  static constexpr int kCH = kU * kTPL;        // tokens per chunk
   static_assert(kLPR >= 1 && kLPR <= 64 && (64 % kLPR) == 0, "row must tile a wavefront");
+  static_assert(HP >= 1 && kRPL % HP == 0, "a load must hold whole tokens");
 };
 
-// Per-lane constants of the chunk loads of one (sequence, head).
-template <typename T, int D, int BT, bool kStream>
+// Heads per workgroup for a row of `row_bytes`: enough for 256 contiguous
+// bytes per token (rows are 32 bytes or more).
+constexpr int preferred_heads(int row_bytes) {
+  return row_bytes >= 256 ? 1 : 256 / row_bytes;
+}
+
+// Per-lane constants of the chunk loads of one (sequence, head group).
+template <typename T, int D, int BT, bool kStream, int HP>
 struct ChunkLoader {
-  using Tl = Tiling<T, D>;
-  static constexpr int VEC = Tl::kVEC, LPR = Tl::kLPR, RPL = Tl::kRPL, CH = Tl::kCH;
+  using Tl = Tiling<T, D, HP>;
+  static constexpr int VEC = Tl::kVEC, LPR = Tl::kLPR, TPL = Tl::kTPL, CH = Tl::kCH;
   // Uniform translation: with a compile-time block size that is a multiple
-  // of the rows per load, the kRPL rows of one load share a frame, so the
-  // frame is read once per load as a scalar.
-  static constexpr bool kUniformFrame = BT > 0 && (BT % RPL) == 0;
+  // of the tokens per load, the kTPL tokens of one load share a frame, so
+  // the frame is read once per load as a scalar.
+  static constexpr bool kUniformFrame = BT > 0 && (BT % TPL) == 0;
 
   const char* kbase;
   const char* vbase;
@@ -90,15 +106,17 @@ struct ChunkLoader {
   uint32_t max_frame;   // num_blocks - 1 (num_blocks <= 2^31)
   int32_t block_size;
   int64_t num_blocks;
-  int grp;              // which of the kRPL rows of a load this lane holds
+  int tok;              // which of the kTPL tokens of a load this lane reads
 
-  __device__ __forceinline__ ChunkLoader(const DecodeArgs& a, const int h, const int lane) {
+  // h0: the group's first head; the lane reads head h0 + (lane / LPR) % HP.
+  __device__ __forceinline__ ChunkLoader(const DecodeArgs& a, const int h0, const int lane) {
     kbase = static_cast<const char*>(a.k_cache);
     vbase = static_cast<const char*>(a.v_cache);
     row_bytes = static_cast<uint32_t>(a.num_heads) * D * T::kBytes;
     frame_bytes = static_cast<int64_t>(row_bytes) * a.block_size;
-    grp = lane / LPR;
-    lane_bytes = (static_cast<uint32_t>(h) * D + (lane % LPR) * VEC) * T::kBytes;
+    tok = lane / LPR / HP;
+    const uint32_t h = static_cast<uint32_t>(h0 + (lane / LPR) % HP);
+    lane_bytes = (h * D + (lane % LPR) * VEC) * T::kBytes;
     max_frame = static_cast<uint32_t>(a.num_blocks - 1);
     block_size = a.block_size;
     num_blocks = a.num_blocks;
@@ -112,7 +130,7 @@ struct ChunkLoader {
   __device__ __forceinline__ void load(const int32_t* table_row, const int t0, const int tok_end,
                                        u32x4 (&kv)[kU], u32x4 (&vv)[kU], bool (&valid)[kU]) const {
 #pragma unroll
-    for (int u = 0; u < kU; ++u) valid[u] = !kMasked || (t0 + u * RPL + grp < tok_end);
+    for (int u = 0; u < kU; ++u) valid[u] = !kMasked || (t0 + u * TPL + tok < tok_end);
     if constexpr (kUniformFrame) {
       // All block-table reads of the chunk first (scalar loads). A load
       // wholly past tok_end reads the last valid table entry instead (its
@@ -120,19 +138,19 @@ struct ChunkLoader {
       uint32_t frame[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const uint32_t tu = static_cast<uint32_t>(t0 + u * RPL);  // wave-uniform
+        const uint32_t tu = static_cast<uint32_t>(t0 + u * TPL);  // wave-uniform
         const uint32_t tc = kMasked ? min(tu, static_cast<uint32_t>(tok_end - 1)) : tu;
         frame[u] = static_cast<uint32_t>(table_row[tc / BT]);
       }
       int64_t step_base[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        const uint32_t tu = static_cast<uint32_t>(t0 + u * RPL);
+        const uint32_t tu = static_cast<uint32_t>(t0 + u * TPL);
         // Out-of-range (or negative) entries are clamped into the pool.
         const uint32_t f = min(frame[u], max_frame);
         step_base[u] = static_cast<int64_t>(f) * frame_bytes + static_cast<int64_t>(tu % BT) * row_bytes;
       }
-      const uint32_t lane_off = grp * row_bytes + lane_bytes;
+      const uint32_t lane_off = tok * row_bytes + lane_bytes;
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         u32x4 kz = {0u, 0u, 0u, 0u}, vz = {0u, 0u, 0u, 0u};
@@ -149,7 +167,7 @@ struct ChunkLoader {
         u32x4 kz = {0u, 0u, 0u, 0u}, vz = {0u, 0u, 0u, 0u};
         if (valid[u]) {
           const int64_t off =
-              token_row(table_row, t0 + u * RPL + grp, block_size, num_blocks) * row_bytes +
+              token_row(table_row, t0 + u * TPL + tok, block_size, num_blocks) * row_bytes +
               lane_bytes;
           kz = load_row<kStream>(kbase + off);
           vz = load_row<kStream>(vbase + off);
@@ -165,7 +183,7 @@ struct ChunkLoader {
 // (log2 units), running sum l and the lane's kVEC accumulator elements.
 template <typename T, int D>
 struct SoftmaxState {
-  static constexpr int VEC = Tiling<T, D>::kVEC;
+  static constexpr int VEC = Tiling<T, D, 1>::kVEC;
   float m, l;
   float acc[VEC];
 
@@ -181,7 +199,7 @@ struct SoftmaxState {
   __device__ __forceinline__ void update(const u32x4 qv, const float scale_log2,
                                          const u32x4 (&kv)[kU], const u32x4 (&vv)[kU],
                                          const bool (&valid)[kU]) {
-    constexpr int LPR = Tiling<T, D>::kLPR;
+    constexpr int LPR = Tiling<T, D, 1>::kLPR;
     float sc[kU];
     float cmax = kNegBig;
 #pragma unroll
@@ -208,34 +226,35 @@ struct SoftmaxState {
   }
 };
 
-// LDS of the wavefront combine.
-template <int D>
+// LDS of the wavefront combine: per wavefront, each of the HP heads' state.
+template <int D, int HP>
 struct CombineLds {
-  float m[kNW];
-  float l[kNW];
-  float acc[kNW][D];
+  float m[kNW][HP];
+  float l[kNW][HP];
+  float acc[kNW][HP * D];
 };
 
-// Combine a (sequence, head, partition)'s states of all lane groups and
-// wavefronts (log-sum-exp rule) and store the result: the normalised output
-// when the sequence has one partition, else the partition's partial (max,
-// sum, unnormalised output) in the workspace. Every thread of the workgroup
-// calls it; it synchronises the workgroup and leaves `lds` free for reuse
-// after a further barrier.
-template <typename T, int D>
-__device__ __forceinline__ void finish_partition(const DecodeArgs& a, const int s, const int h,
+// Combine a (sequence, head group, partition)'s states of all lane groups
+// and wavefronts (log-sum-exp rule, for each head apart) and store the
+// result: the normalised output when the sequence has one partition, else
+// the partition's partial (max, sum, unnormalised output) in the workspace.
+// Every thread of the workgroup calls it; it synchronises the workgroup and
+// leaves `lds` free for reuse after a further barrier.
+template <typename T, int D, int HP>
+__device__ __forceinline__ void finish_partition(const DecodeArgs& a, const int s, const int h0,
                                                  const int part, const int n_parts,
-                                                 SoftmaxState<T, D> st, CombineLds<D>& lds) {
-  using Tl = Tiling<T, D>;
+                                                 SoftmaxState<T, D> st, CombineLds<D, HP>& lds) {
+  using Tl = Tiling<T, D, HP>;
   constexpr int VEC = Tl::kVEC, LPR = Tl::kLPR;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int grp = lane / LPR;
   const int col = lane % LPR;
   float m = st.m, l = st.l;
-  // Combine the kRPL lane groups of the wavefront (lanes col, col + LPR, ...).
+  // Combine the lane groups of the wavefront that hold the same head (lanes
+  // col + LPR * (head + HP * i)).
 #pragma unroll
-  for (int x = LPR; x < 64; x <<= 1) {
+  for (int x = LPR * HP; x < 64; x <<= 1) {
     const float m_o = __shfl_xor(m, x);
     const float l_o = __shfl_xor(l, x);
     const float m_n = fmaxf(m, m_o);
@@ -249,34 +268,33 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const int 
   }
 
   // Combine the wavefronts through LDS.
-  if (grp == 0) {
+  if (grp < HP) {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) lds.acc[wave][col * VEC + j] = st.acc[j];
+    for (int j = 0; j < VEC; ++j) lds.acc[wave][grp * D + col * VEC + j] = st.acc[j];
     if (col == 0) {
-      lds.m[wave] = m;
-      lds.l[wave] = l;
+      lds.m[wave][grp] = m;
+      lds.l[wave][grp] = l;
     }
   }
   __syncthreads();
 
-  float M = kNegBig;
+  for (int e = threadIdx.x; e < HP * D; e += kNW * 64) {
+    const int hs = e / D;
+    float M = kNegBig;
 #pragma unroll
-  for (int w = 0; w < kNW; ++w) M = fmaxf(M, lds.m[w]);
-  float fw[kNW];
-  float L = 0.f;
+    for (int w = 0; w < kNW; ++w) M = fmaxf(M, lds.m[w][hs]);
+    float L = 0.f, O = 0.f;
 #pragma unroll
-  for (int w = 0; w < kNW; ++w) {
-    fw[w] = fast_exp2(lds.m[w] - M);
-    L = __builtin_fmaf(lds.l[w], fw[w], L);
-  }
-  const int64_t sh = static_cast<int64_t>(s) * a.num_heads + h;
-  for (int e = threadIdx.x; e < D; e += kNW * 64) {
-    float O = 0.f;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) O = __builtin_fmaf(lds.acc[w][e], fw[w], O);
+    for (int w = 0; w < kNW; ++w) {
+      const float fw = fast_exp2(lds.m[w][hs] - M);
+      L = __builtin_fmaf(lds.l[w][hs], fw, L);
+      O = __builtin_fmaf(lds.acc[w][e], fw, O);
+    }
+    const int64_t sh = static_cast<int64_t>(s) * a.num_heads + h0 + hs;
+    const int el = e - hs * D;
     if (n_parts == 1) {
       const float r = L > 0.f ? O / L : 0.f;
-      const int64_t o = sh * D + e;
+      const int64_t o = sh * D + el;
       if constexpr (T::kBytes == 4) {
         static_cast<float*>(a.out)[o] = r;
       } else {
@@ -287,8 +305,8 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const int 
       }
     } else {
       const int64_t p = sh * a.max_parts + part;
-      a.ws_acc[p * D + e] = O;
-      if (e == 0) {
+      a.ws_acc[p * D + el] = O;
+      if (el == 0) {
         a.ws_ml[2 * p] = M;
         a.ws_ml[2 * p + 1] = L;
       }
@@ -309,13 +327,13 @@ __device__ __forceinline__ int parts_of(const DecodeArgs& a, const int ctx) {
 // cached loads (frames shared by several sequences of the call).
 // Eight wavefronts per SIMD (at most 64 registers per lane): the kernel is
 // bound by memory latency, so it keeps the most loads in flight.
-template <typename T, int D, int BT, bool kStream>
+template <typename T, int D, int BT, bool kStream, int HP>
 __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_partition_kernel(DecodeArgs a) {
-  using Ld = ChunkLoader<T, D, BT, kStream>;
+  using Ld = ChunkLoader<T, D, BT, kStream, HP>;
   constexpr int VEC = Ld::VEC, LPR = Ld::LPR, CH = Ld::CH;
 
-  const int h = blockIdx.x;
+  const int h0 = blockIdx.x * HP;
   const int part = blockIdx.y;
   const int s = a.seq_order ? min(max(a.seq_order[blockIdx.z], 0), a.num_seqs - 1)
                             : static_cast<int>(blockIdx.z);
@@ -329,8 +347,9 @@ void decode_partition_kernel(DecodeArgs a) {
   // chunk loop, block-table reads and frame arithmetic stay scalar.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const Ld ld(a, h, lane);
+  const Ld ld(a, h0, lane);
   const int32_t* table_row = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
+  const int h = h0 + (lane / LPR) % HP;  // this lane's head
   const u32x4 qv = load16(static_cast<const char*>(a.q) +
                           ((static_cast<int64_t>(s) * a.num_heads + h) * D + (lane % LPR) * VEC) *
                               T::kBytes);
@@ -350,8 +369,8 @@ void decode_partition_kernel(DecodeArgs a) {
     st.update(qv, a.scale_log2, kv, vv, valid);
   }
 
-  __shared__ CombineLds<D> lds;
-  finish_partition<T, D>(a, s, h, part, n_parts, st, lds);
+  __shared__ CombineLds<D, HP> lds;
+  finish_partition<T, D, HP>(a, s, h0, part, n_parts, st, lds);
 }
 
 // Grouped partition pass: a workgroup serves a group of up to G sequences
@@ -363,12 +382,12 @@ void decode_partition_kernel(DecodeArgs a) {
 // chunk-to-wavefront assignment are those of the ungrouped pass (the shared
 // length is rounded down to a whole chunk), so every member's result equals
 // the ungrouped pass's bit for bit.
-template <typename T, int D, int BT, bool kStream, int G>
+template <typename T, int D, int BT, bool kStream, int HP, int G>
 __global__ __launch_bounds__(kNW * 64) void decode_group_kernel(DecodeArgs a, GroupArgs g) {
-  using Ld = ChunkLoader<T, D, BT, kStream>;
+  using Ld = ChunkLoader<T, D, BT, kStream, HP>;
   constexpr int VEC = Ld::VEC, LPR = Ld::LPR, CH = Ld::CH;
 
-  const int h = blockIdx.x;
+  const int h0 = blockIdx.x * HP;
   const int part = blockIdx.y;
   const int gi = a.seq_order ? min(max(a.seq_order[blockIdx.z], 0), g.num_groups - 1)
                              : static_cast<int>(blockIdx.z);
@@ -393,7 +412,8 @@ __global__ __launch_bounds__(kNW * 64) void decode_group_kernel(DecodeArgs a, Gr
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const Ld ld(a, h, lane);
+  const Ld ld(a, h0, lane);
+  const int h = h0 + (lane / LPR) % HP;  // this lane's head
 
   u32x4 qv[G];
   SoftmaxState<T, D> st[G];
@@ -444,13 +464,13 @@ __global__ __launch_bounds__(kNW * 64) void decode_group_kernel(DecodeArgs a, Gr
     }
   }
 
-  __shared__ CombineLds<D> lds;
+  __shared__ CombineLds<D, HP> lds;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     if (i >= members) break;
     const int n_parts = parts_of(a, ctx[i]);
     if (part < n_parts) {  // uniform: the member has tokens in this partition
-      finish_partition<T, D>(a, s0 + i, h, part, n_parts, st[i], lds);
+      finish_partition<T, D, HP>(a, s0 + i, h0, part, n_parts, st[i], lds);
       __syncthreads();  // lds is reused by the next member
     }
   }
@@ -556,44 +576,61 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeAr
   }
 }
 
+// Heads per workgroup of a launch: the preferred grouping for the row size
+// when the head count divides by it, else one head.
+int heads_per_group(int row_bytes, int num_heads) {
+  const int hp = preferred_heads(row_bytes);
+  return num_heads % hp == 0 ? hp : 1;
+}
+
 // Ungrouped (g == nullptr) or grouped partition pass.
-template <typename T, int D, int BT>
+template <typename T, int D, int BT, int HP>
 hipError_t launch_part(const DecodeArgs& a, const GroupArgs* g, hipStream_t stream) {
   const dim3 block(kNW * 64);
   if (g != nullptr) {
-    const dim3 grid(a.num_heads, a.max_parts, g->num_groups);
+    const dim3 grid(a.num_heads / HP, a.max_parts, g->num_groups);
     if (a.stream_loads)
-      return launch_timed(decode_group_kernel<T, D, BT, true, kMaxGroup>, grid, block, stream, a, *g);
-    return launch_timed(decode_group_kernel<T, D, BT, false, kMaxGroup>, grid, block, stream, a, *g);
+      return launch_timed(decode_group_kernel<T, D, BT, true, HP, kMaxGroup>, grid, block, stream, a, *g);
+    return launch_timed(decode_group_kernel<T, D, BT, false, HP, kMaxGroup>, grid, block, stream, a, *g);
   }
-  const dim3 grid(a.num_heads, a.max_parts, a.num_seqs);
+  const dim3 grid(a.num_heads / HP, a.max_parts, a.num_seqs);
   if (a.stream_loads)
-    return launch_timed(decode_partition_kernel<T, D, BT, true>, grid, block, stream, a);
-  return launch_timed(decode_partition_kernel<T, D, BT, false>, grid, block, stream, a);
+    return launch_timed(decode_partition_kernel<T, D, BT, true, HP>, grid, block, stream, a);
+  return launch_timed(decode_partition_kernel<T, D, BT, false, HP>, grid, block, stream, a);
 }
 
-// Block sizes with a uniform-frame specialisation; other sizes take the
-// per-lane translation path (BT = 0).
+template <typename T, int D, int BT>
+hipError_t launch_heads(const DecodeArgs& a, const GroupArgs* g, hipStream_t stream) {
+  constexpr int kHP = preferred_heads(D * T::kBytes);
+  if constexpr (kHP > 1) {
+    if (a.num_heads % kHP == 0) return launch_part<T, D, BT, kHP>(a, g, stream);
+  }
+  return launch_part<T, D, BT, 1>(a, g, stream);
+}
+
+// Block sizes with a uniform-frame specialisation (a multiple of the rows
+// of one load, so of the tokens of one load for any head grouping); other
+// sizes take the per-lane translation path (BT = 0).
 template <typename T, int D>
 hipError_t dispatch_block(const DecodeArgs& a, const GroupArgs* g, hipStream_t stream) {
-  constexpr int RPL = Tiling<T, D>::kRPL;
+  constexpr int RPL = Tiling<T, D, 1>::kRPL;
   switch (a.block_size) {
     case 8:
-      if constexpr (8 % RPL == 0) return launch_part<T, D, 8>(a, g, stream);
+      if constexpr (8 % RPL == 0) return launch_heads<T, D, 8>(a, g, stream);
       break;
     case 16:
-      if constexpr (16 % RPL == 0) return launch_part<T, D, 16>(a, g, stream);
+      if constexpr (16 % RPL == 0) return launch_heads<T, D, 16>(a, g, stream);
       break;
     case 32:
-      if constexpr (32 % RPL == 0) return launch_part<T, D, 32>(a, g, stream);
+      if constexpr (32 % RPL == 0) return launch_heads<T, D, 32>(a, g, stream);
       break;
     case 64:
-      if constexpr (64 % RPL == 0) return launch_part<T, D, 64>(a, g, stream);
+      if constexpr (64 % RPL == 0) return launch_heads<T, D, 64>(a, g, stream);
       break;
     default:
       break;
   }
-  return launch_part<T, D, 0>(a, g, stream);
+  return launch_heads<T, D, 0>(a, g, stream);
 }
 
 template <typename T>
@@ -630,12 +667,12 @@ hipError_t merge_dim(const DecodeArgs& a, int head_dim, hipStream_t stream) {
 
 }  // namespace
 
-int chunk_tokens(Dtype dt, int head_dim) {
+int chunk_tokens(Dtype dt, int head_dim, int num_heads) {
   const int bytes = dt == Dtype::F32 ? 4 : 2;
-  if (head_dim <= 0 || (head_dim * bytes) % 16 != 0) return 0;
+  if (head_dim <= 0 || num_heads <= 0 || (head_dim * bytes) % 16 != 0) return 0;
   const int lpr = head_dim * bytes / 16;
   if (lpr > 64 || 64 % lpr != 0) return 0;
-  return kU * (64 / lpr);
+  return kU * (64 / lpr) / heads_per_group(head_dim * bytes, num_heads);
 }
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, Dtype dt, int head_dim,

@@ -47,10 +47,13 @@ DECODE_CASES = [
 
 @pytest.mark.parametrize("dtype,D,B", DECODE_CASES)
 @pytest.mark.parametrize("pt", [0, 1 << 6])
-def test_decode_shapes(dtype, D, B, pt):
+@pytest.mark.parametrize("H", [3, 8])
+def test_decode_shapes(dtype, D, B, pt, H):
+    """H = 8 takes the launches whose workgroups serve 2 or 4 adjacent heads
+    (rows under 256 bytes); H = 3 the one-head launches of every shape."""
     rng = np.random.default_rng(D * 131 + B)
     ctx = list(rng.integers(1, 400, size=5)) + [1, B, B + 1]
-    w = shape_workload(dtype, D, B, ctx)
+    w = shape_workload(dtype, D, B, ctx, H=H)
     # pt = 64 forces several partitions per sequence (the library rounds it
     # up to a whole number of the kernel's chunks); 0 takes its default
     say(f"[gpu] decode {w.description}, partition tokens {pt or 'default'}")

@@ -102,26 +102,33 @@ def config1() -> Workload:
 
 
 def config2(S: int = 64, H: int = 32, NB: int | None = None, max_ctx: int = 2048,
-            B: int = 16, seed: int = 2) -> Workload:
+            B: int = 16, seed: int = 2, D: int = 128, dtype: str = "bf16") -> Workload:
     """Decode batch 64, bf16, ctx ~ U{1..2048}, permuted 20k-frame pool.
 
     Draw order: ``ctx = integers(1, max_ctx + 1, S)``, then ``permutation(NB)``.
     Another block size keeps the pool's slot count (NB = 20000 * 16 / B).
-    Another seed (structure and values) gives a robustness variant.
+    Another seed (structure and values) gives a robustness variant. Another
+    head dim D (with the default H) keeps H * D = 4096, so a token's row
+    keeps its size; another dtype changes only the storage type.
     """
     NB = NB if NB is not None else 20000 * 16 // B
+    if D != 128 and H == 32:
+        H = 4096 // D
     rng = np.random.default_rng(seed)
     ctx = rng.integers(1, max_ctx + 1, size=S)
     order = rng.permutation(NB)
-    name = "cfg2_batch64_bf16" if (S, H) == (64, 32) else f"cfg2_S{S}_H{H}"
+    if D != 128 or dtype != "bf16":
+        name = f"cfg2_S{S}_H{H}_d{D}_{dtype}"
+    else:
+        name = "cfg2_batch64_bf16" if (S, H) == (64, 32) else f"cfg2_S{S}_H{H}"
     if B != 16:
         name += f"_B{B}"
     if seed != 2:
         name += f"_seed{seed}"
     return Workload(
-        name=name, seed=seed, dtype="bf16", H=H, D=128, B=B, NB=NB, num_seqs=S,
+        name=name, seed=seed, dtype=dtype, H=H, D=D, B=B, NB=NB, num_seqs=S,
         prefill=[(s, int(ctx[s])) for s in range(S)], frame_order=order,
-        description=f"S={S}, H={H}, d=128, B={B}, bf16, ctx U[1,{max_ctx}], permuted pool of {NB}",
+        description=f"S={S}, H={H}, d={D}, B={B}, {dtype}, ctx U[1,{max_ctx}], permuted pool of {NB}",
     )
 
 
