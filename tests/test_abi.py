@@ -77,10 +77,13 @@ def test_workspace_and_partition_sizing():
     assert pkv.partition_tokens(shape(num_seqs=256, num_heads=32, max_context_len=1200,
                                       block_size=32, max_blocks_per_seq=38)) == 2048
     assert pkv.partition_tokens(shape(cache_policy=L.PA_CACHE_REUSE)) == 512
-    # partition sizes round up to the tiling (64 tokens per chunk for fp32 d=16)
-    assert pkv.partition_tokens(shape(head_dim=16, kv_dtype=L.PA_F32, out_dtype=L.PA_F32,
-                                      block_size=10, max_context_len=40,
-                                      max_blocks_per_seq=4, partition_tokens=70)) == 128
+    # partition sizes round up to the tiling: fp32 d=16 rows are 64 bytes, so
+    # a load holds 16 rows; with 3 heads a workgroup serves one head (64
+    # tokens per chunk), with 32 heads four adjacent heads (16 tokens)
+    odd = dict(head_dim=16, kv_dtype=L.PA_F32, out_dtype=L.PA_F32, block_size=10,
+               max_context_len=40, max_blocks_per_seq=4, partition_tokens=70)
+    assert pkv.partition_tokens(shape(num_heads=3, **odd)) == 128
+    assert pkv.partition_tokens(shape(num_heads=32, **odd)) == 80
 
 
 @pytest.mark.parametrize("bad", [
