@@ -576,11 +576,12 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeAr
   }
 }
 
-// Heads per workgroup of a launch: the preferred grouping for the row size
-// when the head count divides by it, else one head.
+// Heads per workgroup of a launch: the preferred grouping for the row size,
+// halved until it divides the head count.
 int heads_per_group(int row_bytes, int num_heads) {
-  const int hp = preferred_heads(row_bytes);
-  return num_heads % hp == 0 ? hp : 1;
+  int hp = preferred_heads(row_bytes);
+  while (hp > 1 && num_heads % hp != 0) hp /= 2;
+  return hp;
 }
 
 // Ungrouped (g == nullptr) or grouped partition pass.
@@ -599,13 +600,16 @@ hipError_t launch_part(const DecodeArgs& a, const GroupArgs* g, hipStream_t stre
   return launch_timed(decode_partition_kernel<T, D, BT, false, HP>, grid, block, stream, a);
 }
 
-template <typename T, int D, int BT>
+// The launch for heads_per_group(row, H) heads per workgroup: the
+// groupings from the row's preferred one down to a single head are compiled.
+template <typename T, int D, int BT, int HP = preferred_heads(D * T::kBytes)>
 hipError_t launch_heads(const DecodeArgs& a, const GroupArgs* g, hipStream_t stream) {
-  constexpr int kHP = preferred_heads(D * T::kBytes);
-  if constexpr (kHP > 1) {
-    if (a.num_heads % kHP == 0) return launch_part<T, D, BT, kHP>(a, g, stream);
+  if constexpr (HP > 1) {
+    if (a.num_heads % HP == 0) return launch_part<T, D, BT, HP>(a, g, stream);
+    return launch_heads<T, D, BT, HP / 2>(a, g, stream);
+  } else {
+    return launch_part<T, D, BT, 1>(a, g, stream);
   }
-  return launch_part<T, D, BT, 1>(a, g, stream);
 }
 
 // Block sizes with a uniform-frame specialisation (a multiple of the rows

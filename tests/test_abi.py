@@ -84,6 +84,8 @@ def test_workspace_and_partition_sizing():
                max_context_len=40, max_blocks_per_seq=4, partition_tokens=70)
     assert pkv.partition_tokens(shape(num_heads=3, **odd)) == 128
     assert pkv.partition_tokens(shape(num_heads=32, **odd)) == 80
+    # with 6 heads, two adjacent heads (the largest grouping that divides 6)
+    assert pkv.partition_tokens(shape(num_heads=6, **odd)) == 96
 
 
 @pytest.mark.parametrize("bad", [

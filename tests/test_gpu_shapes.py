@@ -47,10 +47,11 @@ DECODE_CASES = [
 
 @pytest.mark.parametrize("dtype,D,B", DECODE_CASES)
 @pytest.mark.parametrize("pt", [0, 1 << 6])
-@pytest.mark.parametrize("H", [3, 8])
+@pytest.mark.parametrize("H", [3, 6, 8])
 def test_decode_shapes(dtype, D, B, pt, H):
-    """H = 8 takes the launches whose workgroups serve 2 or 4 adjacent heads
-    (rows under 256 bytes); H = 3 the one-head launches of every shape."""
+    """H = 8 takes the launches whose workgroups serve up to 8 adjacent
+    heads (rows under 256 bytes), H = 6 a smaller grouping that divides it,
+    H = 3 the one-head launches of every shape."""
     rng = np.random.default_rng(D * 131 + B)
     ctx = list(rng.integers(1, 400, size=5)) + [1, B, B + 1]
     w = shape_workload(dtype, D, B, ctx, H=H)
