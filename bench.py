@@ -23,8 +23,9 @@ for its pool-order variant); 6 and 7 paged prefill (a 512-token chunk after
 a cached prefix, whole prompts); 8 prefix-cached prefill rounds, with and
 without caching. Decode and prefill dispatch their longest work first unless
 --decode-batch-order / --prefill-batch-order. --head-dim / --dtype /
---block-size run workload 2 at another head dim (H = 4096 / d, so a token's
-row keeps its size), storage dtype or block size. --gpus N > 1 exits: the
+--block-size / --seqs / --max-ctx run workload 2 at another head dim
+(H = 4096 / d, so a token's row keeps its size), storage dtype, block size,
+batch or context range. --gpus N > 1 exits: the
 library runs on one GPU.
 """
 from __future__ import annotations
@@ -726,6 +727,9 @@ def main():
                     help="workload 2 with this head dim (H = 4096 / d, the same bytes per token)")
     ap.add_argument("--dtype", default="", choices=("", "bf16", "f16", "f32"),
                     help="workload 2 with this storage dtype")
+    ap.add_argument("--seqs", type=int, default=0, help="workload 2 with this many sequences")
+    ap.add_argument("--max-ctx", type=int, default=0,
+                    help="workload 2 with contexts drawn from U[1, max-ctx]")
     ap.add_argument("--block-size", type=int, default=0,
                     help="workloads 2 and 3: tokens per frame (default 16; the pool keeps its "
                          "slot count)")
@@ -771,14 +775,18 @@ def main():
     if args.block_size and args.workload not in (2, 3):
         print("--block-size applies to workloads 2 and 3 only", file=sys.stderr)
         sys.exit(2)
-    if (args.head_dim or args.dtype) and args.workload != 2:
-        print("--head-dim and --dtype apply to workload 2 only", file=sys.stderr)
+    reshaped = bool(args.head_dim or args.dtype or args.seqs or args.max_ctx)
+    if reshaped and args.workload != 2:
+        print("--head-dim, --dtype, --seqs and --max-ctx apply to workload 2 only", file=sys.stderr)
         sys.exit(2)
     if args.permuted_pool and args.workload != 5:
         print("--permuted-pool applies to workload 5 only", file=sys.stderr)
         sys.exit(2)
-    if args.head_dim or args.dtype:
-        w = configs.config2(B=args.block_size or 16, D=args.head_dim or 128,
+    if reshaped:
+        S, C, B = args.seqs or 64, args.max_ctx or 2048, args.block_size or 16
+        # a pool of 20,000 16-token frames, or enough for S contexts of C tokens
+        NB = max(20000 * 16 // B, S * -(-C // B) * 11 // 10)
+        w = configs.config2(S=S, max_ctx=C, NB=NB, B=B, D=args.head_dim or 128,
                             dtype=args.dtype or "bf16")
     elif args.block_size:
         w = {2: configs.config2, 3: configs.config3}[args.workload](B=args.block_size)
@@ -1150,7 +1158,7 @@ def main():
                                  "decode steps) before timing"},
     }
     default_run = (args.workload == 2 and not args.block_size and not args.partition_tokens
-                   and not args.head_dim and not args.dtype
+                   and not args.head_dim and not args.dtype and not args.seqs and not args.max_ctx
                    and not args.decode_batch_order and not args.ungrouped)
     if default_run and not args.no_others:
         res["other_workloads"] = other_workloads(args)

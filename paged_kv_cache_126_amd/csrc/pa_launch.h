@@ -49,6 +49,7 @@ struct DecodeArgs {
   int32_t max_parts;
   int32_t out_f32;  // 1: out is fp32; 0: out has the cache dtype
   int32_t stream_loads;  // 1: non-temporal K/V loads; 0: ordinary cached loads
+  int32_t waves;  // wavefronts per workgroup of the partition pass (set by its launch)
   const int32_t* seq_order;  // dispatch order of the launch's units (sequences or groups), or null
 };
 

@@ -68,6 +68,34 @@ def test_decode_shapes(dtype, D, B, pt, H):
         assert err <= TOL[dtype]
 
 
+# (dtype, D, H, tokens per chunk, heads per workgroup): batches of 128
+# sequences of up to 200 tokens (at most 32 chunks) over at least 4096
+# workgroups, which the decode launch serves with two wavefronts per
+# workgroup instead of eight
+TWO_WAVE_CASES = [("bf16", 128, 32, 16, 1), ("f16", 64, 64, 16, 2), ("f32", 128, 32, 8, 1)]
+
+
+@pytest.mark.parametrize("dtype,D,H,chunk,hp", TWO_WAVE_CASES)
+def test_decode_short_contexts_two_wave_launch(dtype, D, H, chunk, hp):
+    """Many short contexts: the two-wavefront launch of the ungrouped and the
+    grouped pass (bit for bit equal, checked inside run_gpu) against the
+    oracle, at the default partition size and at 64-token partitions."""
+    S = 128
+    rng = np.random.default_rng(D + H)
+    ctx = list(rng.integers(1, 201, size=S - 2)) + [1, 200]
+    assert max(ctx) <= 32 * chunk and S * (H // hp) >= 4096
+    w = shape_workload(dtype, D, 16, ctx, H=H, seed=11)
+    ref = oracle_outputs(w, pad_frame_for(w))
+    for pt in (0, 64):
+        say(f"[gpu] decode {S} short contexts, {dtype} D={D} H={H}, partition tokens {pt or 'default'}")
+        res = run_gpu(w, partition_tokens=pt, grouped=True)
+        for (pt_, out), (snap, o) in zip(res, ref):
+            assert np.array_equal(pt_.tables, snap.tables)
+            err = max_err(out.numpy(), o)
+            say(f"  max-abs err {err:.3e} (tol {TOL[dtype]})")
+            assert err <= TOL[dtype]
+
+
 PREFILL_CASES = [
     # (dtype, D, B, contexts, query lengths)
     ("bf16", 64, 16, [300, 45, 129, 1], [300, 0, 20, 1]),

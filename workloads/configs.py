@@ -121,6 +121,8 @@ def config2(S: int = 64, H: int = 32, NB: int | None = None, max_ctx: int = 2048
         name = f"cfg2_S{S}_H{H}_d{D}_{dtype}"
     else:
         name = "cfg2_batch64_bf16" if (S, H) == (64, 32) else f"cfg2_S{S}_H{H}"
+    if max_ctx != 2048:
+        name += f"_ctx{max_ctx}"
     if B != 16:
         name += f"_B{B}"
     if seed != 2:
