@@ -341,6 +341,7 @@ def frame_patterns(w, buf, sink, part_tokens: int, flush, args, dev) -> dict:
     out = {"what": ("pa_frame_read over the step's K/V bytes in a random frame order, "
                     f"{frame} B frames, one workgroup per (head, {fpu} frames)"), "GB/s": {}}
     for name, (g, gs, pc, ps, pb, f) in specs.items():
+        f = max(f, -(-n // 65535))  # pa_frame_read launches at most 65,535 units
         for _ in range(3):
             pkv.lib.frame_read(buf, order, frame, g, gs, pc, ps, pb, f, sink)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
