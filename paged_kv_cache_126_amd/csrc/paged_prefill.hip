@@ -218,14 +218,25 @@ void prefill_kernel(PrefillArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t lds_kb[2][kBN][D + kPadK];
   __shared__ __attribute__((aligned(16))) uint16_t lds_vb[2][kBN][D + kPadV];
-  // The workgroup's slice of the block table (frames of keys 0 .. wg_last),
-  // clamped into the pool, read once so that a tile's K/V loads need no
-  // dependent table read. Longer contexts read the table directly.
+  // For block sizes whose frames a wavefront's load can cross (not a power
+  // of two, or under kWaveKeys tokens): the workgroup's slice of the block
+  // table (frames of keys 0 .. wg_last), clamped into the pool, read once so
+  // that a tile's K/V loads need no dependent table read. Longer contexts
+  // read the table directly. Otherwise each wavefront reads its frames as
+  // scalars, a tile ahead of the loads that use them (tile_frames).
   __shared__ uint32_t lds_tbl[kTableCache];
   // Set when a V value staged as fp16 was out of fp16's range.
   __shared__ int lds_wide;
+  // Block sizes that are powers of two (the common case) split a token
+  // position into (block, offset) with a shift and a mask. Piece i of a
+  // wavefront covers kWaveKeys consecutive keys; with power-of-two frames of
+  // at least that many tokens they sit in one frame (uniform frames).
+  const bool pow2_block = (a.block_size & (a.block_size - 1)) == 0;
+  const int block_shift = __builtin_ctz(static_cast<unsigned>(a.block_size));
+  constexpr int kWaveKeys = 64 / kPieces;
+  const bool uniform_frames = pow2_block && a.block_size >= kWaveKeys;
   const int n_blk = wg_last / a.block_size + 1;
-  const bool tbl_in_lds = n_blk <= kTableCache;
+  const bool tbl_in_lds = !uniform_frames && n_blk <= kTableCache;
   if (tbl_in_lds) {
     for (int b = threadIdx.x; b < n_blk; b += kWaves * 64)
       lds_tbl[b] = min(static_cast<uint32_t>(table_row[b]), max_frame);
@@ -245,26 +256,28 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int kPer = kBN * kPieces / (kWaves * 64);
   static_assert(kBN * kPieces % (kWaves * 64) == 0, "tile must split evenly over the threads");
   u32x4 pk[kPer], pv[kPer];
-  // Block sizes that are powers of two (the common case) split a token
-  // position into (block, offset) with a shift and a mask.
-  const bool pow2_block = (a.block_size & (a.block_size - 1)) == 0;
-  const int block_shift = __builtin_ctz(static_cast<unsigned>(a.block_size));
-  // Piece i of a wavefront covers kWaveKeys consecutive keys; with
-  // power-of-two frames of at least that many tokens they sit in one frame,
-  // whose number is then the same for the whole wavefront. Rows past the
-  // workgroup's last key are loaded from the last key's row (finite data,
-  // weight 0), which keeps that property and needs no per-lane branch.
-  constexpr int kWaveKeys = 64 / kPieces;
-  const bool uniform_frames = pow2_block && a.block_size >= kWaveKeys && tbl_in_lds;
+  // With uniform frames the frame number is the same for the whole
+  // wavefront's piece. Rows past the workgroup's last key are loaded from
+  // the last key's row (finite data, weight 0), which keeps that property
+  // and needs no per-lane branch.
   const uint32_t lane_col = 16u * (threadIdx.x % kPieces) + static_cast<uint32_t>(head_bytes);
-  auto fetch = [&](const int k0) {
+  // Frames of the wavefront's pieces of the tile at k0 (uniform frames
+  // only), read as scalars a tile before the loads that use them.
+  auto tile_frames = [&](const int k0, uint32_t (&fr)[kPer]) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int key0 = (wave * 64 + i * kWaves * 64) / kPieces;
+      const int tok0 = min(k0 + key0, wg_last);
+      fr[i] = min(static_cast<uint32_t>(table_row[tok0 >> block_shift]), max_frame);
+    }
+  };
+  auto fetch = [&](const int k0, const uint32_t (&fr)[kPer]) {
     if (uniform_frames) {
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         const int key0 = (wave * 64 + i * kWaves * 64) / kPieces;  // the wavefront's first key
-        const int tok0 = min(k0 + key0, wg_last);
         const int tok = min(k0 + key0 + lane / kPieces, wg_last);
-        const uint32_t f = __builtin_amdgcn_readfirstlane(lds_tbl[tok0 >> block_shift]);
+        const uint32_t f = fr[i];
         const int64_t base = static_cast<int64_t>(f) * frame_bytes;
         const uint32_t off = static_cast<uint32_t>(tok & (a.block_size - 1)) * row_bytes + lane_col;
         pk[i] = load16(static_cast<const char*>(a.k_cache) + base + off);
@@ -355,12 +368,16 @@ void prefill_kernel(PrefillArgs a) {
       for (int t = 0; t < 16; ++t) o[b][t] = 0.f;
     m = kNegBig;
     l = 0.f;
-    fetch(0);
+    uint32_t fr[kPer] = {};
+    if (uniform_frames) tile_frames(0, fr);
+    fetch(0, fr);
+    if (uniform_frames && n_tiles > 1) tile_frames(kBN, fr);
     stage(0, v16);
     __syncthreads();
     for (int kt = 0; kt < n_tiles; ++kt) {
       const int k0 = kt * kBN;
-      if (kt + 1 < n_tiles) fetch(k0 + kBN);
+      if (kt + 1 < n_tiles) fetch(k0 + kBN, fr);
+      if (uniform_frames && kt + 2 < n_tiles) tile_frames(k0 + 2 * kBN, fr);
       auto& lds_k = lds_kb[kt & 1];
       auto& lds_v = lds_vb[kt & 1];
 
