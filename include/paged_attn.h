@@ -349,10 +349,10 @@ typedef struct pa_prefill_shape {
  * accumulate in fp32 on the matrix cores. The weighted sum of V takes fp16
  * operands: each softmax weight rounded once to fp16, a rounding the
  * normaliser also sums, so every output is a convex combination of value
- * rows. bf16 V is converted to fp16 on chip, exactly for magnitudes below
- * 2^16 except bits below 2^-24 (values under 2^-17); a work item that meets
- * a larger V value, an infinity or a NaN redoes its tiles as with
- * split_weights = 1. split_weights = 1 (bf16 caches) keeps V in bf16 and
+ * rows. bf16 V is converted to fp16 on chip (to nearest), exactly for
+ * magnitudes in [2^-14, 2^16); smaller ones are rounded to a multiple of
+ * 2^-24. A work item that meets a larger V value, an infinity or a NaN (or
+ * non-finite q or k) redoes its tiles as with split_weights = 1. split_weights = 1 (bf16 caches) keeps V in bf16 and
  * enters each weight as a bf16 value plus its bf16 residual, ~16 significant
  * bits, at about 8 % more time. Any other value is PA_EINVAL.
  * S * Tq * H must not exceed 2^31 - 1 (else PA_EINVAL).

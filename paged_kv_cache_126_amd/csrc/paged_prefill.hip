@@ -27,12 +27,15 @@
 //      its own share of the normaliser, added once at the end),
 //   3. accumulates O^T += V^T P^T on fp16 operands: P rounded once to fp16
 //      (11 significant bits of every softmax weight; the normaliser sums the
-//      rounded weights), and, for bf16 caches, V converted to fp16 as it is
-//      staged, which is exact for magnitudes below 2^16 (apart from bits
-//      below 2^-24). A workgroup that stages a larger V value redoes its
-//      tiles on bf16 operands with P split into a high part and the residual
-//      (two MFMAs, ~16 significant bits); callers can ask for that form
-//      throughout.
+//      rounded weights), and, for bf16 caches, V converted to fp16 (to
+//      nearest) as it is staged, which is exact for magnitudes in
+//      [2^-14, 2^16); smaller ones are rounded to a multiple of 2^-24. A
+//      larger value becomes an fp16 infinity, which makes the accumulators
+//      of every wavefront that reads its tile infinite or NaN (inf x 0 for
+//      a masked key); a workgroup whose accumulators end non-finite redoes
+//      its tiles on bf16 operands with P split into a high part and the
+//      residual (two MFMAs, ~16 significant bits); callers can ask for that
+//      form throughout.
 // Matrix layouts (verified on the device): for v_mfma_f32_32x32x16, A[i][k]
 // sits in lane i + 32 * (k / 8), element k % 8; B[k][j] in lane
 // j + 32 * (k / 8), element k % 8; D[i][j] in lane j + 32 * ((i / 4) % 2),
@@ -56,9 +59,9 @@ constexpr int kTableCache = 2048;         // block-table entries staged in LDS
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // 64-bit transposing LDS read (ds_read_b64_tr_b16) of 16-bit elements.
@@ -225,7 +228,8 @@ void prefill_kernel(PrefillArgs a) {
   // read the table directly. Otherwise each wavefront reads its frames as
   // scalars, a tile ahead of the loads that use them (tile_frames).
   __shared__ uint32_t lds_tbl[kTableCache];
-  // Set when a V value staged as fp16 was out of fp16's range.
+  // Set when a wavefront's accumulators ended non-finite after a pass with
+  // V staged in fp16.
   __shared__ int lds_wide;
   // Block sizes that are powers of two (the common case) split a token
   // position into (block, offset) with a shift and a mask. Piece i of a
@@ -314,16 +318,14 @@ void prefill_kernel(PrefillArgs a) {
     }
   };
   // Write the fetched pieces to LDS buffer `buf`. With kV16 (bf16 caches),
-  // V is written in fp16: a bf16 value of magnitude below 2^16 is exactly
-  // an fp16 value, apart from bits below 2^-24 of values under 2^-17 (fp16
-  // subnormals), which the conversion (toward zero) drops. A larger value
-  // (sign-free bf16 bits 0x4780 and up: 2^16, infinity or NaN) sets
-  // lds_wide.
+  // V is written in fp16, rounded to nearest: a bf16 value of magnitude in
+  // [2^-14, 2^16) is exactly an fp16 value (the largest bf16 value under
+  // 2^16 is 65,280); 2^16 and above become infinities (a bf16 value that
+  // large is at least 65,536), infinities and NaNs stay what they are.
   auto stage = [&](const int buf, auto v16) {
     constexpr bool kV16 = decltype(v16)::value;
     auto& lds_k = lds_kb[buf];
     auto& lds_v = lds_vb[buf];
-    u16x2 vmag = {0, 0};  // largest sign-free bf16 bits of each half seen
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int piece = threadIdx.x + i * kWaves * 64;
@@ -335,16 +337,11 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const uint32_t d = pv[i][w];
-          vmag = __builtin_elementwise_max(vmag, __builtin_bit_cast(u16x2, d & 0x7fff7fffu));
-          const float lo = __uint_as_float(d << 16);
-          const float hi = __uint_as_float(d & 0xffff0000u);
-          vw[w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+          const f32x2 f = {__uint_as_float(d << 16), __uint_as_float(d & 0xffff0000u)};
+          vw[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
         }
       }
       *reinterpret_cast<u32x4*>(&lds_v[key][8 * c]) = vw;
-    }
-    if constexpr (kV16) {
-      if (max(vmag.x, vmag.y) >= 0x4780) lds_wide = 1;
     }
   };
   // Score rows in a permuted key order: row i = 8 u + 4 v + e (u < 4, v < 2,
@@ -507,11 +504,21 @@ void prefill_kernel(PrefillArgs a) {
     bool split = a.split_weights != 0;
     if (!split) {
       pass(std::true_type{});
-      // Read after the pass's last barrier, so every thread sees the same
-      // value. A V value out of fp16's range was staged wrongly: the
+      // A V value out of fp16's range was staged as an infinity or NaN, and
+      // every wavefront that read its tile (the one holding the workgroup's
+      // last query reads every tile) ends with a non-finite accumulator:
+      // p * inf, or 0 * inf = NaN for a key a query does not see. Then the
       // workgroup redoes all its tiles with the bf16 split (the LDS buffers
       // are no longer read, so the second pass may restage them at once),
       // through the same code as a split launch, so with the same bits.
+      // (Non-finite q or k also lead here, to the same non-finite result.)
+      float probe = 0.f;  // NaN iff an accumulator is infinite or NaN
+#pragma unroll
+      for (int b = 0; b < kDBlk; ++b)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) probe = __builtin_fmaf(o[b][t], 0.f, probe);
+      if (probe != probe) lds_wide = 1;
+      __syncthreads();
       split = lds_wide != 0;
     }
     if (split) pass(std::false_type{});
