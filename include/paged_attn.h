@@ -354,7 +354,7 @@ typedef struct pa_prefill_shape {
  * 2^-24. A work item that meets a larger V value, an infinity or a NaN (or
  * non-finite q or k) redoes its tiles as with split_weights = 1. split_weights = 1 (bf16 caches) keeps V in bf16 and
  * enters each weight as a bf16 value plus its bf16 residual, ~16 significant
- * bits, at about 8 % more time. Any other value is PA_EINVAL.
+ * bits, at about 12 % more time. Any other value is PA_EINVAL.
  * S * Tq * H must not exceed 2^31 - 1 (else PA_EINVAL).
  */
 pa_status paged_attn_prefill(const void* q, const void* k_cache, const void* v_cache,
