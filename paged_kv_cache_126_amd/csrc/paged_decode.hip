@@ -15,9 +15,10 @@
 // heads: one for rows of 256 bytes or more, enough for 256 contiguous bytes
 // per token below that (a 64-byte row alone would leave the other half of
 // each 128-byte line to another workgroup, and the line would be fetched
-// twice). The workgroup's wavefronts (kNW, or two when every partition is a
-// few chunks long; chosen per launch) take the partition's chunks of kCH
-// tokens round robin. Inside a wavefront, each cache row (one token's D
+// twice). A short launch (every partition a few chunks long) runs two
+// wavefronts per workgroup instead of kNW and, where it fits, twice the
+// heads (see short_launch). The workgroup's wavefronts take the partition's
+// chunks of kCH tokens round robin. Inside a wavefront, each cache row (one token's D
 // elements of one head) is spread over kLPR lanes holding 16 bytes each, so
 // one load instruction moves kRPL whole rows (kRPL / HP tokens of HP heads)
 // and every lane issues 16-byte loads. q . k is a per-lane dot product (packed
@@ -54,7 +55,7 @@ namespace pa {
 namespace {
 
 constexpr float kNegBig = -1.0e30f;
-constexpr int kNW = 8;  // wavefronts per workgroup (at most; see launch_waves)
+constexpr int kNW = 8;  // wavefronts per workgroup (at most; see short_launch)
 constexpr int kU = 4;   // row loads per lane per chunk (for each of K and V)
 
 template <bool kStream>
@@ -591,32 +592,40 @@ int heads_per_group(int row_bytes, int num_heads) {
   return hp;
 }
 
-// Wavefronts per workgroup. With kNW wavefronts sharing a partition of a few
-// chunks, most of them only wait at the combine; when no partition exceeds
-// kShortChunks chunks, two wavefronts take them instead, provided the launch
-// still has enough workgroups to fill the chip at two wavefronts each
-// (measured at 2048 sequences of up to 128 bf16 tokens, d = 128: 11% faster;
-// no change at up to 512 tokens; longer contexts keep kNW). The grouped pass
-// makes the same choice from the same figures, which keeps its results equal
-// to the ungrouped pass's.
+// Short launches. With kNW wavefronts sharing a partition of a few chunks,
+// most of them only wait at the combine. When no partition exceeds
+// kShortChunks chunks and the launch has enough workgroups to fill the chip
+// at two wavefronts each, a workgroup runs two wavefronts and serves twice
+// the heads (when they divide H and the halved grid still has that many
+// workgroups), so each token's rows of the group form a span twice as long
+// and the per-workgroup work (prologue, combine, store) covers more rows.
+// Measured at 2048 sequences of up to 128 bf16 tokens, d = 128: 438 us with
+// eight wavefronts and one head, 396 us with two wavefronts, 376 us with two
+// wavefronts and two heads; 512 sequences of up to 512 tokens: 351 and 338
+// us. Longer contexts keep kNW and one head (two heads cost 1% at 2048).
+// Chunks of the doubled grouping are half as long, so partition sizes
+// rounded to whole chunks of the normal grouping stay whole. The grouped
+// pass makes the same choice from the same figures, which keeps its results
+// equal to the ungrouped pass's.
 constexpr int kShortChunks = 32;
 constexpr int64_t kShortMinWorkgroups = 4096;
 
-template <int CH, int HP>
-int launch_waves(const DecodeArgs& a) {
-  const int64_t span = a.max_ctx < a.part_tokens ? a.max_ctx : a.part_tokens;
-  const int64_t workgroups =
-      static_cast<int64_t>(a.num_seqs) * (a.num_heads / HP) * a.max_parts;
-  return span <= static_cast<int64_t>(kShortChunks) * CH && workgroups >= kShortMinWorkgroups
-             ? 2
-             : kNW;
+int64_t launch_workgroups(const DecodeArgs& a, int hp) {
+  return static_cast<int64_t>(a.num_seqs) * (a.num_heads / hp) * a.max_parts;
 }
 
-// Ungrouped (g == nullptr) or grouped partition pass.
+bool short_launch(const DecodeArgs& a, int chunk, int hp) {
+  const int64_t span = a.max_ctx < a.part_tokens ? a.max_ctx : a.part_tokens;
+  return span <= static_cast<int64_t>(kShortChunks) * chunk &&
+         launch_workgroups(a, hp) >= kShortMinWorkgroups;
+}
+
+// Ungrouped (g == nullptr) or grouped partition pass, HP heads and `waves`
+// wavefronts per workgroup.
 template <typename T, int D, int BT, int HP>
-hipError_t launch_part(const DecodeArgs& args, const GroupArgs* g, hipStream_t stream) {
+hipError_t launch_part(const DecodeArgs& args, const GroupArgs* g, int waves, hipStream_t stream) {
   DecodeArgs a = args;
-  a.waves = launch_waves<Tiling<T, D, HP>::kCH, HP>(a);
+  a.waves = waves;
   const dim3 block(a.waves * 64);
   if (g != nullptr) {
     const dim3 grid(a.num_heads / HP, a.max_parts, g->num_groups);
@@ -630,16 +639,20 @@ hipError_t launch_part(const DecodeArgs& args, const GroupArgs* g, hipStream_t s
   return launch_timed(decode_partition_kernel<T, D, BT, false, HP>, grid, block, stream, a);
 }
 
-// The launch for heads_per_group(row, H) heads per workgroup: the
-// groupings from the row's preferred one down to a single head are compiled.
+// HP heads per workgroup (the row's preferred grouping, halved until it
+// divides H; every such grouping is compiled), kNW wavefronts; or, for a
+// short launch, two wavefronts and 2 HP heads when that grouping fits.
 template <typename T, int D, int BT, int HP = preferred_heads(D * T::kBytes)>
 hipError_t launch_heads(const DecodeArgs& a, const GroupArgs* g, hipStream_t stream) {
   if constexpr (HP > 1) {
-    if (a.num_heads % HP == 0) return launch_part<T, D, BT, HP>(a, g, stream);
-    return launch_heads<T, D, BT, HP / 2>(a, g, stream);
-  } else {
-    return launch_part<T, D, BT, 1>(a, g, stream);
+    if (a.num_heads % HP != 0) return launch_heads<T, D, BT, HP / 2>(a, g, stream);
   }
+  if (!short_launch(a, Tiling<T, D, HP>::kCH, HP)) return launch_part<T, D, BT, HP>(a, g, kNW, stream);
+  if constexpr (Tiling<T, D, 1>::kRPL % (2 * HP) == 0) {
+    if (a.num_heads % (2 * HP) == 0 && launch_workgroups(a, 2 * HP) >= kShortMinWorkgroups)
+      return launch_part<T, D, BT, 2 * HP>(a, g, 2, stream);
+  }
+  return launch_part<T, D, BT, HP>(a, g, 2, stream);
 }
 
 // Block sizes with a uniform-frame specialisation (a multiple of the rows

@@ -104,6 +104,9 @@ PREFILL_CASES = [
     ("bf16", 128, 7, [150, 99, 260], [40, 99, 260]),
     # B = 1 and 2,200 keys: 2,200 table entries, more than the kernel stages in LDS
     ("bf16", 128, 1, [2200, 40], [130, 40]),
+    # B = 16 and 33,000 keys (2,063 frames): wavefronts whose pieces share a
+    # frame read its number from the table a tile ahead, at any length
+    ("bf16", 64, 16, [33000, 100], [40, 100]),
 ]
 
 
