@@ -52,7 +52,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-KERNEL_SOURCES = {"paged_decode": ("paged_decode.hip", "pa_device.h", "pa_launch.h"),
+KERNEL_SOURCES = {"paged_decode": ("paged_decode.h", "paged_decode.hip", "paged_decode_f32.hip",
+                                  "paged_decode_f16.hip", "paged_decode_bf16.hip", "pa_device.h",
+                                  "pa_launch.h"),
                   "paged_prefill": ("paged_prefill.hip", "pa_device.h", "pa_launch.h",
                                     "pa_prefill.h")}
 

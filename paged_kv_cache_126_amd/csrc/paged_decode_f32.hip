@@ -1,0 +1,12 @@
+// Paged decode partition pass for fp32 caches (its own file, so that the
+// dtypes' instantiations compile in parallel).
+#include "paged_decode.h"
+
+namespace pa {
+
+hipError_t decode_dispatch_f32(const DecodeArgs& a, const GroupArgs* g, int head_dim,
+                               hipStream_t stream) {
+  return dispatch_dim<F32>(a, g, head_dim, stream);
+}
+
+}  // namespace pa
