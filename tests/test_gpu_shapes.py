@@ -68,26 +68,34 @@ def test_decode_shapes(dtype, D, B, pt, H):
         assert err <= TOL[dtype]
 
 
-# (dtype, D, H, tokens per chunk, heads per workgroup): batches of 128
-# sequences of up to 200 tokens (at most 32 chunks) over at least 4096
-# workgroups, which the decode launch serves with two wavefronts per
-# workgroup instead of eight
-TWO_WAVE_CASES = [("bf16", 128, 32, 16, 1), ("f16", 64, 64, 16, 2), ("f32", 128, 32, 8, 1)]
+# (dtype, D, H, S, tokens per chunk, heads per workgroup): S sequences of up
+# to 200 tokens (at most 32 chunks) over at least 4096 workgroups, which the
+# decode launch serves with two wavefronts per workgroup instead of eight,
+# and with twice the heads where 2 * hp divides H and the halved grid still
+# has at least 4096 workgroups (the first three cases); H = 33 keeps one
+# head, and 128 sequences of 32 heads keep it at the default partition size
+# for lack of workgroups (their four 64-token partitions have enough)
+TWO_WAVE_CASES = [("bf16", 128, 32, 256, 16, 1), ("f16", 64, 64, 256, 16, 2),
+                  ("f32", 128, 32, 256, 8, 1), ("bf16", 128, 33, 128, 16, 1),
+                  ("bf16", 128, 32, 128, 16, 1)]
 
 
-@pytest.mark.parametrize("dtype,D,H,chunk,hp", TWO_WAVE_CASES)
-def test_decode_short_contexts_two_wave_launch(dtype, D, H, chunk, hp):
-    """Many short contexts: the two-wavefront launch of the ungrouped and the
-    grouped pass (bit for bit equal, checked inside run_gpu) against the
-    oracle, at the default partition size and at 64-token partitions."""
-    S = 128
-    rng = np.random.default_rng(D + H)
+@pytest.mark.parametrize("dtype,D,H,S,chunk,hp", TWO_WAVE_CASES)
+def test_decode_short_contexts_two_wave_launch(dtype, D, H, S, chunk, hp):
+    """Many short contexts: the two-wavefront launches (twice the heads per
+    workgroup where that fits) of the ungrouped and the grouped pass (bit
+    for bit equal, checked inside run_gpu) against the oracle, at the
+    default partition size and at 64-token partitions."""
+    rng = np.random.default_rng(D + H + S)
     ctx = list(rng.integers(1, 201, size=S - 2)) + [1, 200]
     assert max(ctx) <= 32 * chunk and S * (H // hp) >= 4096
     w = shape_workload(dtype, D, 16, ctx, H=H, seed=11)
     ref = oracle_outputs(w, pad_frame_for(w))
     for pt in (0, 64):
-        say(f"[gpu] decode {S} short contexts, {dtype} D={D} H={H}, partition tokens {pt or 'default'}")
+        parts = 1 if pt == 0 else -(-max(ctx) // pt)
+        doubled = H % (2 * hp) == 0 and S * (H // (2 * hp)) * parts >= 4096
+        say(f"[gpu] decode {S} short contexts, {dtype} D={D} H={H} "
+            f"({2 * hp if doubled else hp} heads per workgroup), partition tokens {pt or 'default'}")
         res = run_gpu(w, partition_tokens=pt, grouped=True)
         for (pt_, out), (snap, o) in zip(res, ref):
             assert np.array_equal(pt_.tables, snap.tables)
