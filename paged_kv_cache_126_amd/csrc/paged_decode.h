@@ -491,11 +491,15 @@ __global__ __launch_bounds__(kNW * 64) void decode_group_kernel(DecodeArgs a, Gr
 // Log-sum-exp merge of a sequence's partitions: with M = max_p m_p,
 // out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p. The workgroup
 // reduces the partitions' maxima and normalisers in parallel; for the
-// weighted sum its wavefronts take every kMergeWaves-th partition and add
-// their parts in LDS. The order of every sum is fixed by the launch shape,
-// so results repeat bit for bit.
+// weighted sum wavefront w takes partitions w, w + kMergeWaves, ..., in
+// groups of kMergeUnroll whose rows are all loaded before they are summed
+// (the first group before the maximum is known), and the wavefronts' parts
+// are added in LDS. The order of every sum is fixed by the launch shape, so
+// results repeat bit for bit.
 constexpr int kMergeWaves = 2;
+constexpr int kMergeUnroll = 8;
 constexpr int kMergeChunk = 1024;  // partitions whose weights sit in LDS at a time
+static_assert(kMergeChunk % (kMergeWaves * kMergeUnroll) == 0, "groups must not straddle chunks");
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -528,6 +532,21 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeAr
   const float* ml = a.ws_ml + 2 * sh * a.max_parts;
   const float* pacc = a.ws_acc + sh * a.max_parts * D;
 
+  // rows of the group of partitions p0 + u * kMergeWaves (u < kMergeUnroll)
+  float rows[kMergeUnroll][kEPL];
+  auto load_rows = [&](const int p0) {
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int p = p0 + u * kMergeWaves;
+#pragma unroll
+      for (int k = 0; k < kEPL; ++k) {
+        const int e = lane + 64 * k;
+        rows[u][k] = (p < n_parts && e < D) ? pacc[static_cast<int64_t>(p) * D + e] : 0.f;
+      }
+    }
+  };
+  load_rows(wave);
+
   float mx = kNegBig;
   for (int p = tid; p < n_parts; p += kMergeWaves * 64) mx = fmaxf(mx, ml[2 * p]);
   mx = wave_max(mx);
@@ -550,13 +569,16 @@ __global__ __launch_bounds__(kMergeWaves * 64) void decode_merge_kernel(DecodeAr
       L += ml[2 * (c0 + p) + 1] * f;
     }
     __syncthreads();
-    for (int p = wave; p < cn; p += kMergeWaves) {
-      const float f = weights[p];
-      const float* row = pacc + static_cast<int64_t>(c0 + p) * D;
+    for (int p0 = wave; p0 < cn; p0 += kMergeWaves * kMergeUnroll) {
+      if (c0 + p0 != wave) load_rows(c0 + p0);  // the first group is loaded
 #pragma unroll
-      for (int k = 0; k < kEPL; ++k) {
-        const int e = lane + 64 * k;
-        if (e < D) O[k] = __builtin_fmaf(row[e], f, O[k]);
+      for (int u = 0; u < kMergeUnroll; ++u) {
+        const int p = p0 + u * kMergeWaves;
+        if (p < cn) {
+          const float f = weights[p];
+#pragma unroll
+          for (int k = 0; k < kEPL; ++k) O[k] = __builtin_fmaf(rows[u][k], f, O[k]);
+        }
       }
     }
   }
