@@ -628,12 +628,14 @@ inline int heads_per_group(int row_bytes, int num_heads) {
 // Measured at 2048 sequences of up to 128 bf16 tokens, d = 128: 438 us with
 // eight wavefronts and one head, 396 us with two wavefronts, 376 us with two
 // wavefronts and two heads; 512 sequences of up to 512 tokens: 351 and 338
-// us. Longer contexts keep kNW and one head (two heads cost 1% at 2048).
+// us; 1024 sequences of up to 1024 tokens: 1354 and 1334 us. At 2048 tokens
+// the two forms run alike (512 sequences), and the batch-64 launch, with too
+// few workgroups for two wavefronts, keeps kNW and one head.
 // Chunks of the doubled grouping are half as long, so partition sizes
 // rounded to whole chunks of the normal grouping stay whole. The grouped
 // pass makes the same choice from the same figures, which keeps its results
 // equal to the ungrouped pass's.
-constexpr int kShortChunks = 32;
+constexpr int kShortChunks = 64;
 constexpr int64_t kShortMinWorkgroups = 4096;
 
 inline int64_t launch_workgroups(const DecodeArgs& a, int hp) {

@@ -69,7 +69,7 @@ def test_decode_shapes(dtype, D, B, pt, H):
 
 
 # (dtype, D, H, S, tokens per chunk, heads per workgroup): S sequences of up
-# to 200 tokens (at most 32 chunks) over at least 4096 workgroups, which the
+# to 200 tokens (at most 64 chunks) over at least 4096 workgroups, which the
 # decode launch serves with two wavefronts per workgroup instead of eight,
 # and with twice the heads where 2 * hp divides H and the halved grid still
 # has at least 4096 workgroups (the first three cases); H = 33 keeps one
@@ -88,7 +88,7 @@ def test_decode_short_contexts_two_wave_launch(dtype, D, H, S, chunk, hp):
     default partition size and at 64-token partitions."""
     rng = np.random.default_rng(D + H + S)
     ctx = list(rng.integers(1, 201, size=S - 2)) + [1, 200]
-    assert max(ctx) <= 32 * chunk and S * (H // hp) >= 4096
+    assert max(ctx) <= 64 * chunk and S * (H // hp) >= 4096
     w = shape_workload(dtype, D, 16, ctx, H=H, seed=11)
     ref = oracle_outputs(w, pad_frame_for(w))
     for pt in (0, 64):
