@@ -618,23 +618,25 @@ inline int heads_per_group(int row_bytes, int num_heads) {
   return hp;
 }
 
-// Short launches. With kNW wavefronts sharing a partition of a few chunks,
-// most of them only wait at the combine. When no partition exceeds
-// kShortChunks chunks and the launch has enough workgroups to fill the chip
-// at two wavefronts each, a workgroup runs two wavefronts and serves twice
-// the heads (when they divide H and the halved grid still has that many
-// workgroups), so each token's rows of the group form a span twice as long
-// and the per-workgroup work (prologue, combine, store) covers more rows.
-// Measured at 2048 sequences of up to 128 bf16 tokens, d = 128: 438 us with
-// eight wavefronts and one head, 396 us with two wavefronts, 376 us with two
-// wavefronts and two heads; 512 sequences of up to 512 tokens: 351 and 338
-// us; 1024 sequences of up to 1024 tokens: 1354 and 1334 us. At 2048 tokens
-// the two forms run alike (512 sequences), and the batch-64 launch, with too
-// few workgroups for two wavefronts, keeps kNW and one head.
-// Chunks of the doubled grouping are half as long, so partition sizes
-// rounded to whole chunks of the normal grouping stay whole. The grouped
-// pass makes the same choice from the same figures, which keeps its results
-// equal to the ungrouped pass's.
+// Short launches. With kNW wavefronts sharing a context of a few chunks,
+// most of them only wait at the combine. When no context exceeds
+// kShortChunks chunks (by max_ctx) and the launch has enough workgroups to
+// fill the chip at two wavefronts each, a workgroup runs two wavefronts and
+// serves twice the heads (when they divide H and the halved grid still has
+// that many workgroups), so each token's rows of the group form a span twice
+// as long and the per-workgroup work (prologue, combine, store) covers more
+// rows. Measured at 2048 sequences of up to 128 bf16 tokens, d = 128: 438 us
+// with eight wavefronts and one head, 396 us with two wavefronts, 376 us
+// with two wavefronts and two heads; 512 sequences of up to 512 tokens: 351
+// and 338 us; 1024 sequences of up to 1024 tokens: 1354 and 1334 us. At 2048
+// tokens the two forms run alike (512 sequences). Full partitions of longer
+// contexts keep the default form (the batch-64 workload split into 512-token
+// partitions took 224 us in the short form), and so does the batch-64
+// launch, with too few workgroups for two wavefronts. Chunks of the doubled
+// grouping are half as long, so partition sizes rounded to whole chunks of
+// the normal grouping stay whole. The grouped pass makes the same choice
+// from the same figures, which keeps its results equal to the ungrouped
+// pass's.
 constexpr int kShortChunks = 64;
 constexpr int64_t kShortMinWorkgroups = 4096;
 
@@ -643,8 +645,7 @@ inline int64_t launch_workgroups(const DecodeArgs& a, int hp) {
 }
 
 inline bool short_launch(const DecodeArgs& a, int chunk, int hp) {
-  const int64_t span = a.max_ctx < a.part_tokens ? a.max_ctx : a.part_tokens;
-  return span <= static_cast<int64_t>(kShortChunks) * chunk &&
+  return static_cast<int64_t>(a.max_ctx) <= static_cast<int64_t>(kShortChunks) * chunk &&
          launch_workgroups(a, hp) >= kShortMinWorkgroups;
 }
 
