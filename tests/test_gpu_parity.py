@@ -88,6 +88,28 @@ def test_full_size_parity(cfg):
     torch.cuda.empty_cache()
 
 
+def test_full_size_short_contexts_parity():
+    """The batch-64 workload's geometry with 2,048 sequences of up to 128
+    tokens, at full size in the benchmark's launch configuration: the launch
+    takes the short form (two wavefronts and two heads per workgroup), and
+    every output is checked against the fp64 oracle."""
+    import torch
+
+    w = configs.config2(S=2048, max_ctx=128, NB=20000)
+    say(f"[gpu] full workload {w.name}: {w.description}")
+    results = run_gpu(w, order="longest")
+    for pt, out in results:
+        o = out.numpy()
+        assert np.all(np.isfinite(o)), "non-finite output"
+        ref = oracle_full(w, pt.step, pt.context_lens)
+        err = max_err(o, ref)
+        say(f"  {w.name} step {pt.step}: all {o.shape[0]} x {o.shape[1]} (seq, head) outputs, "
+            f"max-abs err {err:.3e} (tol {TOL[w.dtype]})")
+        assert err <= TOL[w.dtype]
+    del results
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("pt", [0, 16, 64])
 def test_grouped_decode_equals_ungrouped(cfg, pt):
