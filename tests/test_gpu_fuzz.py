@@ -2,7 +2,8 @@
 random dtypes, head dims, block sizes (on and off the compiled fast paths),
 head counts, batch sizes, context mixes (empty, single-token, block-aligned,
 long) and forced partition sizes; prefill over random chunk shapes, head
-counts and dispatch orders; grouped decode over random fork families. Every case is
+counts and dispatch orders; grouped decode over random fork families; decode
+batches large enough for the short launch form. Every case is
 compared element by element; grouped decode is also compared bit for bit
 with the ungrouped pass."""
 from __future__ import annotations
@@ -57,6 +58,41 @@ def test_decode_random_shapes(seed):
     w = shape_workload(dtype, D, B, ctx, H=H, seed=60 + seed)
     say(f"[gpu] fuzz decode seed {seed}: {w.description}, partition tokens {pt or 'default'}")
     res = run_gpu(w, partition_tokens=pt)
+    ref = oracle_outputs(w, pad_frame_for(w))
+    for (p, out), (snap, o) in zip(res, ref):
+        assert np.array_equal(p.tables, snap.tables)
+        err = max_err(out.numpy(), o)
+        say(f"  max-abs err {err:.3e}")
+        assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_decode_random_short_launches(seed):
+    """Batches large enough for the short launch form (contexts of at most
+    64 chunks over 4,096 workgroups or more: two wavefronts, and twice the
+    heads per workgroup where they divide H): random dtype, head dim, block
+    size, head count and partition size, with empty, single-token and
+    block-aligned contexts, through the ungrouped and the grouped pass (bit
+    for bit equal, checked inside run_gpu)."""
+    rng = np.random.default_rng(7000 + seed)
+    dtype = DTYPES[seed % 3]
+    D = int(rng.choice(HEAD_DIMS))
+    B = int(rng.choice(BLOCKS))
+    H = int(rng.choice([12, 16, 24, 33, 40]))
+    row = D * (4 if dtype == "f32" else 2)
+    hp = 1 if row >= 256 else 256 // row  # the row's preferred grouping, at most
+    # enough sequences for the doubled grouping's grid; contexts of at most
+    # 256 tokens stay within 64 chunks at every shape (chunks are 4 tokens
+    # or more)
+    S = -(-8192 * hp // H) + int(rng.integers(0, 100))
+    cap = 256
+    ctx = [int(c) for c in rng.integers(1, cap + 1, size=S)]
+    ctx[:4] = [0, 1, B, min(cap, 2 * B)]
+    pt = int(rng.choice([0, 16, 64]))
+    w = shape_workload(dtype, D, B, ctx, H=H, seed=70 + seed)
+    say(f"[gpu] fuzz short decode seed {seed}: {dtype} D={D} B={B} H={H} S={S} contexts up to "
+        f"{max(ctx)}, partition tokens {pt or 'default'}")
+    res = run_gpu(w, partition_tokens=pt, grouped=True)
     ref = oracle_outputs(w, pad_frame_for(w))
     for (p, out), (snap, o) in zip(res, ref):
         assert np.array_equal(p.tables, snap.tables)
