@@ -182,6 +182,9 @@ size_t paged_attn_workspace_size(const pa_decode_shape* shape);
  * 8,192 workgroups (S * H * partitions of the longest context), or, with a
  * dispatch_order, about 1,024: longest-first dispatch balances long
  * partitions, which write fewer partial results and often need no merge.
+ * With a dispatch_order and a max_context_len of 2049-4096 tokens it is
+ * 4096 (one partition per sequence) when S * H / (2 * heads per workgroup)
+ * is still 1,024 or more.
  */
 int32_t paged_attn_partition_tokens(const pa_decode_shape* shape);
 

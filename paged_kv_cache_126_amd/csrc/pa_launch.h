@@ -18,14 +18,21 @@ LaunchEvents& launch_events();
 
 // Launch `kernel`; with launch events set, through hipExtLaunchKernelGGL so
 // the events take the kernel's own start and end time stamps.
+// lds_bytes of dynamic shared memory per workgroup.
 template <typename K, typename... Args>
-inline hipError_t launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+inline hipError_t launch_timed_lds(K kernel, dim3 grid, dim3 block, size_t lds_bytes,
+                                   hipStream_t stream, Args... args) {
   const LaunchEvents& ev = launch_events();
   if (ev.start || ev.stop)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
+    hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, ev.start, ev.stop, 0, args...);
   else
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+    hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, args...);
   return hipGetLastError();
+}
+
+template <typename K, typename... Args>
+inline hipError_t launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  return launch_timed_lds(kernel, grid, block, 0, stream, args...);
 }
 
 // Everything one decode launch needs, passed to the kernels by value.
@@ -70,6 +77,10 @@ enum class Dtype : int { F32 = 0, F16 = 1, BF16 = 2 };
 // heads); partition sizes are multiples of it. 0 if the combination is
 // unsupported.
 int chunk_tokens(Dtype dt, int head_dim, int num_heads);
+
+// Heads per workgroup of the default launch form for (dtype, head_dim,
+// heads); 0 if the combination is unsupported.
+int heads_per_workgroup(Dtype dt, int head_dim, int num_heads);
 
 // Queue the partition pass / the merge pass. Return a hipError_t.
 hipError_t launch_decode_partitions(const DecodeArgs& a, Dtype dt, int head_dim,

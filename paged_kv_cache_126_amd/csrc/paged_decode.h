@@ -17,10 +17,11 @@
 // heads: one for rows of 256 bytes or more, enough for 256 contiguous bytes
 // per token below that (a 64-byte row alone would leave the other half of
 // each 128-byte line to another workgroup, and the line would be fetched
-// twice). A short launch (every partition a few chunks long) runs two
-// wavefronts per workgroup instead of kNW and, where it fits, twice the
-// heads (see short_launch). The workgroup's wavefronts take the partition's
-// chunks of kCH tokens round robin. Inside a wavefront, each cache row (one token's D
+// twice). A workgroup runs kNW wavefronts; a short launch (contexts of a
+// few chunks) runs two and a wide launch (long contexts) kWideWaves, both
+// with twice the heads where that fits (see "Launch forms" below). The
+// workgroup's wavefronts take the partition's chunks of kCH tokens round
+// robin. Inside a wavefront, each cache row (one token's D
 // elements of one head) is spread over kLPR lanes holding 16 bytes each, so
 // one load instruction moves kRPL whole rows (kRPL / HP tokens of HP heads)
 // and every lane issues 16-byte loads. q . k is a per-lane dot product (packed
@@ -59,7 +60,8 @@ namespace pa {
 namespace {
 
 constexpr float kNegBig = -1.0e30f;
-constexpr int kNW = 8;  // wavefronts per workgroup (at most; see short_launch)
+constexpr int kNW = 8;          // wavefronts per workgroup of the default form
+constexpr int kWideWaves = 16;  // of the wide form (see wide_launch)
 constexpr int kU = 4;   // row loads per lane per chunk (for each of K and V)
 
 template <bool kStream>
@@ -232,14 +234,26 @@ struct SoftmaxState {
   }
 };
 
-// LDS of the wavefront combine: per wavefront, each of the HP heads' state
-// (sized for kNW wavefronts; a launch may use fewer).
+// LDS of the wavefront combine, sized by the launch for its nw wavefronts
+// (dynamic shared memory): per wavefront, each of the HP heads' running
+// maximum, sum and accumulator.
 template <int D, int HP>
 struct CombineLds {
-  float m[kNW][HP];
-  float l[kNW][HP];
-  float acc[kNW][HP * D];
+  float* base;
+  int nw;
+  __device__ __forceinline__ float& m(int w, int hs) const { return base[w * HP + hs]; }
+  __device__ __forceinline__ float& l(int w, int hs) const { return base[(nw + w) * HP + hs]; }
+  __device__ __forceinline__ float& acc(int w, int e) const {
+    return base[2 * nw * HP + w * HP * D + e];
+  }
 };
+
+template <int D, int HP>
+constexpr size_t combine_lds_bytes(int nw) {
+  return static_cast<size_t>(nw) * HP * (D + 2) * sizeof(float);
+}
+
+extern __shared__ float combine_lds[];
 
 // Combine a (sequence, head group, partition)'s states of all lane groups
 // and wavefronts (log-sum-exp rule, for each head apart) and store the
@@ -250,11 +264,11 @@ struct CombineLds {
 template <typename T, int D, int HP>
 __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const int s, const int h0,
                                                  const int part, const int n_parts,
-                                                 SoftmaxState<T, D> st, CombineLds<D, HP>& lds) {
+                                                 SoftmaxState<T, D> st, const CombineLds<D, HP>& lds) {
   using Tl = Tiling<T, D, HP>;
   constexpr int VEC = Tl::kVEC, LPR = Tl::kLPR;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = a.waves;  // the launch's choice, 2..kNW
+  const int nw = a.waves;  // the launch's choice, 2..kWideWaves
   const int lane = threadIdx.x & 63;
   const int grp = lane / LPR;
   const int col = lane % LPR;
@@ -278,10 +292,10 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const int 
   // Combine the wavefronts through LDS.
   if (grp < HP) {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) lds.acc[wave][grp * D + col * VEC + j] = st.acc[j];
+    for (int j = 0; j < VEC; ++j) lds.acc(wave, grp * D + col * VEC + j) = st.acc[j];
     if (col == 0) {
-      lds.m[wave][grp] = m;
-      lds.l[wave][grp] = l;
+      lds.m(wave, grp) = m;
+      lds.l(wave, grp) = l;
     }
   }
   __syncthreads();
@@ -290,15 +304,15 @@ __device__ __forceinline__ void finish_partition(const DecodeArgs& a, const int 
     const int hs = e / D;
     float M = kNegBig;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w)
-      if (w < nw) M = fmaxf(M, lds.m[w][hs]);
+    for (int w = 0; w < kWideWaves; ++w)
+      if (w < nw) M = fmaxf(M, lds.m(w, hs));
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) {
+    for (int w = 0; w < kWideWaves; ++w) {
       if (w >= nw) break;
-      const float fw = fast_exp2(lds.m[w][hs] - M);
-      L = __builtin_fmaf(lds.l[w][hs], fw, L);
-      O = __builtin_fmaf(lds.acc[w][e], fw, O);
+      const float fw = fast_exp2(lds.m(w, hs) - M);
+      L = __builtin_fmaf(lds.l(w, hs), fw, L);
+      O = __builtin_fmaf(lds.acc(w, e), fw, O);
     }
     const int64_t sh = static_cast<int64_t>(s) * a.num_heads + h0 + hs;
     const int el = e - hs * D;
@@ -338,7 +352,7 @@ __device__ __forceinline__ int parts_of(const DecodeArgs& a, const int ctx) {
 // Eight wavefronts per SIMD (at most 64 registers per lane): the kernel is
 // bound by memory latency, so it keeps the most loads in flight.
 template <typename T, int D, int BT, bool kStream, int HP>
-__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(8)))
+__global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_partition_kernel(DecodeArgs a) {
   using Ld = ChunkLoader<T, D, BT, kStream, HP>;
   constexpr int VEC = Ld::VEC, LPR = Ld::LPR, CH = Ld::CH;
@@ -366,7 +380,7 @@ void decode_partition_kernel(DecodeArgs a) {
 
   SoftmaxState<T, D> st;
   st.reset();
-  const int nw = a.waves;  // the launch's choice, 2..kNW
+  const int nw = a.waves;  // the launch's choice, 2..kWideWaves
   const int n_chunks = (tok_end - tok_begin + CH - 1) / CH;
   for (int chunk = wave; chunk < n_chunks; chunk += nw) {
     const int t0 = tok_begin + chunk * CH;
@@ -380,7 +394,7 @@ void decode_partition_kernel(DecodeArgs a) {
     st.update(qv, a.scale_log2, kv, vv, valid);
   }
 
-  __shared__ CombineLds<D, HP> lds;
+  const CombineLds<D, HP> lds{combine_lds, nw};
   finish_partition<T, D, HP>(a, s, h0, part, n_parts, st, lds);
 }
 
@@ -394,7 +408,7 @@ void decode_partition_kernel(DecodeArgs a) {
 // length is rounded down to a whole chunk), so every member's result equals
 // the ungrouped pass's bit for bit.
 template <typename T, int D, int BT, bool kStream, int HP, int G>
-__global__ __launch_bounds__(kNW * 64) void decode_group_kernel(DecodeArgs a, GroupArgs g) {
+__global__ __launch_bounds__(kWideWaves * 64) void decode_group_kernel(DecodeArgs a, GroupArgs g) {
   using Ld = ChunkLoader<T, D, BT, kStream, HP>;
   constexpr int VEC = Ld::VEC, LPR = Ld::LPR, CH = Ld::CH;
 
@@ -422,7 +436,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_group_kernel(DecodeArgs a, Gr
   shared = shared < 0 ? 0 : shared / CH * CH;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = a.waves;  // the launch's choice, 2..kNW
+  const int nw = a.waves;  // the launch's choice, 2..kWideWaves
   const int lane = threadIdx.x & 63;
   const Ld ld(a, h0, lane);
   const int h = h0 + (lane / LPR) % HP;  // this lane's head
@@ -476,7 +490,7 @@ __global__ __launch_bounds__(kNW * 64) void decode_group_kernel(DecodeArgs a, Gr
     }
   }
 
-  __shared__ CombineLds<D, HP> lds;
+  const CombineLds<D, HP> lds{combine_lds, nw};
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     if (i >= members) break;
@@ -618,27 +632,44 @@ inline int heads_per_group(int row_bytes, int num_heads) {
   return hp;
 }
 
+// Launch forms. The default form runs kNW wavefronts on HP heads (the
+// row's preferred grouping). Two others serve twice the heads where that
+// grouping fits (2 HP divides H and the rows per load), so each token's rows
+// of the group form a span twice as long:
+//
 // Short launches. With kNW wavefronts sharing a context of a few chunks,
 // most of them only wait at the combine. When no context exceeds
 // kShortChunks chunks (by max_ctx) and the launch has enough workgroups to
-// fill the chip at two wavefronts each, a workgroup runs two wavefronts and
-// serves twice the heads (when they divide H and the halved grid still has
-// that many workgroups), so each token's rows of the group form a span twice
-// as long and the per-workgroup work (prologue, combine, store) covers more
-// rows. Measured at 2048 sequences of up to 128 bf16 tokens, d = 128: 438 us
-// with eight wavefronts and one head, 396 us with two wavefronts, 376 us
-// with two wavefronts and two heads; 512 sequences of up to 512 tokens: 351
-// and 338 us; 1024 sequences of up to 1024 tokens: 1354 and 1334 us. At 2048
-// tokens the two forms run alike (512 sequences). Full partitions of longer
-// contexts keep the default form (the batch-64 workload split into 512-token
-// partitions took 224 us in the short form), and so does the batch-64
-// launch, with too few workgroups for two wavefronts. Chunks of the doubled
-// grouping are half as long, so partition sizes rounded to whole chunks of
-// the normal grouping stay whole. The grouped pass makes the same choice
-// from the same figures, which keeps its results equal to the ungrouped
-// pass's.
+// fill the chip at two wavefronts each, a workgroup runs two wavefronts
+// (and 2 HP heads if the halved grid still has that many workgroups), so the
+// per-workgroup work (prologue, combine, store) covers more rows. Measured
+// at 2048 sequences of up to 128 bf16 tokens, d = 128: 438 us with eight
+// wavefronts and one head, 396 us with two wavefronts, 376 us with two
+// wavefronts and two heads; 512 sequences of up to 512 tokens: 351 and 338
+// us; 1024 sequences of up to 1024 tokens: 1354 and 1334 us.
+//
+// Wide launches: kWideWaves wavefronts on 2 HP heads, the same wavefronts in
+// flight as the default form over half the workgroups, when contexts reach
+// kWideMinContext tokens in partitions of at least that length, the launch
+// has one partition or at least kWideMinParts (two or three partitions, the
+// second of them short, ran 4-11% slower than the default form), and the
+// grid keeps kWideMinWorkgroups workgroups. Measured against the default
+// form: batch 64 x 2048 bf16 tokens 181.5 -> 175.4 us, 8 x 32k 832 -> 794
+// us, batch 256 at 64 heads 1701 -> 1613 us, 1024 x 2048 2663 -> 2608 us,
+// d = 16 and 64 3.5%; rows of 512 bytes (d = 256 bf16, d = 128 fp32) run
+// alike in both forms. The grouped pass of the shared-prefix workload
+// (contexts up to about 1200 tokens) keeps the default form: there the wide
+// form was 5.5% slower.
+//
+// Chunks of a doubled grouping are half as long, so partition sizes rounded
+// to whole chunks of the default grouping stay whole. The grouped pass makes
+// the same choice from the same figures, which keeps its results equal to
+// the ungrouped pass's.
 constexpr int kShortChunks = 64;
 constexpr int64_t kShortMinWorkgroups = 4096;
+constexpr int kWideMinContext = 1536;
+constexpr int kWideMinParts = 4;
+constexpr int64_t kWideMinWorkgroups = 1024;
 
 inline int64_t launch_workgroups(const DecodeArgs& a, int hp) {
   return static_cast<int64_t>(a.num_seqs) * (a.num_heads / hp) * a.max_parts;
@@ -649,6 +680,13 @@ inline bool short_launch(const DecodeArgs& a, int chunk, int hp) {
          launch_workgroups(a, hp) >= kShortMinWorkgroups;
 }
 
+// hp2: the doubled grouping (which must fit).
+inline bool wide_launch(const DecodeArgs& a, int hp2) {
+  return a.max_ctx >= kWideMinContext && a.part_tokens >= kWideMinContext &&
+         (a.max_parts == 1 || a.max_parts >= kWideMinParts) &&
+         launch_workgroups(a, hp2) >= kWideMinWorkgroups;
+}
+
 // Ungrouped (g == nullptr) or grouped partition pass, HP heads and `waves`
 // wavefronts per workgroup.
 template <typename T, int D, int BT, int HP>
@@ -656,32 +694,42 @@ hipError_t launch_part(const DecodeArgs& args, const GroupArgs* g, int waves, hi
   DecodeArgs a = args;
   a.waves = waves;
   const dim3 block(a.waves * 64);
+  const size_t lds = combine_lds_bytes<D, HP>(waves);
   if (g != nullptr) {
     const dim3 grid(a.num_heads / HP, a.max_parts, g->num_groups);
     if (a.stream_loads)
-      return launch_timed(decode_group_kernel<T, D, BT, true, HP, kMaxGroup>, grid, block, stream, a, *g);
-    return launch_timed(decode_group_kernel<T, D, BT, false, HP, kMaxGroup>, grid, block, stream, a, *g);
+      return launch_timed_lds(decode_group_kernel<T, D, BT, true, HP, kMaxGroup>, grid, block, lds,
+                              stream, a, *g);
+    return launch_timed_lds(decode_group_kernel<T, D, BT, false, HP, kMaxGroup>, grid, block, lds,
+                            stream, a, *g);
   }
   const dim3 grid(a.num_heads / HP, a.max_parts, a.num_seqs);
   if (a.stream_loads)
-    return launch_timed(decode_partition_kernel<T, D, BT, true, HP>, grid, block, stream, a);
-  return launch_timed(decode_partition_kernel<T, D, BT, false, HP>, grid, block, stream, a);
+    return launch_timed_lds(decode_partition_kernel<T, D, BT, true, HP>, grid, block, lds, stream, a);
+  return launch_timed_lds(decode_partition_kernel<T, D, BT, false, HP>, grid, block, lds, stream, a);
 }
 
 // HP heads per workgroup (the row's preferred grouping, halved until it
-// divides H; every such grouping is compiled), kNW wavefronts; or, for a
-// short launch, two wavefronts and 2 HP heads when that grouping fits.
+// divides H; every such grouping is compiled) in the default form, or the
+// short or wide form with 2 HP heads where that grouping fits.
 template <typename T, int D, int BT, int HP = preferred_heads(D * T::kBytes)>
 hipError_t launch_heads(const DecodeArgs& a, const GroupArgs* g, hipStream_t stream) {
   if constexpr (HP > 1) {
     if (a.num_heads % HP != 0) return launch_heads<T, D, BT, HP / 2>(a, g, stream);
   }
-  if (!short_launch(a, Tiling<T, D, HP>::kCH, HP)) return launch_part<T, D, BT, HP>(a, g, kNW, stream);
-  if constexpr (Tiling<T, D, 1>::kRPL % (2 * HP) == 0) {
-    if (a.num_heads % (2 * HP) == 0 && launch_workgroups(a, 2 * HP) >= kShortMinWorkgroups)
-      return launch_part<T, D, BT, 2 * HP>(a, g, 2, stream);
+  constexpr bool kDoubles = Tiling<T, D, 1>::kRPL % (2 * HP) == 0;
+  const bool doubles = kDoubles && a.num_heads % (2 * HP) == 0;
+  if (short_launch(a, Tiling<T, D, HP>::kCH, HP)) {
+    if constexpr (kDoubles) {
+      if (doubles && launch_workgroups(a, 2 * HP) >= kShortMinWorkgroups)
+        return launch_part<T, D, BT, 2 * HP>(a, g, 2, stream);
+    }
+    return launch_part<T, D, BT, HP>(a, g, 2, stream);
   }
-  return launch_part<T, D, BT, HP>(a, g, 2, stream);
+  if constexpr (kDoubles) {
+    if (doubles && wide_launch(a, 2 * HP)) return launch_part<T, D, BT, 2 * HP>(a, g, kWideWaves, stream);
+  }
+  return launch_part<T, D, BT, HP>(a, g, kNW, stream);
 }
 
 // Block sizes with a uniform-frame specialisation (a multiple of the rows

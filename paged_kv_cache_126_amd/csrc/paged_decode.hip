@@ -13,6 +13,11 @@ int chunk_tokens(Dtype dt, int head_dim, int num_heads) {
   return kU * (64 / lpr) / heads_per_group(head_dim * bytes, num_heads);
 }
 
+int heads_per_workgroup(Dtype dt, int head_dim, int num_heads) {
+  if (chunk_tokens(dt, head_dim, num_heads) <= 0) return 0;
+  return heads_per_group(head_dim * (dt == Dtype::F32 ? 4 : 2), num_heads);
+}
+
 hipError_t launch_decode_partitions(const DecodeArgs& a, Dtype dt, int head_dim,
                                     hipStream_t stream) {
   return launch_decode_groups(a, nullptr, dt, head_dim, stream);
