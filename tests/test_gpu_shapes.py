@@ -8,14 +8,18 @@ that take the head-per-XCD launch mapping.
 Each case is a small seeded workload (random context lengths, a permuted
 frame pool) written through the product block manager and kv_append, and
 compared element by element with the fp64 oracle on the oracle's own replay.
+The decode launch forms for many short contexts (two wavefronts) and for
+long ones over enough workgroups (sixteen wavefronts on twice the heads)
+need larger batches: those cases compare every output with the oracle's
+contiguous definition over each sequence's logical tokens.
 """
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
-from tests.gpu_support import (TOL, max_err, oracle_outputs, oracle_prefill, pad_frame_for,
-                               require_gpu, run_gpu, run_gpu_prefill, say)
+from tests.gpu_support import (TOL, max_err, oracle_full, oracle_outputs, oracle_prefill,
+                               pad_frame_for, require_gpu, run_gpu, run_gpu_prefill, say)
 from workloads.configs import Workload
 
 pytestmark = pytest.mark.gpu
@@ -102,6 +106,49 @@ def test_decode_short_contexts_two_wave_launch(dtype, D, H, S, chunk, hp):
             err = max_err(out.numpy(), o)
             say(f"  max-abs err {err:.3e} (tol {TOL[dtype]})")
             assert err <= TOL[dtype]
+
+
+# (dtype, D, H, S, heads per workgroup of the default form, longest context,
+# partition tokens): contexts of 1,536 tokens or more in four partitions (or
+# one), over at least 1,024 workgroups at twice the heads, which the decode
+# launch serves with sixteen wavefronts on 2 * hp heads (the wide form): the
+# groupings of 16, 8, 4 and 2 heads, 512-byte rows (fp32 d = 128, bf16
+# d = 256), and the ordered default of one 4,096-token partition
+WIDE_CASES = [("bf16", 16, 16, 256, 8, 6144, 1536), ("bf16", 32, 16, 128, 4, 6144, 1536),
+              ("f16", 64, 8, 128, 2, 6144, 1536), ("f32", 128, 4, 128, 1, 6144, 1536),
+              ("bf16", 256, 4, 128, 1, 6144, 1536), ("f32", 64, 8, 64, 1, 6144, 1536),
+              ("bf16", 128, 8, 256, 1, 4096, 0)]
+
+
+@pytest.mark.parametrize("dtype,D,H,S,hp,max_ctx,pt", WIDE_CASES)
+def test_decode_long_contexts_wide_launch(dtype, D, H, S, hp, max_ctx, pt):
+    """Long contexts over enough workgroups: the sixteen-wavefront launches
+    on twice the heads, of the ungrouped and the grouped pass (bit for bit
+    equal, checked inside run_gpu), dispatched longest first as the
+    benchmark does; every output against the fp64 oracle's contiguous
+    definition."""
+    import torch
+
+    rng = np.random.default_rng(D + H + S + max_ctx)
+    ctx = list(rng.integers(1, max_ctx + 1, size=S - 2)) + [1, max_ctx]
+    part = pt if pt else 4096  # the ordered default for contexts of 2,049-4,096 tokens
+    parts = -(-max_ctx // part)
+    assert max_ctx >= 1536 and (parts == 1 or parts >= 4) and H % (2 * hp) == 0
+    assert S * (H // (2 * hp)) * parts >= 1024
+    w = shape_workload(dtype, D, 16, ctx, H=H, seed=16)
+    say(f"[gpu] decode {S} long contexts, {dtype} D={D} H={H} ({2 * hp} heads per workgroup), "
+        f"partition tokens {pt or 'default'}")
+    results = run_gpu(w, partition_tokens=pt, grouped=True, order="longest")
+    for pt_, out in results:
+        o = out.numpy()
+        assert np.all(np.isfinite(o)), "non-finite output"
+        ref = oracle_full(w, pt_.step, pt_.context_lens)
+        err = max_err(o, ref)
+        say(f"  all {o.shape[0]} x {o.shape[1]} (seq, head) outputs, max-abs err {err:.3e} "
+            f"(tol {TOL[dtype]})")
+        assert err <= TOL[dtype]
+    del results
+    torch.cuda.empty_cache()
 
 
 PREFILL_CASES = [
