@@ -3,7 +3,8 @@ random dtypes, head dims, block sizes (on and off the compiled fast paths),
 head counts, batch sizes, context mixes (empty, single-token, block-aligned,
 long) and forced partition sizes; prefill over random chunk shapes, head
 counts and dispatch orders; grouped decode over random fork families; decode
-batches large enough for the short launch form. Every case is
+batches large enough for the short launch form, and long-context batches
+that take the sixteen-wavefront form. Every case is
 compared element by element; grouped decode is also compared bit for bit
 with the ungrouped pass."""
 from __future__ import annotations
@@ -11,8 +12,9 @@ from __future__ import annotations
 import numpy as np
 import pytest
 
-from tests.gpu_support import (TOL, max_err, oracle_default, oracle_outputs, oracle_prefill,
-                               pad_frame_for, require_gpu, run_gpu, run_gpu_prefill, say)
+from tests.gpu_support import (TOL, max_err, oracle_default, oracle_full, oracle_outputs,
+                               oracle_prefill, pad_frame_for, require_gpu, run_gpu, run_gpu_prefill,
+                               say)
 from tests.test_gpu_shapes import shape_workload
 from workloads import values as V
 
@@ -99,6 +101,46 @@ def test_decode_random_short_launches(seed):
         err = max_err(out.numpy(), o)
         say(f"  max-abs err {err:.3e}")
         assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_random_wide_launches(seed):
+    """Batches that take the sixteen-wavefront form (contexts of 1,536 tokens
+    or more in four or more partitions of at least that length, 1,024
+    workgroups or more at twice the heads): random dtype, head dim, block
+    size (on and off the compiled fast paths), head count (a multiple of
+    twice the row's grouping) and partition size, with empty, single-token and block-aligned
+    contexts, dispatched longest first, through the ungrouped and the
+    grouped pass (bit for bit equal, checked inside run_gpu); every output
+    against the oracle's contiguous definition."""
+    import torch
+
+    rng = np.random.default_rng(8000 + seed)
+    dtype = DTYPES[seed % 3]
+    D = HEAD_DIMS[seed % 5]
+    B = int(rng.choice(BLOCKS))
+    row = D * (4 if dtype == "f32" else 2)
+    hp = 1 if row >= 256 else 256 // row  # the row's preferred grouping
+    H = 2 * hp * int(rng.integers(1, 6))  # a multiple of the doubled grouping
+    pt = int(rng.choice([1536, 2048]))
+    parts = int(rng.integers(4, 6))
+    groups = H // (2 * hp)  # workgroups per (sequence, partition) at the doubled grouping
+    S = -(-1024 // (groups * parts)) + int(rng.integers(0, 16))
+    cap = parts * pt
+    ctx = [int(c) for c in rng.integers(1, cap + 1, size=S)]
+    ctx[:5] = [0, 1, B, 2 * B, cap]
+    w = shape_workload(dtype, D, B, ctx, H=H, seed=80 + seed)
+    say(f"[gpu] fuzz wide decode seed {seed}: {dtype} D={D} B={B} H={H} S={S} contexts up to "
+        f"{cap}, partition tokens {pt}, {2 * hp} heads per workgroup")
+    results = run_gpu(w, partition_tokens=pt, grouped=True, order="longest")
+    for p, out in results:
+        o = out.numpy()
+        ref = oracle_full(w, p.step, p.context_lens)
+        err = max_err(o, ref)
+        say(f"  all {o.shape[0]} x {o.shape[1]} (seq, head) outputs, max-abs err {err:.3e}")
+        assert err <= TOL[dtype]
+    del results
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("seed", range(24))
