@@ -156,6 +156,29 @@ def test_grouped_decode_full_size_shared_prefix():
     torch.cuda.empty_cache()
 
 
+def test_grouped_decode_shared_prefix_wide_form():
+    """The shared-prefix workload with 2,000-token prompts at 8 heads: its
+    contexts (2,001-2,200 tokens) take one 4,096-token partition in the
+    ordered launch, and its 256 sequences keep 1,024 workgroups at two heads
+    each, so both passes run in the sixteen-wavefront form, and the grouped
+    pass folds each family's shared chunks into four members' states there.
+    Grouped equals ungrouped bit for bit (inside run_gpu); every output
+    against the oracle's contiguous definition."""
+    import torch
+
+    w = configs.config4(prompt_len=2000, H=8)
+    say(f"[gpu] {w.name}, grouped, sixteen-wavefront form: {w.description}")
+    results = run_gpu(w, grouped=True, order="longest")
+    for pt, out in results:
+        assert 2048 < int(pt.context_lens.max()) <= 4096 and w.num_seqs * w.H // 2 >= 1024
+        ref = oracle_full(w, pt.step, pt.context_lens)
+        err = max_err(out.numpy(), ref)
+        say(f"  {w.name} grouped step {pt.step}: all {out.numel()} values, max-abs err {err:.3e}")
+        assert err <= TOL[w.dtype]
+    del results
+    torch.cuda.empty_cache()
+
+
 def test_grouped_decode_edge_groups():
     """Hand-built groups: members whose context is all shared but for a few
     tokens past the last whole chunk, a member with an empty context, a
