@@ -428,8 +428,11 @@ void prefill_kernel(PrefillArgs a) {
         }
 #pragma unroll
         for (int t = 0; t < 16; ++t) x[t] = fast_exp2(__builtin_fmaf(x[t], a.scale_log2, -m));
-        if (!full) {
-          // masked keys weigh exactly 0 (with a zero scale, -inf * 0 would be NaN)
+        // With a positive scale a masked key's exponent is -inf, so its weight
+        // is already exactly 0; only a zero scale (-inf * 0 = NaN) needs the
+        // mask again (scale_log2 is uniform, so is the branch).
+        if (!full && a.scale_log2 == 0.f) {
+          // masked keys weigh exactly 0
 #pragma unroll
           for (int t = 0; t < 16; ++t) {
             const int key = k0 + 16 * (t / 8) + 8 * half + t % 8;
