@@ -159,9 +159,10 @@ struct ChunkLoader {
         step_base[u] = static_cast<int64_t>(f) * frame_bytes + static_cast<int64_t>(tu % BT) * row_bytes;
       }
       const uint32_t lane_off = tok * row_bytes + lane_bytes;
-      // Every K row of the chunk is issued before any V row: loads complete
-      // in issue order, so the scores can start while the V rows are still
-      // in flight (1-2 % faster than interleaving K and V per row).
+      // Every K row of the chunk is issued before any V row: 1-2 % faster
+      // than interleaving K and V row by row. (Not for an earlier start of
+      // the scores: a form whose scores begin as each K row arrives, instead
+      // of after all eight loads, ran alike.)
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         u32x4 kz = {0u, 0u, 0u, 0u};
